@@ -1,0 +1,157 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch each one: a dropped term, a wrong sign or index, a transposed operand,
+the wrong free-list order, a read past the context length."""
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle.accounting
+import oracle.alloc_model
+import oracle.attention
+import oracle.layout
+import pins
+
+
+def _ns():
+    return types.SimpleNamespace(alloc_model=oracle.alloc_model, layout=oracle.layout,
+                                 attention=oracle.attention, accounting=oracle.accounting)
+
+
+def _no_scale(q, K, V, scale):
+    return _orig_attention(q, K, V, 1.0)
+
+
+def _wrong_sign(q, K, V, scale):
+    if K.shape[0] == 0:
+        return np.zeros(q.shape[0])
+    z = -scale * (K @ q)
+    w = np.exp(z - z.max())
+    return (w @ V) / w.sum()
+
+
+def _no_normalise(q, K, V, scale):
+    if K.shape[0] == 0:
+        return np.zeros(q.shape[0])
+    z = scale * (K @ q)
+    w = np.exp(z - z.max())
+    return w @ V
+
+
+def _transposed(q, K, V, scale):
+    # keys and values swapped
+    return _orig_attention(q, V, K, scale)
+
+
+def _default_scale_1_over_d(d):
+    return 1.0 / d
+
+
+def _floor_blocks(length, block_size):
+    return length // block_size
+
+
+def _slot_off_by_one(table, pos, block_size):
+    return table[pos // block_size], (pos + 1) % block_size
+
+
+def _kind_inner(g, page, layer, head, kind, slot, dim):
+    # kind and slot nested the other way round: K and V interleaved per token
+    return ((((page * g.L + layer) * g.H + head) * g.B + slot) * 2 + kind) * g.D + dim
+
+
+def _readback_past_length(pool, g, layer, table, length):
+    # reads whole blocks, tail slots included
+    full = len(table) * g.B if length else 0
+    kc, vc = _orig_readback(pool, g, layer, table, full)
+    return kc, vc
+
+
+def _gqa_interleaved(q_bits, pool, g, layer, tables, lengths, dtype, scale=None):
+    q = oracle.attention.decode_bits(q_bits, dtype)
+    n, hq, d = q.shape
+    if scale is None:
+        scale = oracle.attention.default_scale(d)
+    out = np.zeros((n, hq, d))
+    for s in range(n):
+        kc, vc = oracle.layout.readback(pool, g, layer, tables[s], int(lengths[s]))
+        K = oracle.attention.decode_bits(kc, dtype)
+        V = oracle.attention.decode_bits(vc, dtype)
+        for h in range(hq):
+            out[s, h] = oracle.attention.attention(q[s, h], K[:, h % g.H, :], V[:, h % g.H, :], scale)
+    return out
+
+
+_orig_attention = oracle.attention.attention
+_orig_readback = oracle.layout.readback
+
+
+class _FifoModel(oracle.alloc_model.AllocModel):
+    def alloc(self, seq_id, new_len):
+        if new_len < 0:
+            return oracle.alloc_model.INVALID, 0
+        table = self.tables.get(seq_id, [])
+        if new_len < self.lengths.get(seq_id, 0):
+            return oracle.alloc_model.INVALID, 0
+        need = oracle.alloc_model.blocks_for(new_len, self.block_size) - len(table)
+        if need > len(self.stack):
+            return oracle.alloc_model.OOM, 0
+        new_pages = [self.stack.pop(0) for _ in range(need)]   # takes from the bottom
+        self.tables[seq_id] = table + new_pages
+        self.lengths[seq_id] = new_len
+        return oracle.alloc_model.OK, need
+
+
+class _ForwardPushModel(oracle.alloc_model.AllocModel):
+    def free(self, seq_id):
+        if seq_id not in self.tables:
+            return oracle.alloc_model.UNKNOWN_SEQ
+        self.stack.extend(self.tables[seq_id])                # last page ends on top
+        del self.tables[seq_id]
+        del self.lengths[seq_id]
+        return oracle.alloc_model.OK
+
+
+class _LeakyModel(oracle.alloc_model.AllocModel):
+    def free(self, seq_id):
+        if seq_id not in self.tables:
+            return oracle.alloc_model.UNKNOWN_SEQ
+        for page in reversed(self.tables[seq_id][1:]):          # drops the first page
+            self.stack.append(page)
+        del self.tables[seq_id]
+        del self.lengths[seq_id]
+        return oracle.alloc_model.OK
+
+
+MUTANTS = {
+    "attention_without_scale": (oracle.attention, "attention", _no_scale),
+    "attention_wrong_sign": (oracle.attention, "attention", _wrong_sign),
+    "attention_not_normalised": (oracle.attention, "attention", _no_normalise),
+    "attention_keys_values_swapped": (oracle.attention, "attention", _transposed),
+    "default_scale_1_over_d": (oracle.attention, "default_scale", _default_scale_1_over_d),
+    "gqa_interleaved_heads": (oracle.attention, "paged_decode_attention", _gqa_interleaved),
+    "blocks_floor_not_ceil": (oracle.alloc_model, "blocks_for", _floor_blocks),
+    "slot_off_by_one": (oracle.layout, "token_location", _slot_off_by_one),
+    "kv_interleaved_per_token": (oracle.layout, "elem_offset", _kind_inner),
+    "readback_past_length": (oracle.layout, "readback", _readback_past_length),
+    "fifo_free_list": (oracle.alloc_model, "AllocModel", _FifoModel),
+    "free_pushes_forward": (oracle.alloc_model, "AllocModel", _ForwardPushModel),
+    "free_leaks_a_page": (oracle.alloc_model, "AllocModel", _LeakyModel),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    module, attr, replacement = MUTANTS[name]
+    monkeypatch.setattr(module, attr, replacement)
+    if module is oracle.alloc_model and attr == "blocks_for":
+        monkeypatch.setattr(oracle.accounting, "blocks_for", replacement)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(_ns())
+        except (AssertionError, IndexError, ValueError, OverflowError, ZeroDivisionError):
+            caught.append(pin.__name__)
+    assert caught, "no pin catches the planted mistake " + name
