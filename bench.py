@@ -1,0 +1,268 @@
+"""Decode-step paged attention benchmark on one MI355X.
+
+A step is one pass of the whole hot path over the batch: grow every sequence
+by one token in the host allocator (one batched call), export the block tables
+and lengths (pinned host -> device copy), scatter the new tokens' K/V into
+their page slots for every layer, and run paged decode attention for every
+layer (partition kernel + split merge).  Inputs are resident in HBM when the
+timed region starts.  Sequences keep growing over the steps; bytes are counted
+from the actual lengths.
+
+Prints ONE JSON line.  ``value`` is the algorithmic KV bandwidth of the whole
+step (attention's K/V + q + out + table + length bytes, plus the scatter's
+reads and writes) over the step time; ``roofline`` is for the attention
+partition kernel alone, timed with HIP events recorded around it on its own
+stream; ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the
+same workload.
+"""
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+WORKLOADS = {
+    "tiny": "Tiny: 4 seqs, 1 layer, 2 heads, d_head 16, fp32, block 16, pool 64 pages, context U[1,64], {frames} frames",
+    "gpt2": "GPT-2-124M shape: 12 layers x 12 heads, d_head 64, fp16, 32 seqs, prompts U[8,64] + 50 decode steps, block 16, pool 1024 pages, {frames} frames",
+    "mixed": "Mixed-length: 32 seqs, 50% U[32,128] / 30% U[256,512] / 20% U[1024,2048], 12 heads, d_head 64, fp16, block 16, pool 4096, {frames} frames",
+    "13b": "13B-style: 40 heads, d_head 128, fp16, one layer's decode, 64 seqs, context U[256,2048], block 16, pool 1.1x blocks used, {frames} frames",
+    "gqa": "GQA large batch: 14 q heads / 2 kv heads, d_head 64, bf16, 256 seqs, context U[1024,4096], block 16, pool 70k pages after 500x16 alloc/free churn, {frames} frames",
+}
+
+
+def alg_bytes_attention(ctx, w, out_bytes):
+    """Bytes attention must move: K+V of every context token, q, out, the
+    table entries in use, the lengths."""
+    ctx = np.asarray(ctx, dtype=np.int64)
+    kv = int(ctx.sum()) * w.hkv * w.d * 2 * w.es
+    qo = w.n * w.hq * w.d * (w.es + out_bytes)
+    tables = int(((ctx + 15) // 16).sum()) * 4
+    return kv + qo + tables + 4 * w.n
+
+
+def alg_bytes_scatter(w):
+    """One new token per sequence: read k and v, write them into the pool, read
+    tok_seq/tok_pos and one table entry each."""
+    return w.n * w.hkv * w.d * 2 * w.es * 2 + w.n * 12
+
+
+def run_gpu(args, name, frames, steps, warmup, flush):
+    import torch
+    from paged_kv_cache_43_amd import inputs, pf, runner
+
+    dev = "cuda"
+    w = inputs.Workload(name, frames=frames)
+    kv = runner.PagedKV(w, device=dev, sentinel=False, extra_tokens=steps + warmup + 1)
+    q = runner.fill_workload(kv, device=dev)
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(123)
+    newk = runner.bits_to_device(inputs.normal_bits(rng, (w.layers, w.n, w.hkv, w.d), w.dtype), dev)
+    newv = runner.bits_to_device(inputs.normal_bits(rng, (w.layers, w.n, w.hkv, w.d), w.dtype), dev)
+    out_t = torch.empty((w.layers, w.n, w.hq, w.d), dtype=torch.int32 if w.es == 4 else torch.int16,
+                        device=dev)
+    ids = np.arange(w.n, dtype=np.uint64)
+    base = w.ctx.astype(np.int64)
+    total_steps = warmup + steps
+    max_ctx_final = int(base.max()) + total_steps
+    kv.ensure_workspace(max_ctx_final)
+    # pinned staging ring for the per-step table/length export
+    ring = 4
+    stage_bt = [torch.empty((w.n, kv.max_blocks), dtype=torch.int32).pin_memory() for _ in range(ring)]
+    stage_len = [torch.empty(w.n, dtype=torch.int32).pin_memory() for _ in range(ring)]
+    stage_ev = [torch.cuda.Event() for _ in range(ring)]
+    tok_seq = torch.arange(w.n, dtype=torch.int32, device=dev)
+    tok_pos = torch.empty(w.n, dtype=torch.int32, device=dev)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+    ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
+    ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
+    ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(total_steps)]
+    for row in ev_a + ev_b:
+        for e in row:
+            e.record(stream)   # creates the underlying hipEvent_t
+    torch.cuda.synchronize()
+    ctx_per_step = []
+
+    def step(t):
+        slot = t % ring
+        stage_ev[slot].synchronize()           # the copy that last used this slot is done
+        new_lens = (base + t + 1).astype(np.int32)
+        st, _ = pf.pf_alloc_for_seqs(kv.h, ids, new_lens)
+        pf.check(st, "pf_alloc_for_seqs")
+        st, _, _ = pf.pf_block_tables(kv.h, ids, kv.max_blocks, stage_bt[slot].numpy(),
+                                      stage_len[slot].numpy())
+        pf.check(st, "pf_block_tables")
+        if flush:
+            flush_buf.zero_()
+        ev_step[t][0].record(stream)
+        kv.bt.copy_(stage_bt[slot], non_blocking=True)
+        kv.ctx.copy_(stage_len[slot], non_blocking=True)
+        tok_pos.copy_(kv.ctx)
+        tok_pos.sub_(1)
+        stage_ev[slot].record(stream)
+        mc = int(new_lens.max())
+        for layer in range(w.layers):
+            kv.scatter(layer, newk[layer], newv[layer], tok_seq, tok_pos)
+        for layer in range(w.layers):
+            pf.check(pf.pf_pool_set_timing_events(kv.h, ev_a[t][layer].cuda_event,
+                                                  ev_b[t][layer].cuda_event))
+            kv.attention(layer, q[layer], out_t[layer], mc)
+        ev_step[t][1].record(stream)
+        ctx_per_step.append(new_lens.astype(np.int64))
+
+    for t in range(warmup):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warmup, total_steps):
+        step(t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pf.check(pf.pf_pool_set_timing_events(kv.h, None, None))
+
+    timed = range(warmup, total_steps)
+    step_ms = [ev_step[t][0].elapsed_time(ev_step[t][1]) for t in timed]
+    part_ms = [ev_a[t][l].elapsed_time(ev_b[t][l]) for t in timed for l in range(w.layers)]
+    attn_bytes = [alg_bytes_attention(ctx_per_step[t], w, w.es) for t in timed]
+    step_bytes = [b * w.layers + alg_bytes_scatter(w) * w.layers for b in attn_bytes]
+    # free everything: the pool must come back whole
+    for s in range(w.n):
+        pf.check(pf.pf_free_seq(kv.h, s))
+    assert pf.pf_free_pages(kv.h) == w.num_pages
+    split = pf.pf_attention_split_tokens(kv.h, w.n, w.hq, max_ctx_final)
+    mfma = pf.pf_pool_get_option(kv.h, pf.PF_OPT_GQA_MFMA)[1] and w.hq > w.hkv and w.dtype != "f32"
+    kv.close()
+    ms_step_events = float(np.mean(step_ms))
+    ms_step_wall = wall * 1e3 / steps
+    # value uses the step time the timed loop actually took (flushes excluded
+    # only when --flush is given, then from per-step events)
+    ms_step = ms_step_events if flush else ms_step_wall
+    avg_step_bytes = float(np.mean(step_bytes))
+    avg_attn_bytes = float(np.mean(attn_bytes))
+    part_avg_ms = float(np.mean(part_ms))
+    achieved = avg_attn_bytes / (part_avg_ms * 1e-3) / 1e9
+    return dict(
+        w=w, name=name, frames=frames, ms_step=ms_step, ms_step_wall=ms_step_wall,
+        ms_step_events=ms_step_events, value=avg_step_bytes / (ms_step * 1e-3) / 1e9,
+        seqs_per_ms=w.n / ms_step, part_avg_us=part_avg_ms * 1e3,
+        part_med_us=float(np.median(part_ms)) * 1e3, part_min_us=float(np.min(part_ms)) * 1e3,
+        attn_bytes=avg_attn_bytes, achieved=achieved, split=split, mfma=bool(mfma),
+        kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers))
+
+
+def cpu_baseline(name, budget_s):
+    """The CPU fp64 oracle (contiguous two-pass softmax attention on decoded
+    K/V) on the first sequences of the same workload, single thread."""
+    from paged_kv_cache_43_amd import inputs
+    import oracle.attention as oa
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    w = inputs.Workload(name, frames="shuffled")
+    ks, vs, qb = w.values()
+    qd = oa.decode_bits(qb[0], w.dtype)
+    g = w.hq // w.hkv
+    sc = oa.default_scale(w.d)
+    t0 = time.perf_counter()
+    done = 0
+    tokens = 0
+    while done < w.n and time.perf_counter() - t0 < budget_s:
+        s = done
+        K = oa.decode_bits(ks[s][0], w.dtype)
+        V = oa.decode_bits(vs[s][0], w.dtype)
+        for h in range(w.hq):
+            oa.attention(qd[s, h], K[:, h // g, :], V[:, h // g, :], sc)
+        tokens += int(w.ctx[s])
+        done += 1
+    el = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    b = alg_bytes_attention(w.ctx[:done], type("W", (), dict(n=done, hq=w.hq, hkv=w.hkv, d=w.d, es=w.es))(),
+                            w.es)
+    return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seqs_per_ms": round(done / (el * 1e3), 5), "seconds": round(el, 2),
+            "sample": "first %d of %d sequences (%d context tokens), layer 0, all %d query heads; "
+                      "decode + fp64 two-pass softmax attention, one thread" % (done, w.n, tokens, w.hq)}
+
+
+def describe(r):
+    w = r["w"]
+    return {"workload": WORKLOADS[r["name"]].format(frames=r["frames"]), "n_seqs": w.n,
+            "layers": w.layers, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
+            "block_size": 16, "pool_pages": w.num_pages, "frames": r["frames"],
+            "split_tokens": r["split"], "kernel": "mfma" if r["mfma"] else "valu"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="13b", choices=sorted(WORKLOADS))
+    ap.add_argument("--frames", default="shuffled", choices=["shuffled", "ordered"])
+    ap.add_argument("--also", default="gqa", help="comma list of extra configs reported beside the headline")
+    ap.add_argument("--flush", action="store_true", help="zero 1 GiB between steps (outside the step events)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.synchronize()
+    head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, args.flush)
+    others = {}
+    for extra in [x for x in args.also.split(",") if x and x != args.config]:
+        for fr in ("shuffled", "ordered"):
+            r = run_gpu(args, extra, fr, args.steps, args.warmup, args.flush)
+            others["%s_%s" % (extra, fr)] = {
+                "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
+                "seqs_per_ms": round(r["seqs_per_ms"], 2), "ms_per_step": round(r["ms_step"], 4),
+                "attn_partition_avg_us": round(r["part_avg_us"], 2),
+                "attn_partition_GBps": round(r["achieved"], 1), "config": describe(r)}
+    w = head["w"]
+    line = {
+        "metric": "paged decode attention KV GB/s (% of MI355X HBM peak) + sequences/ms",
+        "value": round(head["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": describe(head),
+        "pct_hbm_peak": round(100 * head["value"] / HBM_PEAK_GBS, 1),
+        "seqs_per_ms": round(head["seqs_per_ms"], 2),
+        "ms_per_step_wall": round(head["ms_step_wall"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attention partition", "avg_launch_us": round(head["part_avg_us"], 2),
+                     "median_launch_us": round(head["part_med_us"], 2),
+                     "alg_bytes_per_launch": int(head["attn_bytes"])},
+        "others": others,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * pf.h -- C ABI of libpf: decode-step paged attention on MI355X (gfx950).
+ *
+ * Three parts, all behind plain pointers and sizes:
+ *
+ *  1. A host page allocator: an O(1) LIFO free list of fixed-size pages plus a
+ *     block table per sequence (PageForge, "Four layers, one pointer moving
+ *     through all of them" and "Five techniques": free-list allocation and
+ *     page-table-style indirection; mini-infer, "Implementation Walkthrough":
+ *     the free-list stack; PagedAttention blog, "Architecture": a new block is
+ *     taken only when the last one is full).
+ *  2. A device KV pool that the caller allocates (one allocation for every
+ *     page, every layer, K and V combined: PageForge, "Four layers") and binds
+ *     to the allocator handle.  Page p is one contiguous region; inside it the
+ *     element (layer l, kv head h, kind c [K=0, V=1], slot o, dim d) sits at
+ *         ((((p*L + l)*H + h)*2 + c)*B + o)*D + d
+ *     so the K block and the V block of one (page, layer, head) are adjacent
+ *     B x D tiles.
+ *  3. HIP kernels: scatter of new tokens' K/V into their page slots (PageForge,
+ *     "Five techniques": gather / scatter kernels), a read-back gather, and
+ *     decode attention softmax(q.K^T.scale).V that walks each sequence's block
+ *     table (PagedAttention blog, "The Attention Kernel"; PageFault, "The OS
+ *     analogy": every K/V load goes through the table).
+ *
+ * Ownership: the library owns only the host handle.  Every device buffer (pool,
+ * q, k, v, tables, lengths, out, workspace) belongs to the caller; streams are
+ * passed as hipStream_t cast to void* (NULL = the default stream).  Kernel entry
+ * points only enqueue work: device faults surface at the caller's next
+ * synchronisation.  No function throws; every int result is a pf_status.
+ *
+ * Thread safety: allocator calls on one handle are serialised by an internal
+ * mutex.  Kernel entry points read the handle's geometry, bound pointer and
+ * options only; changing options or re-binding while kernels are being
+ * enqueued from another thread is the caller's race.
+ */
+#ifndef PF_H
+#define PF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the pool, q, k, v (and out unless out_dtype says PF_F32). */
+typedef enum { PF_F32 = 0, PF_F16 = 1, PF_BF16 = 2 } pf_dtype;
+
+typedef enum {
+  PF_OK = 0,
+  PF_ERR_INVALID = -1,      /* bad argument (range, null pointer, shape) */
+  PF_ERR_OOM = -2,          /* not enough free pages; nothing was changed */
+  PF_ERR_UNKNOWN_SEQ = -3,  /* sequence id not live (includes double free) */
+  PF_ERR_UNBOUND = -4,      /* kernel call before pf_pool_bind */
+  PF_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
+  PF_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
+  PF_ERR_UNSUPPORTED = -7   /* valid but not built: block size / head dim */
+} pf_status;
+
+typedef struct {
+  int32_t num_pages;     /* physical pages in the pool, >= 1 */
+  int32_t block_size;    /* tokens per page; kernels are built for 16 */
+  int32_t num_layers;    /* layers sharing the pool, >= 1 */
+  int32_t num_kv_heads;  /* kv heads per layer, >= 1 */
+  int32_t head_dim;      /* kernels: 16, 32, 64, 128 or 256 */
+  int32_t dtype;         /* pf_dtype */
+} pf_geometry;
+
+typedef struct pf_pool pf_pool; /* opaque, host-owned */
+
+/* ---------------------------------------------------------------- allocator */
+
+/* Create a handle.  initial_free_order (nullable) is a permutation of
+ * 0..num_pages-1 giving the order in which a fresh pool hands pages out
+ * (index 0 first); NULL means 0, 1, 2, ... (mini-infer, "Implementation
+ * Walkthrough": a fresh stack pops block 0 first).  A shuffled order models a
+ * pool after churn (PageFault, "Four stages", stage 3: ordered and shuffled
+ * frames).  *out receives the handle.  Errors: PF_ERR_INVALID. */
+int pf_pool_create(const pf_geometry* geom, const int32_t* initial_free_order, pf_pool** out);
+
+/* Destroy a handle (NULL is ignored).  Does not touch the bound device memory. */
+void pf_pool_destroy(pf_pool* pool);
+
+/* Bytes the device pool needs: num_pages * L * H * 2 * B * D * element size. */
+size_t pf_pool_bytes(const pf_pool* pool);
+
+/* Bytes of one page (all layers, heads, K and V). */
+size_t pf_page_bytes(const pf_pool* pool);
+
+/* Bind caller-owned device memory of at least pf_pool_bytes bytes, 256-byte
+ * aligned.  Errors: PF_ERR_INVALID (null, too small, misaligned). */
+int pf_pool_bind(pf_pool* pool, void* dev_ptr, size_t bytes);
+
+/* Grow sequence seq_id to new_len tokens in total, taking
+ * ceil(new_len/B) - (pages it has) pages from the top of the free stack and
+ * appending them to its table in pop order.  An unknown id creates the
+ * sequence.  *n_new_pages (nullable) receives the number of pages taken.
+ * Errors: PF_ERR_INVALID (new_len < 0 or below the current length),
+ * PF_ERR_OOM (not enough free pages: all or nothing, nothing changes; PageFault,
+ * "Test": exhaustion and all-or-nothing).  O(1) per page. */
+int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n_new_pages);
+
+/* Batch form of pf_alloc_for_seq for one decode step: grow seq_ids[i] to
+ * new_lens[i] for i = 0..n-1, in order, under one lock.  All or nothing over
+ * the whole batch: if any entry is invalid (PF_ERR_INVALID, checked first,
+ * against the lengths earlier entries would leave) or the pages do not suffice
+ * (PF_ERR_OOM), nothing changes.  n_new_pages (nullable) is [n].
+ * A sequence may appear more than once; later entries see earlier growth. */
+int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
+                      int32_t* n_new_pages);
+
+/* Return every page of seq_id to the free stack (last page first, so the
+ * sequence's first page ends on top) and forget the sequence.
+ * Errors: PF_ERR_UNKNOWN_SEQ (never allocated or already freed). */
+int pf_free_seq(pf_pool* pool, uint64_t seq_id);
+
+/* Pages currently on the free stack (-1 for a NULL handle). */
+int32_t pf_free_pages(const pf_pool* pool);
+
+/* Number of live sequences (-1 for a NULL handle). */
+int32_t pf_num_seqs(const pf_pool* pool);
+
+/* Current length of seq_id.  Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID. */
+int pf_seq_len(const pf_pool* pool, uint64_t seq_id, int32_t* len);
+
+/* Export dense host tables for n sequences: bt_host is [n][max_blocks] int32,
+ * row i = the block table of seq_ids[i] padded with -1; lens_host (nullable)
+ * is [n] int32 lengths.  Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID (a table
+ * longer than max_blocks, null pointers with n > 0). */
+int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                    int32_t* bt_host, int32_t* lens_host);
+
+/* ------------------------------------------------------------------ kernels */
+
+/* Write num_tokens tokens' K and V into their page slots for one layer.
+ *   k, v     device [num_tokens][H][D] in the pool dtype.
+ *   tok_seq  device [num_tokens] int32: row of bt_dev holding the token's table.
+ *   tok_pos  device [num_tokens] int32: the token's logical position.
+ *   bt_dev   device [num_rows][max_blocks] int32 block tables.
+ * Token t lands in page bt_dev[tok_seq[t]][tok_pos[t] / B], slot tok_pos[t] % B
+ * (PageFault, "The OS analogy").  A token whose row, position or table entry is
+ * out of range writes nothing (no access outside the pool).  Two tokens mapped
+ * to the same slot race.  Errors: PF_ERR_INVALID, PF_ERR_UNBOUND, PF_ERR_HIP. */
+int pf_scatter_kv(const pf_pool* pool, int32_t layer, const void* k, const void* v,
+                  const int32_t* tok_seq, const int32_t* tok_pos, int32_t num_tokens,
+                  const int32_t* bt_dev, int32_t num_rows, int32_t max_blocks, void* hip_stream);
+
+/* Read back sequences' K and V through their tables into contiguous buffers
+ * k_out, v_out: device [n][max_len][H][D] in the pool dtype (PageForge, "Five
+ * techniques": gather_kv assembles scattered pages into a contiguous view).
+ * Positions >= min(lens_dev[i], max_len) are not written.  Table entries that
+ * are not valid pages leave their tokens unwritten.
+ * Errors: PF_ERR_INVALID, PF_ERR_UNBOUND, PF_ERR_HIP. */
+int pf_gather_kv(const pf_pool* pool, int32_t layer, const int32_t* bt_dev, const int32_t* lens_dev,
+                 int32_t n, int32_t max_blocks, int32_t max_len, void* k_out, void* v_out,
+                 void* hip_stream);
+
+/* Workspace bytes pf_paged_decode_attention needs for these sizes under the
+ * handle's current options (0 means none is needed). */
+size_t pf_attention_workspace_bytes(const pf_pool* pool, int32_t n, int32_t num_q_heads,
+                                    int32_t max_context_len);
+
+/* Decode attention for one layer (PagedAttention blog, "The Attention Kernel";
+ * PageFault, "Four stages", stage 3): for every sequence i and query head h,
+ *     out[i][h] = softmax(scale * K_i q[i][h]) V_i
+ * over the first ctx_dev[i] tokens of sequence i, read through row i of bt_dev,
+ * with K_i, V_i of kv head h / (num_q_heads / H) (grouped-query heads are
+ * consecutive).  Tokens at positions >= the length are never read.
+ *   q        device [n][num_q_heads][D], pool dtype.
+ *   bt_dev   device [n][max_blocks] int32 tables (-1 padding is never read).
+ *   ctx_dev  device [n] int32 lengths; each is clamped to [0, max_context_len].
+ *   max_context_len  host bound on the lengths, <= max_blocks * B; sizes the grid.
+ *   scale    <= 0 selects 1/sqrt(D).
+ *   out      device [n][num_q_heads][D] in out_dtype (PF_F32 or the pool dtype).
+ *   workspace  device, >= pf_attention_workspace_bytes(...), 256-byte aligned
+ *            (nullable when that is 0); holds split-K partials.
+ * Math is fp32 with an online softmax; long contexts are split into fixed
+ * token ranges whose partials are merged by log-sum-exp in a second kernel, in
+ * a fixed order, so results depend only on logical positions (the same bits for
+ * any physical page order).  A length of 0 gives a zero output.  A table entry
+ * that is not a valid page contributes nothing (no access outside the pool).
+ * Errors: PF_ERR_INVALID, PF_ERR_UNBOUND, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED,
+ * PF_ERR_HIP. */
+int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                              const int32_t* bt_dev, int32_t max_blocks, const int32_t* ctx_dev,
+                              int32_t n, int32_t max_context_len, float scale, void* out,
+                              int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+
+/* ------------------------------------------------------------------ options */
+
+typedef enum {
+  PF_OPT_SPLIT_TOKENS = 0, /* tokens per context split (multiple of B); 0 = automatic */
+  PF_OPT_GQA_MFMA = 1      /* 1 (default): matrix-core kernel for grouped 16-bit heads; 0: vector kernel */
+} pf_option;
+
+/* Set / read a tuning option of a handle.  Errors: PF_ERR_INVALID. */
+int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value);
+int pf_pool_get_option(const pf_pool* pool, int32_t option, int32_t* value);
+
+/* Tokens per split the attention kernels will use for these sizes (the
+ * automatic choice or the option), for diagnostics and tests. */
+int32_t pf_attention_split_tokens(const pf_pool* pool, int32_t n, int32_t num_q_heads,
+                                  int32_t max_context_len);
+
+/* Instrumentation: when both are non-NULL, every later
+ * pf_paged_decode_attention call on this handle records start_event right
+ * before its partition kernel and stop_event right after it, on the call's
+ * stream (hipEvent_t values cast to void*, owned by the caller).  NULL, NULL
+ * turns it off.  Errors: PF_ERR_INVALID (NULL handle or only one event). */
+int pf_pool_set_timing_events(pf_pool* pool, void* start_event, void* stop_event);
+
+/* Static description of a status code. */
+const char* pf_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PF_H */

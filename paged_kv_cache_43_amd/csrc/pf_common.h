@@ -1,0 +1,126 @@
+// Device helpers shared by the libpf kernels: element types, raw vector loads,
+// wave64 cross-lane reductions.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pf {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;  // tokens per page the kernels are built for
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- elements
+// Stored element types.  Values are handled as raw bit patterns in 32-bit
+// words and widened to fp32 for arithmetic.
+struct ElF32 {
+  static constexpr int es = 4;
+  static constexpr int per_word = 1;
+  __device__ static inline void widen(uint32_t w, float* o) { o[0] = __uint_as_float(w); }
+  __device__ static inline uint32_t narrow_bits(float f) { return __float_as_uint(f); }
+};
+
+struct ElF16 {
+  static constexpr int es = 2;
+  static constexpr int per_word = 2;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  __device__ static inline void widen(uint32_t w, float* o) {
+    f2 f = __builtin_convertvector(__builtin_bit_cast(h2, w), f2);
+    o[0] = f.x;
+    o[1] = f.y;
+  }
+  __device__ static inline uint32_t narrow_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+  }
+};
+
+struct ElBF16 {
+  static constexpr int es = 2;
+  static constexpr int per_word = 2;
+  __device__ static inline void widen(uint32_t w, float* o) {
+    o[0] = __uint_as_float(w << 16);
+    o[1] = __uint_as_float(w & 0xffff0000u);
+  }
+  __device__ static inline uint32_t narrow_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);                                                  // nearest even
+    return u >> 16;
+  }
+};
+
+// ------------------------------------------------------------------ loads
+template <int NW>
+struct Raw {
+  uint32_t w[NW];
+};
+
+template <int NW>
+__device__ inline Raw<NW> load_raw(const void* p) {
+  Raw<NW> r;
+  if constexpr (NW == 4) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (NW == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+    static_assert(NW == 1, "load width");
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+  return r;
+}
+
+// ------------------------------------------------------- cross-lane moves
+// DPP controls (GFX9 encoding).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor = 0x120;     // + amount (1..15)
+
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ inline float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+struct OpSum {
+  __device__ static inline float f(float a, float b) { return a + b; }
+};
+struct OpMax {
+  __device__ static inline float f(float a, float b) { return fmaxf(a, b); }
+};
+
+// All-reduce over aligned groups of G consecutive lanes (G a power of two <= 64).
+template <int G, class Op>
+__device__ inline float group_reduce(float v) {
+  if constexpr (G >= 2) v = Op::f(v, dpp<kDppXor1>(v));
+  if constexpr (G >= 4) v = Op::f(v, dpp<kDppXor2>(v));
+  if constexpr (G >= 8) v = Op::f(v, dpp<kDppRowHalfMirror>(v));
+  if constexpr (G >= 16) v = Op::f(v, dpp<kDppRowMirror>(v));
+  if constexpr (G >= 32) v = Op::f(v, shfl_xor(v, 16));
+  if constexpr (G >= 64) v = Op::f(v, shfl_xor(v, 32));
+  return v;
+}
+
+// All-reduce over the lanes that share (lane % G): strides G, 2G, ..., 32.
+template <int G, class Op>
+__device__ inline float strided_reduce(float v) {
+  if constexpr (G <= 1) v = Op::f(v, dpp<kDppRowRor + 1>(v));
+  if constexpr (G <= 2) v = Op::f(v, dpp<kDppRowRor + 2>(v));
+  if constexpr (G <= 4) v = Op::f(v, dpp<kDppRowRor + 4>(v));
+  if constexpr (G <= 8) v = Op::f(v, dpp<kDppRowRor + 8>(v));
+  if constexpr (G <= 16) v = Op::f(v, shfl_xor(v, 16));
+  if constexpr (G <= 32) v = Op::f(v, shfl_xor(v, 32));
+  return v;
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pf

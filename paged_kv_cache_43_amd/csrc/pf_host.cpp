@@ -1,0 +1,264 @@
+// Host page allocator of libpf: an O(1) LIFO free list of fixed-size pages and
+// one block table per sequence.
+//
+// Follows PageForge, "Four layers, one pointer moving through all of them"
+// (a free list plus a sequence -> page-ids table behind one object whose
+// alloc_for_seq / free_seq are O(1) per page), mini-infer, "Implementation
+// Walkthrough" (the free list is a stack that hands out block 0 first from a
+// fresh pool, and an empty pool is an error), the PagedAttention blog,
+// "Architecture" (a block is taken only when the last one is full; tables only
+// grow) and PageFault, "Test" (exhaustion, double free and all-or-nothing are
+// checked).  Freed pages go back last-page-first so a sequence of the same shape
+// allocated next gets the same pages in the same order (PageForge, "Does the
+// pool actually come back to zero?": batch 2 claims batch 1's pages).
+#include <cstring>
+#include <limits>
+#include <new>
+
+#include "pf_internal.h"
+
+size_t pf_elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PF_F32: return 4;
+    case PF_F16: return 2;
+    case PF_BF16: return 2;
+    default: return 0;
+  }
+}
+
+static bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > std::numeric_limits<size_t>::max() / a) return false;
+  *out = a * b;
+  return true;
+}
+
+extern "C" {
+
+int pf_pool_create(const pf_geometry* geom, const int32_t* initial_free_order, pf_pool** out) {
+  if (!geom || !out) return PF_ERR_INVALID;
+  *out = nullptr;
+  const pf_geometry& g = *geom;
+  if (g.num_pages <= 0 || g.block_size <= 0 || g.num_layers <= 0 || g.num_kv_heads <= 0 ||
+      g.head_dim <= 0 || pf_elem_bytes(g.dtype) == 0)
+    return PF_ERR_INVALID;
+  size_t pe = 1;
+  if (!mul_ok(pe, (size_t)g.num_layers, &pe) || !mul_ok(pe, (size_t)g.num_kv_heads, &pe) ||
+      !mul_ok(pe, 2, &pe) || !mul_ok(pe, (size_t)g.block_size, &pe) ||
+      !mul_ok(pe, (size_t)g.head_dim, &pe))
+    return PF_ERR_INVALID;
+  size_t total = 0;
+  if (!mul_ok(pe, (size_t)g.num_pages, &total) || !mul_ok(total, pf_elem_bytes(g.dtype), &total))
+    return PF_ERR_INVALID;
+  pf_pool* p = new (std::nothrow) pf_pool();
+  if (!p) return PF_ERR_INVALID;
+  p->g = g;
+  p->elem_bytes = pf_elem_bytes(g.dtype);
+  p->page_elems = pe;
+  p->stack.resize((size_t)g.num_pages);
+  if (initial_free_order) {
+    std::vector<uint8_t> seen((size_t)g.num_pages, 0);
+    for (int32_t i = 0; i < g.num_pages; ++i) {
+      int32_t v = initial_free_order[i];
+      if (v < 0 || v >= g.num_pages || seen[(size_t)v]) {
+        delete p;
+        return PF_ERR_INVALID;
+      }
+      seen[(size_t)v] = 1;
+    }
+  }
+  // order[0] must pop first: it goes on top, i.e. at the back.
+  for (int32_t i = 0; i < g.num_pages; ++i)
+    p->stack[(size_t)(g.num_pages - 1 - i)] = initial_free_order ? initial_free_order[i] : i;
+  *out = p;
+  return PF_OK;
+}
+
+void pf_pool_destroy(pf_pool* pool) { delete pool; }
+
+size_t pf_page_bytes(const pf_pool* pool) { return pool ? pool->page_elems * pool->elem_bytes : 0; }
+
+size_t pf_pool_bytes(const pf_pool* pool) {
+  return pool ? pool->page_elems * pool->elem_bytes * (size_t)pool->g.num_pages : 0;
+}
+
+int pf_pool_bind(pf_pool* pool, void* dev_ptr, size_t bytes) {
+  if (!pool || !dev_ptr) return PF_ERR_INVALID;
+  if (bytes < pf_pool_bytes(pool)) return PF_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(dev_ptr) % 256 != 0) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  pool->dev = dev_ptr;
+  pool->dev_bytes = bytes;
+  return PF_OK;
+}
+
+int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n_new_pages) {
+  if (n_new_pages) *n_new_pages = 0;
+  if (!pool || new_len < 0) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq_id);
+  const int32_t cur_len = it == pool->seqs.end() ? 0 : it->second.len;
+  const size_t have = it == pool->seqs.end() ? 0 : it->second.pages.size();
+  if (new_len < cur_len) return PF_ERR_INVALID;
+  const int64_t B = pool->g.block_size;
+  const size_t want = (size_t)(((int64_t)new_len + B - 1) / B);
+  const size_t need = want - have;
+  if (need > pool->stack.size()) return PF_ERR_OOM;  // all or nothing
+  pf_seq_entry& e = it == pool->seqs.end() ? pool->seqs[seq_id] : it->second;
+  e.pages.reserve(want);
+  for (size_t i = 0; i < need; ++i) {
+    e.pages.push_back(pool->stack.back());
+    pool->stack.pop_back();
+  }
+  e.len = new_len;
+  if (n_new_pages) *n_new_pages = (int32_t)need;
+  return PF_OK;
+}
+
+int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
+                      int32_t* n_new_pages) {
+  if (!pool || n < 0 || (n > 0 && (!seq_ids || !new_lens))) return PF_ERR_INVALID;
+  if (n_new_pages)
+    for (int32_t i = 0; i < n; ++i) n_new_pages[i] = 0;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  const int64_t B = pool->g.block_size;
+  // Validation pass: lengths and page counts as the batch would leave them.
+  std::unordered_map<uint64_t, std::pair<int32_t, size_t>> pending;  // id -> (len, pages)
+  size_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (new_lens[i] < 0) return PF_ERR_INVALID;
+    auto pit = pending.find(seq_ids[i]);
+    int32_t cur_len;
+    size_t have;
+    if (pit != pending.end()) {
+      cur_len = pit->second.first;
+      have = pit->second.second;
+    } else {
+      auto it = pool->seqs.find(seq_ids[i]);
+      cur_len = it == pool->seqs.end() ? 0 : it->second.len;
+      have = it == pool->seqs.end() ? 0 : it->second.pages.size();
+    }
+    if (new_lens[i] < cur_len) return PF_ERR_INVALID;
+    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+    total += want - have;
+    pending[seq_ids[i]] = {new_lens[i], want};
+  }
+  if (total > pool->stack.size()) return PF_ERR_OOM;
+  for (int32_t i = 0; i < n; ++i) {
+    pf_seq_entry& e = pool->seqs[seq_ids[i]];
+    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+    const size_t need = want - e.pages.size();
+    for (size_t j = 0; j < need; ++j) {
+      e.pages.push_back(pool->stack.back());
+      pool->stack.pop_back();
+    }
+    e.len = new_lens[i];
+    if (n_new_pages) n_new_pages[i] = (int32_t)need;
+  }
+  return PF_OK;
+}
+
+int pf_free_seq(pf_pool* pool, uint64_t seq_id) {
+  if (!pool) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq_id);
+  if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+  const std::vector<int32_t>& pages = it->second.pages;
+  for (size_t i = pages.size(); i-- > 0;) pool->stack.push_back(pages[i]);
+  pool->seqs.erase(it);
+  return PF_OK;
+}
+
+int32_t pf_free_pages(const pf_pool* pool) {
+  if (!pool) return -1;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  return (int32_t)pool->stack.size();
+}
+
+int32_t pf_num_seqs(const pf_pool* pool) {
+  if (!pool) return -1;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  return (int32_t)pool->seqs.size();
+}
+
+int pf_seq_len(const pf_pool* pool, uint64_t seq_id, int32_t* len) {
+  if (!pool || !len) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq_id);
+  if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+  *len = it->second.len;
+  return PF_OK;
+}
+
+int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                    int32_t* bt_host, int32_t* lens_host) {
+  if (!pool || n < 0 || max_blocks < 0) return PF_ERR_INVALID;
+  if (n > 0 && (!seq_ids || (!bt_host && max_blocks > 0))) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seq_ids[i]);
+    if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+    if (it->second.pages.size() > (size_t)max_blocks) return PF_ERR_INVALID;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pf_seq_entry& e = pool->seqs.find(seq_ids[i])->second;
+    int32_t* row = bt_host + (size_t)i * (size_t)max_blocks;
+    const size_t np = e.pages.size();
+    if (np) std::memcpy(row, e.pages.data(), np * sizeof(int32_t));
+    for (size_t j = np; j < (size_t)max_blocks; ++j) row[j] = -1;
+    if (lens_host) lens_host[i] = e.len;
+  }
+  return PF_OK;
+}
+
+int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {
+  if (!pool) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  switch (option) {
+    case PF_OPT_SPLIT_TOKENS:
+      if (value < 0 || (value > 0 && (value % pool->g.block_size != 0 ||
+                                      value > 64 * pool->g.block_size)))
+        return PF_ERR_INVALID;
+      pool->split_tokens = value;
+      return PF_OK;
+    case PF_OPT_GQA_MFMA:
+      if (value != 0 && value != 1) return PF_ERR_INVALID;
+      pool->gqa_mfma = value;
+      return PF_OK;
+    default:
+      return PF_ERR_INVALID;
+  }
+}
+
+int pf_pool_get_option(const pf_pool* pool, int32_t option, int32_t* value) {
+  if (!pool || !value) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  switch (option) {
+    case PF_OPT_SPLIT_TOKENS: *value = pool->split_tokens; return PF_OK;
+    case PF_OPT_GQA_MFMA: *value = pool->gqa_mfma; return PF_OK;
+    default: return PF_ERR_INVALID;
+  }
+}
+
+int pf_pool_set_timing_events(pf_pool* pool, void* start_event, void* stop_event) {
+  if (!pool || ((start_event == nullptr) != (stop_event == nullptr))) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  pool->ev_start = start_event;
+  pool->ev_stop = stop_event;
+  return PF_OK;
+}
+
+const char* pf_status_string(int status) {
+  switch (status) {
+    case PF_OK: return "ok";
+    case PF_ERR_INVALID: return "invalid argument";
+    case PF_ERR_OOM: return "out of free pages (nothing changed)";
+    case PF_ERR_UNKNOWN_SEQ: return "unknown sequence id";
+    case PF_ERR_UNBOUND: return "no device pool bound";
+    case PF_ERR_WORKSPACE: return "workspace missing or too small";
+    case PF_ERR_HIP: return "HIP runtime error";
+    case PF_ERR_UNSUPPORTED: return "unsupported block size or head dim";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Internal definition of the pf_pool handle, shared by the host allocator
+// (pf_host.cpp) and the kernel entry points (pf_kernels.hip).  Not part of
+// the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <mutex>
+#include <unordered_map>
+#include <vector>
+
+#include "pf.h"
+
+struct pf_seq_entry {
+  std::vector<int32_t> pages;  // block table: logical block i -> physical page
+  int32_t len = 0;             // tokens held
+};
+
+struct pf_pool {
+  pf_geometry g{};
+  size_t elem_bytes = 0;
+  size_t page_elems = 0;       // L * H * 2 * B * D
+  // LIFO free stack of page ids; the top is the back of the vector.
+  std::vector<int32_t> stack;
+  std::unordered_map<uint64_t, pf_seq_entry> seqs;
+  mutable std::mutex mu;
+  // Caller-owned device memory bound with pf_pool_bind.
+  void* dev = nullptr;
+  size_t dev_bytes = 0;
+  // Tuning options (pf_pool_set_option).
+  int32_t split_tokens = 0;
+  int32_t gqa_mfma = 1;
+  // Instrumentation events around the partition kernel (hipEvent_t).
+  void* ev_start = nullptr;
+  void* ev_stop = nullptr;
+};
+
+size_t pf_elem_bytes(int32_t dtype);

@@ -1,0 +1,167 @@
+// scatter_kv and gather_kv: moving tokens' K/V into and out of their pages.
+//
+// PageForge, "Five techniques" (gather / scatter kernels): new tokens' K/V are
+// written into their physical pages, and a gather assembles a sequence's
+// scattered pages into one contiguous view.  Here the gather is only a
+// read-back for verification; attention reads the pages in place.
+//
+// Pool layout (see include/pf.h): page p, layer l, kv head h, kind c (K=0,
+// V=1), slot o, dim d at ((((p*L + l)*H + h)*2 + c)*B + o)*D + d.  Both kernels
+// move 16-byte chunks: one thread per (token, head, kind, 16-byte column), so
+// a token's D-vector is written by D*es/16 adjacent threads into one
+// contiguous row of its page.
+#include "pf_common.h"
+#include "pf_internal.h"
+
+namespace pf {
+
+struct KvArgs {
+  uint8_t* pool;
+  const uint8_t* k;        // scatter: source [T][H][D]
+  const uint8_t* v;
+  uint8_t* k_out;          // gather: destination [n][max_len][H][D]
+  uint8_t* v_out;
+  const int32_t* tok_seq;
+  const int32_t* tok_pos;
+  const int32_t* bt;
+  const int32_t* lens;
+  int64_t total;           // threads of work
+  int64_t page_elems;
+  int32_t layer, L, H, D, B, es, num_pages, rows, max_blocks, max_len;
+};
+
+__global__ __launch_bounds__(256) void scatter_kv_kernel(KvArgs a) {
+  const int cols = a.D * a.es / 16;  // 16-byte columns per token row
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int col = (int)(i % cols);
+    int64_t r = i / cols;
+    const int kind = (int)(r % 2);
+    r /= 2;
+    const int h = (int)(r % a.H);
+    const int64_t t = r / a.H;
+    const int32_t seq = a.tok_seq[t];
+    const int32_t pos = a.tok_pos[t];
+    if (seq < 0 || seq >= a.rows || pos < 0 || (int64_t)pos >= (int64_t)a.max_blocks * a.B) continue;
+    const int32_t page = a.bt[(int64_t)seq * a.max_blocks + pos / a.B];
+    if (page < 0 || page >= a.num_pages) continue;
+    const int64_t dst_el = (int64_t)page * a.page_elems +
+                           ((((int64_t)a.layer * a.H + h) * 2 + kind) * a.B + pos % a.B) * a.D;
+    const int64_t src_el = (t * a.H + h) * (int64_t)a.D;
+    const uint8_t* src = (kind ? a.v : a.k) + src_el * a.es + col * 16;
+    uint8_t* dst = a.pool + dst_el * a.es + col * 16;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_kv_kernel(KvArgs a) {
+  const int cols = a.D * a.es / 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int col = (int)(i % cols);
+    int64_t r = i / cols;
+    const int kind = (int)(r % 2);
+    r /= 2;
+    const int h = (int)(r % a.H);
+    r /= a.H;
+    const int pos = (int)(r % a.max_len);
+    const int64_t s = r / a.max_len;
+    int32_t len = a.lens[s];
+    if (len > a.max_len) len = a.max_len;
+    if (pos >= len || (int64_t)pos >= (int64_t)a.max_blocks * a.B) continue;
+    const int32_t page = a.bt[s * a.max_blocks + pos / a.B];
+    if (page < 0 || page >= a.num_pages) continue;
+    const int64_t src_el = (int64_t)page * a.page_elems +
+                           ((((int64_t)a.layer * a.H + h) * 2 + kind) * a.B + pos % a.B) * a.D;
+    const int64_t dst_el = ((s * a.max_len + pos) * a.H + h) * (int64_t)a.D;
+    uint8_t* dst = (kind ? a.v_out : a.k_out) + dst_el * a.es + col * 16;
+    *reinterpret_cast<uint4*>(dst) =
+        *reinterpret_cast<const uint4*>(a.pool + src_el * a.es + col * 16);
+  }
+}
+
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+static int launch_grid(int64_t total, int* blocks) {
+  int64_t b = (total + 255) / 256;
+  if (b > 65536) b = 65536;  // grid-stride beyond this
+  if (b < 1) b = 1;
+  *blocks = (int)b;
+  return 0;
+}
+
+}  // namespace pf
+
+extern "C" int pf_scatter_kv(const pf_pool* pool, int32_t layer, const void* k, const void* v,
+                             const int32_t* tok_seq, const int32_t* tok_pos, int32_t num_tokens,
+                             const int32_t* bt_dev, int32_t num_rows, int32_t max_blocks,
+                             void* hip_stream) {
+  using namespace pf;
+  if (!pool) return PF_ERR_INVALID;
+  if (!pool->dev) return PF_ERR_UNBOUND;
+  const pf_geometry& g = pool->g;
+  if (layer < 0 || layer >= g.num_layers || num_tokens < 0 || num_rows < 0 || max_blocks < 0)
+    return PF_ERR_INVALID;
+  if ((size_t)g.head_dim * pool->elem_bytes % 16 != 0) return PF_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PF_OK;
+  if (!k || !v || !tok_seq || !tok_pos || !bt_dev || !aligned16(k) || !aligned16(v))
+    return PF_ERR_INVALID;
+  KvArgs a{};
+  a.pool = static_cast<uint8_t*>(pool->dev);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.tok_seq = tok_seq;
+  a.tok_pos = tok_pos;
+  a.bt = bt_dev;
+  a.page_elems = (int64_t)pool->page_elems;
+  a.layer = layer;
+  a.L = g.num_layers;
+  a.H = g.num_kv_heads;
+  a.D = g.head_dim;
+  a.B = g.block_size;
+  a.es = (int32_t)pool->elem_bytes;
+  a.num_pages = g.num_pages;
+  a.rows = num_rows;
+  a.max_blocks = max_blocks;
+  a.total = (int64_t)num_tokens * g.num_kv_heads * 2 * (g.head_dim * a.es / 16);
+  int blocks;
+  launch_grid(a.total, &blocks);
+  hipLaunchKernelGGL(scatter_kv_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream, a);
+  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}
+
+extern "C" int pf_gather_kv(const pf_pool* pool, int32_t layer, const int32_t* bt_dev,
+                            const int32_t* lens_dev, int32_t n, int32_t max_blocks, int32_t max_len,
+                            void* k_out, void* v_out, void* hip_stream) {
+  using namespace pf;
+  if (!pool) return PF_ERR_INVALID;
+  if (!pool->dev) return PF_ERR_UNBOUND;
+  const pf_geometry& g = pool->g;
+  if (layer < 0 || layer >= g.num_layers || n < 0 || max_blocks < 0 || max_len < 0)
+    return PF_ERR_INVALID;
+  if ((size_t)g.head_dim * pool->elem_bytes % 16 != 0) return PF_ERR_UNSUPPORTED;
+  if (n == 0 || max_len == 0) return PF_OK;
+  if (!bt_dev || !lens_dev || !k_out || !v_out || !aligned16(k_out) || !aligned16(v_out))
+    return PF_ERR_INVALID;
+  KvArgs a{};
+  a.pool = static_cast<uint8_t*>(pool->dev);
+  a.k_out = static_cast<uint8_t*>(k_out);
+  a.v_out = static_cast<uint8_t*>(v_out);
+  a.bt = bt_dev;
+  a.lens = lens_dev;
+  a.page_elems = (int64_t)pool->page_elems;
+  a.layer = layer;
+  a.L = g.num_layers;
+  a.H = g.num_kv_heads;
+  a.D = g.head_dim;
+  a.B = g.block_size;
+  a.es = (int32_t)pool->elem_bytes;
+  a.num_pages = g.num_pages;
+  a.max_blocks = max_blocks;
+  a.max_len = max_len;
+  a.total = (int64_t)n * max_len * g.num_kv_heads * 2 * (g.head_dim * a.es / 16);
+  int blocks;
+  launch_grid(a.total, &blocks);
+  hipLaunchKernelGGL(gather_kv_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream, a);
+  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}

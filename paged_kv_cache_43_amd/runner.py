@@ -1,0 +1,140 @@
+"""Drive libpf for a workload: device pool, allocator handle, table export,
+scatter and attention.  PyTorch supplies device memory, host staging and the
+stream; every step of the method runs in libpf (``pf``).
+"""
+import numpy as np
+import torch
+
+from . import inputs
+from . import pf
+
+_BITS_TORCH = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
+_BITS_NP = {"f32": np.int32, "f16": np.int16, "bf16": np.int16}
+
+
+def bits_to_device(bits, device="cuda"):
+    """Upload raw bit patterns (uint16/uint32 numpy) without any conversion."""
+    signed = bits.view(np.int32 if bits.dtype == np.uint32 else np.int16)
+    return torch.from_numpy(np.ascontiguousarray(signed)).to(device)
+
+
+def bits_from_device(t):
+    a = t.cpu().numpy()
+    return a.view(np.uint32 if a.dtype == np.int32 else np.uint16)
+
+
+class PagedKV:
+    """A pool handle bound to a torch-allocated device pool, plus device tables."""
+
+    def __init__(self, w, device="cuda", sentinel=True, extra_tokens=0, max_blocks=None):
+        self.w = w
+        self.device = device
+        st, self.h = pf.pf_pool_create(w.num_pages, w.block, w.layers, w.hkv, w.d, w.dtype,
+                                       w.free_order)
+        pf.check(st, "pf_pool_create")
+        nbytes = pf.pf_pool_bytes(self.h)
+        self.pool = torch.empty(nbytes // inputs.DTYPE_BYTES[w.dtype], dtype=_BITS_TORCH[w.dtype],
+                                device=device)
+        if sentinel:
+            nan = inputs.NAN_BITS[w.dtype]
+            self.pool.fill_(int(np.array(nan, dtype=np.uint32 if w.es == 4 else np.uint16)
+                                .view(_BITS_NP[w.dtype])))
+        pf.check(pf.pf_pool_bind(self.h, self.pool, nbytes), "pf_pool_bind")
+        self.max_blocks = max_blocks or w.max_blocks(extra_tokens)
+        self.ids = list(range(w.n))
+        self.bt_host = torch.empty((w.n, self.max_blocks), dtype=torch.int32).pin_memory() \
+            if torch.cuda.is_available() else torch.empty((w.n, self.max_blocks), dtype=torch.int32)
+        self.len_host = torch.empty(w.n, dtype=torch.int32).pin_memory() \
+            if torch.cuda.is_available() else torch.empty(w.n, dtype=torch.int32)
+        self.bt = torch.empty((w.n, self.max_blocks), dtype=torch.int32, device=device)
+        self.ctx = torch.empty(w.n, dtype=torch.int32, device=device)
+        self.ws = None
+        self.ws_bytes = 0
+
+    def close(self):
+        if self.h is not None:
+            pf.pf_pool_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -------------------------------------------------------------- host ops
+    def apply(self, ops):
+        for op in ops:
+            if op[0] == "alloc":
+                st, _ = pf.pf_alloc_for_seq(self.h, op[1], op[2])
+                pf.check(st, "pf_alloc_for_seq")
+            else:
+                pf.check(pf.pf_free_seq(self.h, op[1]), "pf_free_seq")
+
+    def export_tables(self, stream=None):
+        """Block tables and lengths of sequences 0..n-1 into pinned host memory,
+        then one asynchronous copy each to the device."""
+        st, _, _ = pf.pf_block_tables(self.h, self.ids, self.max_blocks, self.bt_host.numpy(),
+                                      self.len_host.numpy())
+        pf.check(st, "pf_block_tables")
+        self.bt.copy_(self.bt_host, non_blocking=True)
+        self.ctx.copy_(self.len_host, non_blocking=True)
+
+    # --------------------------------------------------------------- kernels
+    def scatter(self, layer, k, v, tok_seq, tok_pos, stream=None):
+        st = pf.pf_scatter_kv(self.h, layer, k, v, tok_seq, tok_pos, int(tok_seq.numel()), self.bt,
+                              self.w.n, self.max_blocks, stream)
+        pf.check(st, "pf_scatter_kv")
+
+    def ensure_workspace(self, max_ctx, hq=None):
+        need = pf.pf_attention_workspace_bytes(self.h, self.w.n, hq or self.w.hq, max_ctx)
+        if need > self.ws_bytes:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self.ws_bytes = need
+        return need
+
+    def attention(self, layer, q, out, max_ctx, out_dtype=None, scale=0.0, stream=None, hq=None):
+        hq = hq or self.w.hq
+        self.ensure_workspace(max_ctx, hq)
+        st = pf.pf_paged_decode_attention(self.h, layer, q, hq, self.bt, self.max_blocks, self.ctx,
+                                          self.w.n, max_ctx, scale, out,
+                                          out_dtype or self.w.dtype, self.ws, self.ws_bytes, stream)
+        pf.check(st, "pf_paged_decode_attention")
+
+    def gather(self, layer, max_len, stream=None):
+        w = self.w
+        k = torch.empty((w.n, max_len, w.hkv, w.d), dtype=_BITS_TORCH[w.dtype], device=self.device)
+        v = torch.empty_like(k)
+        st = pf.pf_gather_kv(self.h, layer, self.bt, self.ctx, w.n, self.max_blocks, max_len, k, v,
+                             stream)
+        pf.check(st, "pf_gather_kv")
+        return k, v
+
+
+def token_arrays(w, positions):
+    """Flattened (tok_seq, tok_pos) for ``positions[s]`` = iterable of positions."""
+    seq, pos = [], []
+    for s, ps in enumerate(positions):
+        for p in ps:
+            seq.append(s)
+            pos.append(p)
+    return np.array(seq, dtype=np.int32), np.array(pos, dtype=np.int32)
+
+
+def fill_workload(kv, device="cuda"):
+    """Replay the workload's history and measured-step allocations, export the
+    tables and scatter every context token's K/V of every layer.  Returns the
+    device q [L][n][Hq][D] bits."""
+    w = kv.w
+    kv.apply(w.history_ops + w.step_ops)
+    kv.export_tables()
+    ks, vs, q = w.values()
+    tok_seq, tok_pos = token_arrays(w, [range(int(c)) for c in w.ctx])
+    ts = torch.from_numpy(tok_seq).to(device)
+    tp = torch.from_numpy(tok_pos).to(device)
+    for layer in range(w.layers):
+        k = np.concatenate([ks[s][layer] for s in range(w.n)]) if w.n else None
+        v = np.concatenate([vs[s][layer] for s in range(w.n)]) if w.n else None
+        if len(tok_seq):
+            kv.scatter(layer, bits_to_device(k, device), bits_to_device(v, device), ts, tp)
+    return bits_to_device(q, device)

@@ -1,0 +1,290 @@
+"""Host side of libpf on the CPU: every symbol of include/pf.h is exported, and
+the allocator reproduces the oracle's block tables bit for bit.  No kernel is
+launched here (kernel entry points are only called with arguments they reject
+before touching the GPU)."""
+import re
+import subprocess
+import threading
+
+import numpy as np
+import pytest
+
+import oracle.alloc_model as am
+from paged_kv_cache_43_amd import inputs
+
+pf = pytest.importorskip("paged_kv_cache_43_amd.pf", reason="libpf.so not built")
+
+HEADER = open(__import__("os").path.join(__import__("os").path.dirname(__file__), "..", "include", "pf.h")).read()
+DECLARED = sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+)+\**(pf_\w+)\s*\(", HEADER, re.M)))
+
+STATUS = {pf.PF_OK: am.OK, pf.PF_ERR_OOM: am.OOM, pf.PF_ERR_UNKNOWN_SEQ: am.UNKNOWN_SEQ,
+          pf.PF_ERR_INVALID: am.INVALID}
+
+
+def test_header_declares_the_abi():
+    for name in ("pf_pool_create", "pf_alloc_for_seq", "pf_free_seq", "pf_scatter_kv",
+                 "pf_paged_decode_attention", "pf_gather_kv", "pf_block_tables"):
+        assert name in DECLARED
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", pf._LIB_PATH], stdout=subprocess.PIPE,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pf_\w+)", out))
+    missing = [n for n in DECLARED if n not in exported]
+    assert not missing, missing
+    for n in DECLARED:
+        getattr(pf.lib, n)
+    assert sorted(pf.EXPORTED) == DECLARED
+
+
+def _make(num_pages, order=None, block=16):
+    st, h = pf.pf_pool_create(num_pages, block, 1, 1, 16, "f16", order)
+    assert st == pf.PF_OK
+    return h
+
+
+def _tables_equal(h, model):
+    ids = sorted(model.tables)
+    if not ids:
+        return
+    mb = max(1, max(len(model.tables[s]) for s in ids))
+    st, bt, lens = pf.pf_block_tables(h, ids, mb)
+    assert st == pf.PF_OK
+    rows, mlens = model.block_tables(ids, mb)
+    assert np.array_equal(bt, np.array(rows, dtype=np.int32))
+    assert list(lens) == mlens
+
+
+def _random_ops(rng, n_ops, num_pages, n_ids=12, max_len=300):
+    ops = []
+    lens = {}
+    for _ in range(n_ops):
+        r = rng.random()
+        s = int(rng.integers(0, n_ids))
+        if r < 0.65:
+            cur = lens.get(s, 0)
+            if rng.random() < 0.05:
+                new = cur - 1                      # invalid: shrink
+            else:
+                new = cur + int(rng.integers(0, 40))
+            if rng.random() < 0.02:
+                new = num_pages * 16 + 1           # certain OOM
+            ops.append(("alloc", s, new))
+            if new >= cur and new <= max_len * 4:
+                lens[s] = max(new, cur)
+        else:
+            ops.append(("free", s))
+            lens.pop(s, None)
+    return ops
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_allocator_replays_oracle_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    P = 96
+    order = rng.permutation(P) if seed % 2 else None
+    h = _make(P, order)
+    model = am.AllocModel(P, 16, order)
+    for op in _random_ops(rng, 1500, P):
+        if op[0] == "alloc":
+            st, nn = pf.pf_alloc_for_seq(h, op[1], op[2])
+            mst, mnn = model.alloc(op[1], op[2])
+            assert (STATUS[st], nn) == (mst, mnn), op
+        else:
+            st = pf.pf_free_seq(h, op[1])
+            assert STATUS[st] == model.free(op[1]), op
+        assert pf.pf_free_pages(h) == model.free_pages()
+        assert pf.pf_num_seqs(h) == len(model.tables)
+    _tables_equal(h, model)
+    model.check_invariants()
+    pf.pf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("name,frames", [("tiny", "shuffled"), ("gpt2", "shuffled"), ("gpt2", "ordered"),
+                                         ("mixed", "ordered"), ("13b", "shuffled"), ("gqa", "shuffled")])
+def test_workload_histories_match_oracle(name, frames):
+    w = inputs.Workload(name, frames=frames)
+    h = _make(w.num_pages, w.free_order)
+    model = am.AllocModel(w.num_pages, 16, w.free_order)
+    for op in w.history_ops + w.step_ops:
+        if op[0] == "alloc":
+            st, nn = pf.pf_alloc_for_seq(h, op[1], op[2])
+            assert (STATUS[st], nn) == model.alloc(op[1], op[2])
+        else:
+            assert STATUS[pf.pf_free_seq(h, op[1])] == model.free(op[1])
+    _tables_equal(h, model)
+    model.check_invariants()
+    # every sequence holds ceil(len/16) pages; free + used == pool
+    used = sum(len(t) for t in model.tables.values())
+    assert pf.pf_free_pages(h) + used == w.num_pages
+    for s in range(w.n):
+        assert pf.pf_free_seq(h, s) == pf.PF_OK
+    assert pf.pf_free_pages(h) == w.num_pages and pf.pf_num_seqs(h) == 0
+    pf.pf_pool_destroy(h)
+
+
+def test_churn_500_cycles_no_leaks():
+    rng = np.random.default_rng(7)
+    ops = inputs.churn_ops(rng, 500, 16, 512)
+    h = _make(512, rng.permutation(512))
+    ooms = 0
+    for op in ops:
+        if op[0] == "alloc":
+            st, _ = pf.pf_alloc_for_seq(h, op[1], op[2])
+            ooms += st == pf.PF_ERR_OOM
+            assert st in (pf.PF_OK, pf.PF_ERR_OOM)
+        else:
+            assert pf.pf_free_seq(h, op[1]) == pf.PF_OK
+    assert ooms == 0 and pf.pf_free_pages(h) == 512 and pf.pf_num_seqs(h) == 0
+    pf.pf_pool_destroy(h)
+
+
+def test_errors_and_all_or_nothing():
+    assert pf.pf_pool_create(0, 16, 1, 1, 16, "f16")[0] == pf.PF_ERR_INVALID
+    assert pf.pf_pool_create(4, 16, 1, 1, 16, 9)[0] == pf.PF_ERR_INVALID
+    assert pf.pf_pool_create(4, 16, 1, 1, 16, "f16", [0, 1, 1, 3])[0] == pf.PF_ERR_INVALID
+    assert pf.pf_pool_create(4, 16, 1, 1, 16, "f16", [0, 1, 2, 4])[0] == pf.PF_ERR_INVALID
+    h = _make(10)
+    assert pf.pf_alloc_for_seq(h, 1, -1)[0] == pf.PF_ERR_INVALID
+    assert pf.pf_alloc_for_seq(h, 1, 96) == (pf.PF_OK, 6)
+    assert pf.pf_alloc_for_seq(h, 2, 80) == (pf.PF_ERR_OOM, 0)
+    assert pf.pf_num_seqs(h) == 1 and pf.pf_free_pages(h) == 4
+    assert pf.pf_alloc_for_seq(h, 1, 95)[0] == pf.PF_ERR_INVALID
+    assert pf.pf_seq_len(h, 1) == (pf.PF_OK, 96)
+    assert pf.pf_seq_len(h, 2)[0] == pf.PF_ERR_UNKNOWN_SEQ
+    assert pf.pf_free_seq(h, 1) == pf.PF_OK
+    assert pf.pf_free_seq(h, 1) == pf.PF_ERR_UNKNOWN_SEQ
+    st, bt, lens = pf.pf_block_tables(h, [1], 4)
+    assert st == pf.PF_ERR_UNKNOWN_SEQ
+    pf.pf_alloc_for_seq(h, 5, 70)
+    assert pf.pf_block_tables(h, [5], 4)[0] == pf.PF_ERR_INVALID   # needs 5 blocks
+    st, bt, lens = pf.pf_block_tables(h, [5], 6)
+    assert st == pf.PF_OK and list(bt[0][-1:]) == [-1] and lens[0] == 70
+    # options
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SPLIT_TOKENS, 24) == pf.PF_ERR_INVALID
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SPLIT_TOKENS, 64 * 16 + 16) == pf.PF_ERR_INVALID
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SPLIT_TOKENS, 128) == pf.PF_OK
+    assert pf.pf_pool_get_option(h, pf.PF_OPT_SPLIT_TOKENS) == (pf.PF_OK, 128)
+    assert pf.pf_pool_set_option(h, 99, 1) == pf.PF_ERR_INVALID
+    pf.pf_pool_destroy(h)
+
+
+def test_kernel_entry_points_validate_before_launch():
+    h = _make(8)
+    # unbound pool
+    assert pf.pf_scatter_kv(h, 0, 16, 16, 16, 16, 1, 16, 1, 1, stream=0) == pf.PF_ERR_UNBOUND
+    assert pf.pf_gather_kv(h, 0, 16, 16, 1, 1, 16, 16, 16, stream=0) == pf.PF_ERR_UNBOUND
+    assert pf.pf_paged_decode_attention(h, 0, 256, 1, 256, 1, 256, 1, 16, 0.0, 256, "f16", None, 0,
+                                        stream=0) == pf.PF_ERR_UNBOUND
+    # a fake, never dereferenced, 256-aligned address only to get past the bind checks
+    fake = 1 << 40
+    assert pf.pf_pool_bind(h, fake, pf.pf_pool_bytes(h) - 1) == pf.PF_ERR_INVALID
+    assert pf.pf_pool_bind(h, fake + 8, pf.pf_pool_bytes(h)) == pf.PF_ERR_INVALID
+    assert pf.pf_pool_bind(h, fake, pf.pf_pool_bytes(h)) == pf.PF_OK
+    A = fake
+    call = lambda **kw: pf.pf_paged_decode_attention(
+        h, kw.get("layer", 0), A, kw.get("hq", 1), A, kw.get("mb", 1), A, kw.get("n", 1),
+        kw.get("mc", 16), 0.0, A, kw.get("od", "f16"), kw.get("ws", None), kw.get("wsb", 0), stream=0)
+    assert call(layer=1) == pf.PF_ERR_INVALID
+    assert call(hq=0) == pf.PF_ERR_INVALID
+    assert call(mc=17) == pf.PF_ERR_INVALID            # beyond max_blocks * B
+    assert call(od="bf16") == pf.PF_ERR_INVALID         # neither f32 nor the pool dtype
+    assert call(n=0) == pf.PF_OK                        # nothing to do
+    # needs a workspace: 2 splits
+    assert pf.pf_attention_workspace_bytes(h, 1, 1, 16 * 64) > 0
+    assert call(mb=64, mc=16 * 64) == pf.PF_ERR_WORKSPACE
+    assert pf.pf_scatter_kv(h, 3, A, A, A, A, 1, A, 1, 1, stream=0) == pf.PF_ERR_INVALID
+    assert pf.pf_scatter_kv(h, 0, A + 8, A, A, A, 1, A, 1, 1, stream=0) == pf.PF_ERR_INVALID
+    assert pf.pf_scatter_kv(h, 0, A, A, A, A, 0, A, 1, 1, stream=0) == pf.PF_OK   # no tokens
+    pf.pf_pool_destroy(h)
+    # unsupported kernel shapes are reported, not launched
+    st, h2 = pf.pf_pool_create(8, 8, 1, 1, 16, "f16")
+    assert pf.pf_pool_bind(h2, fake, pf.pf_pool_bytes(h2)) == pf.PF_OK
+    assert pf.pf_paged_decode_attention(h2, 0, A, 1, A, 2, A, 1, 16, 0.0, A, "f16", None, 0,
+                                        stream=0) == pf.PF_ERR_UNSUPPORTED
+    pf.pf_pool_destroy(h2)
+
+
+def test_pool_bytes_matches_layout():
+    st, h = pf.pf_pool_create(1024, 16, 12, 12, 64, "f16")
+    assert st == pf.PF_OK
+    assert pf.pf_page_bytes(h) == 589824               # PageForge: 0.59 MB per page
+    assert pf.pf_pool_bytes(h) == 1024 * 589824
+    pf.pf_pool_destroy(h)
+
+
+def test_threads_share_one_pool():
+    """8 threads allocate and free their own sequences on one handle; the mutex
+    keeps the pool consistent (PageFault, "Test": 8-thread stress)."""
+    P = 4096
+    h = _make(P)
+    errors = []
+
+    def worker(t):
+        rng = np.random.default_rng(100 + t)
+        try:
+            for c in range(300):
+                ids = [t * 10**6 + c * 8 + i for i in range(8)]
+                for s in ids:
+                    for k in range(1, 4):
+                        st, _ = pf.pf_alloc_for_seq(h, s, int(rng.integers(1, 100)) * k)
+                        if st not in (pf.PF_OK, pf.PF_ERR_INVALID):
+                            errors.append(st)
+                for s in ids:
+                    if pf.pf_free_seq(h, s) != pf.PF_OK:
+                        errors.append("free")
+        except Exception as e:  # pragma: no cover
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors
+    assert pf.pf_free_pages(h) == P and pf.pf_num_seqs(h) == 0
+    pf.pf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_batch_alloc_is_all_or_nothing_and_matches_oracle(seed):
+    """pf_alloc_for_seqs equals applying the single allocs in order when they all
+    succeed; otherwise nothing changes (oracle snapshot rolled back)."""
+    rng = np.random.default_rng(seed)
+    P = 200
+    order = rng.permutation(P)
+    h = _make(P, order)
+    model = am.AllocModel(P, 16, order)
+    for it in range(300):
+        n = int(rng.integers(1, 12))
+        ids = rng.integers(0, 20, size=n)
+        cur = np.array([model.lengths.get(int(s), 0) for s in ids])
+        new = cur + rng.integers(-2 if it % 7 == 0 else 0, 60, size=n)
+        new = np.maximum(new, -1 if it % 11 == 0 else 0)
+        st, nn = pf.pf_alloc_for_seqs(h, ids, new)
+        # reference: validate every entry against the lengths the batch would
+        # leave, then compare the total page need with the free pages
+        lens = dict(model.lengths)
+        mst, need = am.OK, 0
+        for s_, ln in zip(ids, new):
+            cur = lens.get(int(s_), 0)
+            if ln < 0 or ln < cur:
+                mst = am.INVALID
+                break
+            need += am.blocks_for(int(ln), 16) - am.blocks_for(cur, 16)
+            lens[int(s_)] = int(ln)
+        if mst == am.OK and need > model.free_pages():
+            mst = am.OOM
+        if mst != am.OK:
+            assert STATUS[st] == mst and not nn.any()
+        else:
+            mnn = [model.alloc(int(s_), int(ln))[1] for s_, ln in zip(ids, new)]
+            assert st == pf.PF_OK and list(nn) == mnn
+        assert pf.pf_free_pages(h) == model.free_pages()
+        if rng.random() < 0.2 and model.tables:
+            s = int(rng.choice(sorted(model.tables)))
+            assert pf.pf_free_seq(h, s) == pf.PF_OK
+            model.free(s)
+    _tables_equal(h, model)
+    pf.pf_pool_destroy(h)
