@@ -73,13 +73,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
     total_steps = warmup + steps
     max_ctx_final = int(base.max()) + total_steps
     kv.ensure_workspace(max_ctx_final)
-    # pinned staging ring for the per-step table/length export
-    ring = 4
-    stage_bt = [torch.empty((w.n, kv.max_blocks), dtype=torch.int32).pin_memory() for _ in range(ring)]
-    stage_len = [torch.empty(w.n, dtype=torch.int32).pin_memory() for _ in range(ring)]
-    stage_ev = [torch.cuda.Event() for _ in range(ring)]
     tok_seq = torch.arange(w.n, dtype=torch.int32, device=dev)
-    tok_pos = torch.empty(w.n, dtype=torch.int32, device=dev)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
     ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
     ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
@@ -92,25 +86,16 @@ def run_gpu(args, name, frames, steps, warmup, flush):
     ctx_per_step = []
 
     def step(t):
-        slot = t % ring
-        stage_ev[slot].synchronize()           # the copy that last used this slot is done
         new_lens = (base + t + 1).astype(np.int32)
         st, _ = pf.pf_alloc_for_seqs(kv.h, ids, new_lens)
         pf.check(st, "pf_alloc_for_seqs")
-        st, _, _ = pf.pf_block_tables(kv.h, ids, kv.max_blocks, stage_bt[slot].numpy(),
-                                      stage_len[slot].numpy())
-        pf.check(st, "pf_block_tables")
         if flush:
             flush_buf.zero_()
         ev_step[t][0].record(stream)
-        kv.bt.copy_(stage_bt[slot], non_blocking=True)
-        kv.ctx.copy_(stage_len[slot], non_blocking=True)
-        tok_pos.copy_(kv.ctx)
-        tok_pos.sub_(1)
-        stage_ev[slot].record(stream)
+        kv.export_tables()
         mc = int(new_lens.max())
         for layer in range(w.layers):
-            kv.scatter(layer, newk[layer], newv[layer], tok_seq, tok_pos)
+            kv.scatter(layer, newk[layer], newv[layer], tok_seq, kv.last_pos)
         for layer in range(w.layers):
             pf.check(pf.pf_pool_set_timing_events(kv.h, ev_a[t][layer].cuda_event,
                                                   ev_b[t][layer].cuda_event))
@@ -138,7 +123,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         pf.check(pf.pf_free_seq(kv.h, s))
     assert pf.pf_free_pages(kv.h) == w.num_pages
     split = pf.pf_attention_split_tokens(kv.h, w.n, w.hq, max_ctx_final)
-    mfma = pf.pf_pool_get_option(kv.h, pf.PF_OPT_GQA_MFMA)[1] and w.hq > w.hkv and w.dtype != "f32"
+    mfma = pf.pf_attention_kernel(kv.h, w.hq) == 1
     kv.close()
     ms_step_events = float(np.mean(step_ms))
     ms_step_wall = wall * 1e3 / steps

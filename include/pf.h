@@ -166,12 +166,13 @@ size_t pf_attention_workspace_bytes(const pf_pool* pool, int32_t n, int32_t num_
  * over the first ctx_dev[i] tokens of sequence i, read through row i of bt_dev,
  * with K_i, V_i of kv head h / (num_q_heads / H) (grouped-query heads are
  * consecutive).  Tokens at positions >= the length are never read.
- *   q        device [n][num_q_heads][D], pool dtype.
+ *   q        device [n][num_q_heads][D], pool dtype, 16-byte aligned.
  *   bt_dev   device [n][max_blocks] int32 tables (-1 padding is never read).
  *   ctx_dev  device [n] int32 lengths; each is clamped to [0, max_context_len].
  *   max_context_len  host bound on the lengths, <= max_blocks * B; sizes the grid.
  *   scale    <= 0 selects 1/sqrt(D).
- *   out      device [n][num_q_heads][D] in out_dtype (PF_F32 or the pool dtype).
+ *   out      device [n][num_q_heads][D] in out_dtype (PF_F32 or the pool dtype),
+ *            16-byte aligned.
  *   workspace  device, >= pf_attention_workspace_bytes(...), 256-byte aligned
  *            (nullable when that is 0); holds split-K partials.
  * Math is fp32 with an online softmax; long contexts are split into fixed
@@ -209,6 +210,11 @@ int32_t pf_attention_split_tokens(const pf_pool* pool, int32_t n, int32_t num_q_
  * stream (hipEvent_t values cast to void*, owned by the caller).  NULL, NULL
  * turns it off.  Errors: PF_ERR_INVALID (NULL handle or only one event). */
 int pf_pool_set_timing_events(pf_pool* pool, void* start_event, void* stop_event);
+
+/* Which attention kernel a call with num_q_heads query heads would use:
+ * 1 = matrix-core kernel for grouped heads, 0 = vector kernel, -1 = NULL handle
+ * or bad head count. */
+int32_t pf_attention_kernel(const pf_pool* pool, int32_t num_q_heads);
 
 /* Static description of a status code. */
 const char* pf_status_string(int status);

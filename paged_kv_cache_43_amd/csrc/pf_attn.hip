@@ -123,6 +123,9 @@ __global__ __launch_bounds__(kWave) void attn_valu_kernel(AttnArgs a) {
 
   Raw<S::NW> ka[S::ROWS], va[S::ROWS], kb[S::ROWS], vb[S::ROWS];
 
+  // Page i's address; an entry that is not a valid page reads page 0 instead
+  // (in bounds) and is then skipped, so every path issues the same loads and
+  // the wait counts stay exact.
   auto page_ptr = [&](int i, bool* ok) -> const uint8_t* {
     const int page = __builtin_amdgcn_readlane(my_page, i);
     *ok = (unsigned)page < (unsigned)a.num_pages;
@@ -131,10 +134,10 @@ __global__ __launch_bounds__(kWave) void attn_valu_kernel(AttnArgs a) {
   };
   auto load_tile = [&](const uint8_t* p, Raw<S::NW>* kt, Raw<S::NW>* vt) {
 #pragma unroll
-    for (int r = 0; r < S::ROWS; ++r) {
-      kt[r] = load_raw<S::NW>(p + (int64_t)r * S::TPI * D * S::ES);
+    for (int r = 0; r < S::ROWS; ++r) kt[r] = load_raw<S::NW>(p + (int64_t)r * S::TPI * D * S::ES);
+#pragma unroll
+    for (int r = 0; r < S::ROWS; ++r)
       vt[r] = load_raw<S::NW>(p + ((int64_t)kBlock * D + r * S::TPI * D) * S::ES);
-    }
   };
   auto process = [&](const Raw<S::NW>* kt, const Raw<S::NW>* vt, int nvalid) {
     // nvalid: tokens of this page below the length (1..B)
@@ -180,23 +183,24 @@ __global__ __launch_bounds__(kWave) void attn_valu_kernel(AttnArgs a) {
   };
   auto nvalid_of = [&](int i) { return min(kBlock, tok_end - (pg0 + i) * kBlock); };
 
-  bool ok_a = false, ok_b = false;
-  {
-    const uint8_t* p = page_ptr(0, &ok_a);
-    if (ok_a) load_tile(p, ka, va);
+  // Two register tiles: the next page's loads are in flight while the current
+  // page is used.  The steady-state loop issues its prefetch unconditionally;
+  // the last one or two pages are peeled off after it.
+  bool ok_a, ok_b;
+  load_tile(page_ptr(0, &ok_a), ka, va);
+  int i = 0;
+  for (; i + 2 < npg; i += 2) {
+    load_tile(page_ptr(i + 1, &ok_b), kb, vb);
+    if (ok_a) process(ka, va, kBlock);
+    load_tile(page_ptr(i + 2, &ok_a), ka, va);
+    if (ok_b) process(kb, vb, kBlock);
   }
-  for (int i = 0; i < npg; i += 2) {
-    if (i + 1 < npg) {
-      const uint8_t* p = page_ptr(i + 1, &ok_b);
-      if (ok_b) load_tile(p, kb, vb);
-    }
-    if (ok_a) process(ka, va, nvalid_of(i));
-    if (i + 1 >= npg) break;
-    if (i + 2 < npg) {
-      const uint8_t* p = page_ptr(i + 2, &ok_a);
-      if (ok_a) load_tile(p, ka, va);
-    }
+  if (i + 1 < npg) {
+    load_tile(page_ptr(i + 1, &ok_b), kb, vb);
+    if (ok_a) process(ka, va, kBlock);
     if (ok_b) process(kb, vb, nvalid_of(i + 1));
+  } else {
+    if (ok_a) process(ka, va, nvalid_of(i));
   }
 
   // combine the per-lane accumulators of the TPI token slots
@@ -312,6 +316,11 @@ static bool use_mfma(const pf_pool* pool, int32_t num_q_heads) {
   return group > 1 && group <= 16 && mfma_supports(g.head_dim);
 }
 
+extern "C" int32_t pf_attention_kernel(const pf_pool* pool, int32_t num_q_heads) {
+  if (!pool || num_q_heads <= 0 || num_q_heads % pool->g.num_kv_heads != 0) return -1;
+  return use_mfma(pool, num_q_heads) ? 1 : 0;
+}
+
 extern "C" int32_t pf_attention_split_tokens(const pf_pool* pool, int32_t n, int32_t num_q_heads,
                                              int32_t max_context_len) {
   (void)n;
@@ -352,7 +361,7 @@ extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, con
   if (n > 65535 || num_q_heads > 65535) return PF_ERR_INVALID;
   if (!q || !bt_dev || !ctx_dev || !out) return PF_ERR_INVALID;
   const size_t qa = (size_t)g.head_dim * pool->elem_bytes >= 16 ? 16 : 8;
-  if (reinterpret_cast<uintptr_t>(q) % qa != 0 || reinterpret_cast<uintptr_t>(out) % 4 != 0)
+  if (reinterpret_cast<uintptr_t>(q) % qa != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return PF_ERR_INVALID;
 
   const bool mfma = use_mfma(pool, num_q_heads);

@@ -67,6 +67,7 @@ _SIGS = {
     "pf_pool_get_option": (_i32, [_vp, _i32, _pi32]),
     "pf_attention_split_tokens": (_i32, [_vp, _i32, _i32, _i32]),
     "pf_pool_set_timing_events": (_i32, [_vp, _vp, _vp]),
+    "pf_attention_kernel": (_i32, [_vp, _i32]),
     "pf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -229,6 +230,10 @@ def pf_gather_kv(pool, layer, bt_dev, lens_dev, n, max_blocks, max_len, k_out, v
 
 def pf_attention_workspace_bytes(pool, n, num_q_heads, max_context_len):
     return lib.pf_attention_workspace_bytes(pool, n, num_q_heads, max_context_len)
+
+
+def pf_attention_kernel(pool, num_q_heads):
+    return lib.pf_attention_kernel(pool, num_q_heads)
 
 
 def pf_attention_split_tokens(pool, n, num_q_heads, max_context_len):

@@ -41,13 +41,18 @@ class PagedKV:
                                 .view(_BITS_NP[w.dtype])))
         pf.check(pf.pf_pool_bind(self.h, self.pool, nbytes), "pf_pool_bind")
         self.max_blocks = max_blocks or w.max_blocks(extra_tokens)
-        self.ids = list(range(w.n))
-        self.bt_host = torch.empty((w.n, self.max_blocks), dtype=torch.int32).pin_memory() \
-            if torch.cuda.is_available() else torch.empty((w.n, self.max_blocks), dtype=torch.int32)
-        self.len_host = torch.empty(w.n, dtype=torch.int32).pin_memory() \
-            if torch.cuda.is_available() else torch.empty(w.n, dtype=torch.int32)
-        self.bt = torch.empty((w.n, self.max_blocks), dtype=torch.int32, device=device)
-        self.ctx = torch.empty(w.n, dtype=torch.int32, device=device)
+        self.ids = np.arange(w.n, dtype=np.uint64)
+        # Per-step metadata, packed so one copy moves it: block tables
+        # [n][max_blocks], lengths [n], and each sequence's newest position [n].
+        nb = w.n * self.max_blocks
+        self.meta_elems = nb + 2 * w.n
+        self.meta = torch.empty(max(self.meta_elems, 1), dtype=torch.int32, device=device)
+        self.bt = self.meta[:nb].view(w.n, self.max_blocks)
+        self.ctx = self.meta[nb:nb + w.n]
+        self.last_pos = self.meta[nb + w.n:nb + 2 * w.n]
+        self.ring = [self._host_meta() for _ in range(4)]
+        self.ring_ev = [torch.cuda.Event() if torch.cuda.is_available() else None for _ in range(4)]
+        self.ring_i = 0
         self.ws = None
         self.ws_bytes = 0
 
@@ -71,14 +76,30 @@ class PagedKV:
             else:
                 pf.check(pf.pf_free_seq(self.h, op[1]), "pf_free_seq")
 
-    def export_tables(self, stream=None):
-        """Block tables and lengths of sequences 0..n-1 into pinned host memory,
-        then one asynchronous copy each to the device."""
-        st, _, _ = pf.pf_block_tables(self.h, self.ids, self.max_blocks, self.bt_host.numpy(),
-                                      self.len_host.numpy())
+    def _host_meta(self):
+        t = torch.empty(max(self.meta_elems, 1), dtype=torch.int32)
+        return t.pin_memory() if torch.cuda.is_available() else t
+
+    def export_tables(self):
+        """Block tables, lengths and newest positions of sequences 0..n-1 into a
+        pinned staging buffer (a ring of four, so the host can run ahead), then
+        one asynchronous copy to the device on the current stream."""
+        w = self.w
+        slot = self.ring_i
+        self.ring_i = (slot + 1) % len(self.ring)
+        if self.ring_ev[slot] is not None:
+            self.ring_ev[slot].synchronize()   # the copy that last read this slot is done
+        host = self.ring[slot].numpy()
+        nb = w.n * self.max_blocks
+        bt = host[:nb].reshape(w.n, self.max_blocks)
+        lens = host[nb:nb + w.n]
+        st, _, _ = pf.pf_block_tables(self.h, self.ids, self.max_blocks, bt, lens)
         pf.check(st, "pf_block_tables")
-        self.bt.copy_(self.bt_host, non_blocking=True)
-        self.ctx.copy_(self.len_host, non_blocking=True)
+        np.subtract(lens, 1, out=host[nb + w.n:nb + 2 * w.n])
+        self.meta.copy_(self.ring[slot], non_blocking=True)
+        if self.ring_ev[slot] is not None:
+            self.ring_ev[slot].record()
+        return lens
 
     # --------------------------------------------------------------- kernels
     def scatter(self, layer, k, v, tok_seq, tok_pos, stream=None):
