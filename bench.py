@@ -16,6 +16,7 @@ stream; ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the
 same workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import subprocess
@@ -36,6 +37,31 @@ WORKLOADS = {
     "13b": "13B-style: 40 heads, d_head 128, fp16, one layer's decode, 64 seqs, context U[256,2048], block 16, pool 1.1x blocks used, {frames} frames",
     "gqa": "GQA large batch: 14 q heads / 2 kv heads, d_head 64, bf16, 256 seqs, context U[1024,4096], block 16, pool 70k pages after 500x16 alloc/free churn, {frames} frames",
 }
+
+
+def kernel_source_hash():
+    """Hash of the HIP/C++ sources the library is built from."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "paged_kv_cache_43_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per partition launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-kernel calibrated), or None when the
+    kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    try:
+        kv = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_hash", "").strip() != kernel_source_hash() or config not in kv:
+        return None
+    return int(kv[config])
 
 
 def alg_bytes_attention(ctx, w, out_bytes):
@@ -123,6 +149,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         pf.check(pf.pf_free_seq(kv.h, s))
     assert pf.pf_free_pages(kv.h) == w.num_pages
     split = pf.pf_attention_split_tokens(kv.h, w.n, w.hq, max_ctx_final)
+    waves = pf.pf_attention_waves(kv.h, w.n, w.hq, max_ctx_final)
     mfma = pf.pf_attention_kernel(kv.h, w.hq) == 1
     kv.close()
     ms_step_events = float(np.mean(step_ms))
@@ -139,7 +166,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         ms_step_events=ms_step_events, value=avg_step_bytes / (ms_step * 1e-3) / 1e9,
         seqs_per_ms=w.n / ms_step, part_avg_us=part_avg_ms * 1e3,
         part_med_us=float(np.median(part_ms)) * 1e3, part_min_us=float(np.min(part_ms)) * 1e3,
-        attn_bytes=avg_attn_bytes, achieved=achieved, split=split, mfma=bool(mfma),
+        attn_bytes=avg_attn_bytes, achieved=achieved, split=split, waves=waves, mfma=bool(mfma),
         kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers))
 
 
@@ -185,7 +212,9 @@ def describe(r):
     return {"workload": WORKLOADS[r["name"]].format(frames=r["frames"]), "n_seqs": w.n,
             "layers": w.layers, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
             "block_size": 16, "pool_pages": w.num_pages, "frames": r["frames"],
-            "split_tokens": r["split"], "kernel": "mfma" if r["mfma"] else "valu"}
+            "schedule": "balanced" if r["waves"] else "fixed splits",
+            "waves": r["waves"] or None, "split_tokens": r["split"] or None,
+            "kernel": "mfma" if r["mfma"] else "valu"}
 
 
 def main():
@@ -199,6 +228,9 @@ def main():
     ap.add_argument("--flush", action="store_true", help="zero 1 GiB between steps (outside the step events)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first copy a 256 MiB buffer 3 times (a plain copy kernel of known size, "
+                         "the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1",
@@ -209,6 +241,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, args.flush)
     others = {}
     for extra in [x for x in args.also.split(",") if x and x != args.config]:
@@ -238,7 +277,8 @@ def main():
         "seqs_per_ms": round(head["seqs_per_ms"], 2),
         "ms_per_step_wall": round(head["ms_step_wall"], 4),
         "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.config),
                      "kernel": "attention partition", "avg_launch_us": round(head["part_avg_us"], 2),
                      "median_launch_us": round(head["part_med_us"], 2),
                      "alg_bytes_per_launch": int(head["attn_bytes"])},

@@ -132,6 +132,18 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
 
 /* ------------------------------------------------------------------ kernels */
 
+/* The per-step host -> device table export in one call: fill staging_host
+ * (caller-owned pinned memory, hipHostMalloc / pin_memory, 16-byte aligned)
+ * with int32 [n][max_blocks] block tables (rows of seq_ids, padded with -1),
+ * then [n] lengths, then [n] newest positions (length - 1), and enqueue on
+ * the stream one kernel that copies those n*max_blocks + 2n words to meta_dev
+ * (device, 16-byte aligned), reading the pinned memory directly (no DMA
+ * engine round trip).  The staging buffer must not be rewritten until the
+ * stream has passed this call.  Errors: as pf_block_tables, plus
+ * PF_ERR_INVALID for null or misaligned buffers and PF_ERR_HIP. */
+int pf_export_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                     int32_t* staging_host, int32_t* meta_dev, void* hip_stream);
+
 /* Write num_tokens tokens' K and V into their page slots for one layer.
  *   k, v     device [num_tokens][H][D] in the pool dtype.
  *   tok_seq  device [num_tokens] int32: row of bt_dev holding the token's table.
@@ -175,9 +187,11 @@ size_t pf_attention_workspace_bytes(const pf_pool* pool, int32_t n, int32_t num_
  *            16-byte aligned.
  *   workspace  device, >= pf_attention_workspace_bytes(...), 256-byte aligned
  *            (nullable when that is 0); holds split-K partials.
- * Math is fp32 with an online softmax; long contexts are split into fixed
- * token ranges whose partials are merged by log-sum-exp in a second kernel, in
- * a fixed order, so results depend only on logical positions (the same bits for
+ * Math is fp32 with an online softmax.  Work is split either into fixed token
+ * ranges per (sequence, head) or, by default, into equal slices of all
+ * sequences' pages (balanced schedule); partial results are merged by
+ * log-sum-exp in a second kernel, in a fixed order.  The split depends only on
+ * the lengths, so results depend only on logical positions (the same bits for
  * any physical page order).  A length of 0 gives a zero output.  A table entry
  * that is not a valid page contributes nothing (no access outside the pool).
  * Errors: PF_ERR_INVALID, PF_ERR_UNBOUND, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED,
@@ -191,18 +205,25 @@ int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
 /* ------------------------------------------------------------------ options */
 
 typedef enum {
-  PF_OPT_SPLIT_TOKENS = 0, /* tokens per context split (multiple of B); 0 = automatic */
-  PF_OPT_GQA_MFMA = 1      /* 1 (default): matrix-core kernel for grouped 16-bit heads; 0: vector kernel */
+  PF_OPT_SPLIT_TOKENS = 0, /* fixed-split schedule: tokens per split (multiple of B, <= 64 B); 0 = automatic */
+  PF_OPT_GQA_MFMA = 1,     /* 1 (default): matrix-core kernel for grouped 16-bit heads; 0: vector kernel */
+  PF_OPT_SCHEDULE = 2,     /* 0 (default): balanced if n <= 2048, else fixed splits; 1: fixed splits;
+                              2: balanced (n <= 2048) */
+  PF_OPT_WAVES_PER_CU = 3  /* balanced schedule: waves launched per compute unit; 0 = resident capacity */
 } pf_option;
 
 /* Set / read a tuning option of a handle.  Errors: PF_ERR_INVALID. */
 int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value);
 int pf_pool_get_option(const pf_pool* pool, int32_t option, int32_t* value);
 
-/* Tokens per split the attention kernels will use for these sizes (the
- * automatic choice or the option), for diagnostics and tests. */
+/* Tokens per split the fixed-split schedule will use for these sizes (the
+ * automatic choice or the option); 0 when the balanced schedule is chosen. */
 int32_t pf_attention_split_tokens(const pf_pool* pool, int32_t n, int32_t num_q_heads,
                                   int32_t max_context_len);
+
+/* Waves the balanced schedule will launch for these sizes; 0 when the
+ * fixed-split schedule is chosen. */
+int32_t pf_attention_waves(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_context_len);
 
 /* Instrumentation: when both are non-NULL, every later
  * pf_paged_decode_attention call on this handle records start_event right

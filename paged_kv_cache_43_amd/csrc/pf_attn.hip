@@ -1,5 +1,5 @@
-// Decode attention over paged K/V: split partition kernel, split-K merge
-// kernel and the pf_paged_decode_attention entry point.
+// Decode attention over paged K/V: the vector partition kernel, the split
+// merge kernel and the pf_paged_decode_attention entry point.
 //
 // What is computed (PagedAttention blog, "The Attention Kernel"; PageFault,
 // "Four stages", stage 3): for sequence s and query head h,
@@ -9,34 +9,32 @@
 // softmax) and merges partial results across thread blocks with log-sum-exp;
 // both are used here, in fp32.
 //
-// Work decomposition (gfx950, wave64):
-//  * One wave per work item (sequence, head, context split).  A split is a
-//    fixed range of split_tokens logical tokens (a multiple of the page size),
-//    so split boundaries and the merge order depend only on logical positions:
-//    ordered and shuffled page orders give the same bits.
-//  * The split's block-table entries are loaded once into lanes and broadcast
-//    per page with readlane: there is no dependent load chain per page.
+// Vector kernel (any head grouping, all dtypes), per wave:
 //  * Lanes lie across the head dimension: each lane holds VEC consecutive
 //    elements (a 16-byte load), D/VEC lanes cover one token, and one wave
 //    instruction loads 64/(D/VEC) consecutive tokens of a page.  The K and V
 //    tiles of a (page, layer, kv head) are adjacent in the pool, so a page is
 //    read as 2*B*D*es contiguous bytes.
-//  * The next page's K/V loads are issued before the current page is used.
+//  * Table entries are loaded once per batch of pages into lanes and broadcast
+//    per page with readlane: there is no dependent load chain per page; the
+//    next page's loads are issued before the current page is used.
 //  * QK partial dots are summed across the D/VEC lanes of a token with DPP
 //    moves; the page maximum is a wave-wide reduction; the running max is
-//    therefore wave-uniform, so each lane can accumulate p*v for its own
-//    tokens and the per-lane accumulators are combined once per split.
-//  * Only the sequence's last page can hold tokens past the length; it takes
-//    a masked path that replaces their scores by -inf and their values by 0
-//    (selects, never multiplications, so sentinel NaNs in the tail never reach
-//    the result).
+//    therefore wave-uniform, so each lane accumulates p*v for its own tokens
+//    and the per-lane accumulators are combined once per piece.
+//  * Only a sequence's last page can hold tokens past the length; those get
+//    score -inf and value 0 by select, never by multiplication, so sentinel
+//    NaNs in the tail never reach the result.
 //  * Scores are kept in log2 units: q is pre-multiplied by scale*log2(e) and
 //    exponentials are exp2.
+// Work is assigned by the balanced schedule (pf_sched.h) or by fixed context
+// splits; both end with the same merge.
 #include <cmath>
 
 #include "pf_attn.h"
 #include "pf_common.h"
 #include "pf_internal.h"
+#include "pf_sched.h"
 
 namespace pf {
 
@@ -70,85 +68,79 @@ __device__ inline void store_out(void* out, int64_t idx, float v) {
   }
 }
 
-template <class T, int D, bool OUT_F32>
-__global__ __launch_bounds__(kWave) void attn_valu_kernel(AttnArgs a) {
-  using S = ValuShape<T, D>;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int dc = lane % S::LPT;   // which VEC-chunk of the head dimension
-  const int tq = lane / S::LPT;   // which token of a wave instruction
-
-  int ctx = a.ctx[s];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
-  const int64_t out_row = ((int64_t)s * a.hq + h) * D;
-  if (ctx == 0) {
-    if (split == 0 && tq == 0) {
-#pragma unroll
-      for (int i = 0; i < S::VEC; ++i) store_out<T, OUT_F32>(a.out, out_row + dc * S::VEC + i, 0.f);
-    }
-    return;
+// Zero outputs of every sequence with length 0 (balanced schedule: the
+// workgroup-0 threads do it from the LDS lengths, one thread per sequence, so
+// the common case costs one LDS read per thread).
+template <class T, bool OUT_F32>
+__device__ inline void zero_empty_rows(const AttnArgs& a, const SchedLds& L, int D) {
+  if (blockIdx.x != 0) return;
+  const int64_t row_elems = (int64_t)a.hq * D;
+  for (int s = threadIdx.x; s < a.n; s += kSchedThreads) {  // one thread per sequence
+    if (L.ctx[s] != 0) continue;
+    for (int64_t e = 0; e < row_elems; ++e) store_out<T, OUT_F32>(a.out, s * row_elems + e, 0.f);
   }
-  if (split >= nsplit) return;
+}
 
-  // q, pre-scaled into log2 units
+// Per-wave state of the vector kernel: the current piece's online softmax.
+template <class T, int D, bool OUT_F32>
+struct ValuWave {
+  using S = ValuShape<T, D>;
+  struct Tile {
+    Raw<S::NW> k[S::ROWS], v[S::ROWS];
+  };
+  const AttnArgs& a;
+  const int lane, dc, tq;
+  const uint8_t* pool;
+  int64_t lane_off;  // elements
   float qf[S::VEC];
-  {
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (out_row + dc * S::VEC) * S::ES;
+  float m, l, acc[S::VEC];
+
+  __device__ ValuWave(const AttnArgs& args, int ln)
+      : a(args), lane(ln), dc(ln % S::LPT), tq(ln / S::LPT),
+        pool(static_cast<const uint8_t*>(args.pool)), lane_off((int64_t)(tq * D + dc * S::VEC)) {}
+
+  // Start a piece of (sequence s, query head h): q in log2 units, empty state.
+  __device__ inline void begin(int s, int h) {
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + ((((int64_t)s * a.hq + h) * D) + dc * S::VEC) * S::ES;
     Raw<S::NW> r = load_raw<S::NW>(qp);
     widen_words<T, S::NW>(r, qf);
 #pragma unroll
     for (int i = 0; i < S::VEC; ++i) qf[i] *= a.qscale;
+    // Pin q in registers here (see the matrix-core kernel's begin): it must
+    // neither be re-loaded per page nor stay pending where the item-switch
+    // branch rejoins the page loop.
+#pragma unroll
+    for (int i = 0; i < S::VEC; ++i) asm volatile("" : "+v"(qf[i]));
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int i = 0; i < S::VEC; ++i) acc[i] = 0.f;
   }
 
-  const int tok0 = split * a.split_tokens;
-  const int tok_end = min(ctx, tok0 + a.split_tokens);
-  const int pg0 = tok0 / kBlock;
-  const int npg = (tok_end - tok0 + kBlock - 1) / kBlock;
-  // this split's table entries, one per lane
-  const int my_page = lane < npg ? a.bt[(int64_t)s * a.max_blocks + pg0 + lane] : -1;
-
-  const int hk = h / a.group;
-  const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
-  const int64_t head_off = ((int64_t)a.layer * a.hkv + hk) * 2 * kBlock * D;  // elements
-  const int64_t lane_off = (int64_t)(tq * D + dc * S::VEC);                   // elements
-
-  float m = -INFINITY;
-  float l = 0.f;
-  float acc[S::VEC];
+  // Issue the K and V loads of page `page` for query head h; an entry that is
+  // not a valid page reads page 0 (in bounds) and reports false.
+  __device__ inline bool load(int page, int h, Tile& t) const {
+    const bool ok = (unsigned)page < (unsigned)a.num_pages;
+    const int64_t head_off = ((int64_t)a.layer * a.hkv + h / a.group) * 2 * kBlock * D;
+    const uint8_t* p = pool + ((int64_t)(ok ? page : 0) * a.page_elems + head_off + lane_off) * S::ES;
 #pragma unroll
-  for (int i = 0; i < S::VEC; ++i) acc[i] = 0.f;
-
-  Raw<S::NW> ka[S::ROWS], va[S::ROWS], kb[S::ROWS], vb[S::ROWS];
-
-  // Page i's address; an entry that is not a valid page reads page 0 instead
-  // (in bounds) and is then skipped, so every path issues the same loads and
-  // the wait counts stay exact.
-  auto page_ptr = [&](int i, bool* ok) -> const uint8_t* {
-    const int page = __builtin_amdgcn_readlane(my_page, i);
-    *ok = (unsigned)page < (unsigned)a.num_pages;
-    const int64_t el = (int64_t)(*ok ? page : 0) * a.page_elems + head_off + lane_off;
-    return pool + el * S::ES;
-  };
-  auto load_tile = [&](const uint8_t* p, Raw<S::NW>* kt, Raw<S::NW>* vt) {
-#pragma unroll
-    for (int r = 0; r < S::ROWS; ++r) kt[r] = load_raw<S::NW>(p + (int64_t)r * S::TPI * D * S::ES);
+    for (int r = 0; r < S::ROWS; ++r) t.k[r] = load_raw<S::NW>(p + (int64_t)r * S::TPI * D * S::ES);
 #pragma unroll
     for (int r = 0; r < S::ROWS; ++r)
-      vt[r] = load_raw<S::NW>(p + ((int64_t)kBlock * D + r * S::TPI * D) * S::ES);
-  };
-  auto process = [&](const Raw<S::NW>* kt, const Raw<S::NW>* vt, int nvalid) {
-    // nvalid: tokens of this page below the length (1..B)
+      t.v[r] = load_raw<S::NW>(p + ((int64_t)kBlock * D + r * S::TPI * D) * S::ES);
+    return ok;
+  }
+
+  // One page: nvalid of its 16 tokens are below the length.
+  __device__ inline void page(const Tile& t, int nvalid) {
     float sc[S::ROWS];
 #pragma unroll
     for (int r = 0; r < S::ROWS; ++r) {
       float kf[S::VEC];
-      widen_words<T, S::NW>(kt[r], kf);
+      widen_words<T, S::NW>(t.k[r], kf);
       float d = 0.f;
 #pragma unroll
-      for (int i = 0; i < S::VEC; ++i) d = fmaf(qf[i], kf[i], d);
+      for (int e = 0; e < S::VEC; ++e) d = fmaf(qf[e], kf[e], d);
       sc[r] = group_reduce<S::LPT, OpSum>(d);
     }
     const bool full = nvalid >= kBlock;
@@ -166,110 +158,245 @@ __global__ __launch_bounds__(kWave) void attn_valu_kernel(AttnArgs a) {
     m = mn;
     l *= alpha;
 #pragma unroll
-    for (int i = 0; i < S::VEC; ++i) acc[i] *= alpha;
+    for (int e = 0; e < S::VEC; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int r = 0; r < S::ROWS; ++r) {
       const float p = fast_exp2(sc[r] - mn);
       float vf[S::VEC];
-      widen_words<T, S::NW>(vt[r], vf);
+      widen_words<T, S::NW>(t.v[r], vf);
       if (!full && r * S::TPI + tq >= nvalid) {
 #pragma unroll
-        for (int i = 0; i < S::VEC; ++i) vf[i] = 0.f;
+        for (int e = 0; e < S::VEC; ++e) vf[e] = 0.f;
       }
       l += p;
 #pragma unroll
-      for (int i = 0; i < S::VEC; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
+      for (int e = 0; e < S::VEC; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
     }
-  };
-  auto nvalid_of = [&](int i) { return min(kBlock, tok_end - (pg0 + i) * kBlock); };
-
-  // Two register tiles: the next page's loads are in flight while the current
-  // page is used.  The steady-state loop issues its prefetch unconditionally;
-  // the last one or two pages are peeled off after it.
-  bool ok_a, ok_b;
-  load_tile(page_ptr(0, &ok_a), ka, va);
-  int i = 0;
-  for (; i + 2 < npg; i += 2) {
-    load_tile(page_ptr(i + 1, &ok_b), kb, vb);
-    if (ok_a) process(ka, va, kBlock);
-    load_tile(page_ptr(i + 2, &ok_a), ka, va);
-    if (ok_b) process(kb, vb, kBlock);
-  }
-  if (i + 1 < npg) {
-    load_tile(page_ptr(i + 1, &ok_b), kb, vb);
-    if (ok_a) process(ka, va, kBlock);
-    if (ok_b) process(kb, vb, nvalid_of(i + 1));
-  } else {
-    if (ok_a) process(ka, va, nvalid_of(i));
   }
 
-  // combine the per-lane accumulators of the TPI token slots
-  l = strided_reduce<S::LPT, OpSum>(l);
+  // Close the piece of row (s, h): the final output if the piece is the whole
+  // context, else partial record `rec`.
+  __device__ inline void finish(int s, int h, bool whole, int64_t rec) {
+    l = strided_reduce<S::LPT, OpSum>(l);
 #pragma unroll
-  for (int i = 0; i < S::VEC; ++i) acc[i] = strided_reduce<S::LPT, OpSum>(acc[i]);
-
-  if (tq != 0) return;
-  if (nsplit == 1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    for (int i = 0; i < S::VEC; ++i) acc[i] = strided_reduce<S::LPT, OpSum>(acc[i]);
+    if (tq != 0) return;
+    if (whole) {
+      const int64_t row = ((int64_t)s * a.hq + h) * D;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int i = 0; i < S::VEC; ++i) store_out<T, OUT_F32>(a.out, out_row + dc * S::VEC + i, acc[i] * inv);
-  } else {
-    const int64_t rec = ((int64_t)s * a.hq + h) * a.max_splits + split;
+      for (int i = 0; i < S::VEC; ++i) store_out<T, OUT_F32>(a.out, row + dc * S::VEC + i, acc[i] * inv);
+    } else {
 #pragma unroll
-    for (int i = 0; i < S::VEC; ++i) a.ws_acc[rec * D + dc * S::VEC + i] = acc[i];
-    if (dc == 0) a.ws_ml[rec] = make_float2(m, l);
+      for (int i = 0; i < S::VEC; ++i) a.ws_acc[rec * D + dc * S::VEC + i] = acc[i];
+      if (dc == 0) a.ws_ml[rec] = make_float2(m, l);
+    }
   }
+};
+
+// Grid schedule: one wave per (split, query head, sequence).
+template <class T, int D, int U, bool OUT_F32>
+__global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
+  using Wv = ValuWave<T, D, OUT_F32>;
+  using Tile = typename Wv::Tile;
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  const int lane = threadIdx.x;
+  // The split's table entries, bounded by the table width (independent of
+  // the length load).
+  const int split_pages = a.split_tokens / kBlock;
+  const int pg0 = split * split_pages;
+  const int my_page =
+      (lane < split_pages && pg0 + lane < a.max_blocks) ? a.bt[(int64_t)s * a.max_blocks + pg0 + lane] : -1;
+  const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
+  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
+  Wv w(a, lane);
+  if (ctx == 0) {
+    if (split == 0 && w.tq == 0) {
+#pragma unroll
+      for (int i = 0; i < Wv::S::VEC; ++i)
+        store_out<T, OUT_F32>(a.out, ((int64_t)s * a.hq + h) * D + w.dc * Wv::S::VEC + i, 0.f);
+    }
+    return;
+  }
+  if (split >= nsplit) return;
+  const int tok_end = min(ctx, (split + 1) * a.split_tokens);
+  const int npg = (tok_end - split * a.split_tokens + kBlock - 1) / kBlock;
+  w.begin(s, h);
+  page_pipeline<U, Tile>(
+      npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), h, t); },
+      [&](int i, const Tile& t, bool ok) {
+        if (ok) w.page(t, min(kBlock, tok_end - (pg0 + i) * kBlock));
+      });
+  w.finish(s, h, nsplit == 1, ((int64_t)s * a.hq + h) * a.max_splits + split);
 }
 
-// Merge the splits of every (sequence, query head) with more than one split:
-// M = max m_j, out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j, summed in
-// split order (PagedAttention blog, "The Attention Kernel": the final
-// reduction combines partial softmax results with log-sum-exp).
-template <class T, bool OUT_F32>
-__global__ __launch_bounds__(kWave) void attn_merge_kernel(AttnArgs a, int D) {
+// Balanced schedule (pf_sched.h): four waves per workgroup, items are query
+// heads.
+template <class T, int D, int U, bool OUT_F32>
+__global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) {
+  using Wv = ValuWave<T, D, OUT_F32>;
+  using Tile = typename Wv::Tile;
+  __shared__ SchedLds L;
+  sched_build(a, L);
+  zero_empty_rows<T, OUT_F32>(a, L, D);
+  const int lane = threadIdx.x % kWave;
+  const int gw = blockIdx.x * (kSchedThreads / kWave) + threadIdx.x / kWave;
+  const int X = a.hq;
+  const int64_t total = (int64_t)X * L.pfx[a.n];
+  if (total == 0) return;
+  const int64_t chunk = (total + a.waves - 1) / a.waves;
+  const int64_t wa = (int64_t)gw * chunk;
+  const int64_t wb = min(wa + chunk, total);
+  if (wa >= wb) return;
+
+  Wv w(a, lane);
+  int cur = -1, cs = 0, cx = 0, cP = 0, cp0 = 0, cplast = 0;
+  auto close_piece = [&]() {
+    const bool first = cp0 == 0, last = cplast == cP - 1;
+    const int item = cs * X + cx;
+    w.finish(cs, cx, first && last, (int64_t)item + gw);
+    if (last && lane == 0) {
+      const int64_t start = (int64_t)X * L.pfx[cs] + (int64_t)cx * cP;
+      const int wf = (int)(start / chunk), wl = (int)((start + cP - 1) / chunk);
+      a.ws_meta[item] = make_int2(item + wf, wl - wf + 1);
+    }
+  };
+  for (int64_t base = wa; base < wb; base += kWave) {
+    const int cnt = (int)min((int64_t)kWave, wb - base);
+    int ls = 0, lx = 0, lp = 0, lP = 1, lpage = -1, lnv = 0;
+    if (lane < cnt) {
+      const PagePos pp = sched_locate(L, a.n, X, base + lane);
+      ls = pp.s;
+      lx = pp.x;
+      lp = pp.p;
+      lP = pp.P;
+      lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
+      lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
+    }
+    page_pipeline<U, Tile>(
+        cnt,
+        [&](int i, Tile& t) {
+          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(lx, i), t);
+        },
+        [&](int i, const Tile& t, bool ok) {
+          const int s = __builtin_amdgcn_readlane(ls, i);
+          const int x = __builtin_amdgcn_readlane(lx, i);
+          const int p = __builtin_amdgcn_readlane(lp, i);
+          if (s * X + x != cur) {
+            if (cur >= 0) close_piece();
+            cur = s * X + x;
+            cs = s;
+            cx = x;
+            cP = __builtin_amdgcn_readlane(lP, i);
+            cp0 = p;
+            w.begin(s, x);
+          }
+          cplast = p;
+          if (ok) w.page(t, __builtin_amdgcn_readlane(lnv, i));
+        });
+  }
+  if (cur >= 0) close_piece();
+}
+
+// Merge the pieces of every output row that was split: M = max m_j,
+// out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j, summed in piece
+// order (PagedAttention blog, "The Attention Kernel": the final reduction
+// combines partial softmax results with log-sum-exp).  Grid schedule: the
+// row's splits are records row*max_splits + j; balanced schedule: the item's
+// (first record, pieces) pair, records (first + j) * rows_per_item + c.
+template <class T, bool OUT_F32, bool BAL>
+__global__ __launch_bounds__(kWave) void attn_merge_kernel(AttnArgs a, int D, int items_per_seq,
+                                                           int rows_per_item) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  int ctx = a.ctx[s];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
-  if (nsplit <= 1) return;
-  const int64_t rec0 = ((int64_t)s * a.hq + h) * a.max_splits;
-  float M = -INFINITY;
-  for (int j = 0; j < nsplit; ++j) M = fmaxf(M, a.ws_ml[rec0 + j].x);
-  float den = 0.f;
-  for (int j = 0; j < nsplit; ++j) {
-    const float2 ml = a.ws_ml[rec0 + j];
-    den += ml.x == -INFINITY ? 0.f : ml.y * fast_exp2(ml.x - M);
+  const int lane = threadIdx.x;
+  const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
+  if (ctx == 0) return;
+  int64_t first, stride = 1;
+  int cnt;
+  int c = 0;
+  if constexpr (BAL) {
+    const int item = s * items_per_seq + h / rows_per_item;
+    const int2 meta = a.ws_meta[item];
+    if (meta.y <= 1) return;
+    cnt = meta.y;
+    c = h % rows_per_item;
+    first = (int64_t)meta.x * rows_per_item + c;
+    stride = rows_per_item;
+  } else {
+    cnt = (ctx + a.split_tokens - 1) / a.split_tokens;
+    if (cnt <= 1) return;
+    first = ((int64_t)s * a.hq + h) * a.max_splits;
   }
+  float M = -INFINITY;
+  for (int j0 = 0; j0 < cnt; j0 += kWave)
+    if (j0 + lane < cnt) M = fmaxf(M, a.ws_ml[first + (j0 + lane) * stride].x);
+  M = group_reduce<kWave, OpMax>(M);
+  float den = 0.f;
+  float num[4] = {0.f, 0.f, 0.f, 0.f};  // dims lane, lane+64, lane+128, lane+192
+  for (int j0 = 0; j0 < cnt; j0 += kWave) {
+    float wj = 0.f;
+    if (j0 + lane < cnt) {
+      const float2 ml = a.ws_ml[first + (j0 + lane) * stride];
+      wj = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
+      den += ml.y * wj;
+    }
+    const int n = min(kWave, cnt - j0);
+    for (int j = 0; j < n; ++j) {
+      const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+      const float* src = a.ws_acc + (first + (j0 + j) * stride) * D;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (k * kWave + lane < D) num[k] += wgt * src[k * kWave + lane];
+    }
+  }
+  den = group_reduce<kWave, OpSum>(den);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const int64_t out_row = ((int64_t)s * a.hq + h) * D;
-  for (int d = threadIdx.x; d < D; d += kWave) {
-    float num = 0.f;
-    for (int j = 0; j < nsplit; ++j) {
-      const float mj = a.ws_ml[rec0 + j].x;
-      if (mj != -INFINITY) num += a.ws_acc[(rec0 + j) * D + d] * fast_exp2(mj - M);
-    }
-    store_out<T, OUT_F32>(a.out, out_row + d, num * inv);
-  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k * kWave + lane < D) store_out<T, OUT_F32>(a.out, out_row + k * kWave + lane, num[k] * inv);
 }
 
 // ---------------------------------------------------------------- launchers
+// Pages per prefetch unit: two units are in flight per wave; a unit holds
+// about 32 VGPRs of K/V per lane.
+template <class T, int D>
+struct ValuUnit {
+  static constexpr int bytes = 2 * kBlock * D * T::es / kWave;  // per lane per page
+  static constexpr int U = bytes >= 128 ? 1 : (bytes >= 64 ? 2 : 4);
+};
+
 template <class T, int D, bool OUT_F32>
-static void launch_valu(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_valu_kernel<T, D, OUT_F32>), dim3(a.max_splits, a.hq, a.n), dim3(kWave),
-                     0, st, a);
+static const void* valu_kernel_ptr(bool balanced) {
+  constexpr int U = ValuUnit<T, D>::U;
+  return balanced ? reinterpret_cast<const void*>(&attn_valu_balanced<T, D, U, OUT_F32>)
+                  : reinterpret_cast<const void*>(&attn_valu_grid<T, D, U, OUT_F32>);
+}
+
+template <class T, int D, bool OUT_F32>
+static void launch_valu(const AttnArgs& a, bool balanced, hipStream_t st) {
+  constexpr int U = ValuUnit<T, D>::U;
+  if (balanced)
+    hipLaunchKernelGGL((attn_valu_balanced<T, D, U, OUT_F32>), dim3(a.waves / (kSchedThreads / kWave)),
+                       dim3(kSchedThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_valu_grid<T, D, U, OUT_F32>), dim3(a.max_splits, a.hq, a.n), dim3(kWave), 0, st,
+                       a);
 }
 
 template <class T, bool OUT_F32>
-static int dispatch_valu_d(const AttnArgs& a, int D, hipStream_t st) {
+static int dispatch_valu_d(const AttnArgs& a, int D, bool balanced, hipStream_t st) {
   switch (D) {
-    case 16: launch_valu<T, 16, OUT_F32>(a, st); return PF_OK;
-    case 32: launch_valu<T, 32, OUT_F32>(a, st); return PF_OK;
-    case 64: launch_valu<T, 64, OUT_F32>(a, st); return PF_OK;
-    case 128: launch_valu<T, 128, OUT_F32>(a, st); return PF_OK;
+    case 16: launch_valu<T, 16, OUT_F32>(a, balanced, st); return PF_OK;
+    case 32: launch_valu<T, 32, OUT_F32>(a, balanced, st); return PF_OK;
+    case 64: launch_valu<T, 64, OUT_F32>(a, balanced, st); return PF_OK;
+    case 128: launch_valu<T, 128, OUT_F32>(a, balanced, st); return PF_OK;
     case 256:
       if constexpr (T::es == 2) {
-        launch_valu<T, 256, OUT_F32>(a, st);
+        launch_valu<T, 256, OUT_F32>(a, balanced, st);
         return PF_OK;
       }
       return PF_ERR_UNSUPPORTED;
@@ -278,16 +405,35 @@ static int dispatch_valu_d(const AttnArgs& a, int D, hipStream_t st) {
 }
 
 template <class T>
-static int dispatch_valu(const AttnArgs& a, int D, hipStream_t st) {
-  return a.out_f32 ? dispatch_valu_d<T, true>(a, D, st) : dispatch_valu_d<T, false>(a, D, st);
+static int dispatch_valu(const AttnArgs& a, int D, bool balanced, hipStream_t st) {
+  return a.out_f32 ? dispatch_valu_d<T, true>(a, D, balanced, st) : dispatch_valu_d<T, false>(a, D, balanced, st);
 }
 
 template <class T>
-static void launch_merge(const AttnArgs& a, int D, hipStream_t st) {
-  if (a.out_f32)
-    hipLaunchKernelGGL((attn_merge_kernel<T, true>), dim3(a.hq, a.n), dim3(kWave), 0, st, a, D);
-  else
-    hipLaunchKernelGGL((attn_merge_kernel<T, false>), dim3(a.hq, a.n), dim3(kWave), 0, st, a, D);
+static const void* valu_ptr_dtype(int D) {
+  switch (D) {
+    case 16: return valu_kernel_ptr<T, 16, false>(true);
+    case 32: return valu_kernel_ptr<T, 32, false>(true);
+    case 64: return valu_kernel_ptr<T, 64, false>(true);
+    case 128: return valu_kernel_ptr<T, 128, false>(true);
+    case 256:
+      if constexpr (T::es == 2) return valu_kernel_ptr<T, 256, false>(true);
+      return nullptr;
+    default: return nullptr;
+  }
+}
+
+template <class T>
+static void launch_merge(const AttnArgs& a, int D, bool balanced, int items_per_seq, int rows_per_item,
+                         hipStream_t st) {
+  const dim3 grid(a.hq, a.n);
+  if (balanced) {
+    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
+    else hipLaunchKernelGGL((attn_merge_kernel<T, false, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
+  } else {
+    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
+    else hipLaunchKernelGGL((attn_merge_kernel<T, false, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
+  }
 }
 
 static bool valu_supports(int dtype, int D) {
@@ -298,23 +444,123 @@ static bool valu_supports(int dtype, int D) {
   }
 }
 
+// Compute units of the current device (256 on MI355X if the query fails).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Resident waves per CU of a balanced kernel (16 if the query fails).
+static int occupancy_waves(const void* kernel, size_t lds) {
+  int blocks = 0;
+  if (!kernel || hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kSchedThreads, lds) != hipSuccess ||
+      blocks <= 0) {
+    (void)hipGetLastError();
+    return 16;
+  }
+  return blocks * (kSchedThreads / kWave);
+}
+
 }  // namespace pf
 
 using namespace pf;
 
-static int32_t split_tokens_for(const pf_pool* pool, bool mfma, int32_t max_ctx) {
-  int32_t st = pool->split_tokens;
-  if (st <= 0) st = mfma ? 512 : 256;
-  (void)max_ctx;
-  return st;
-}
+namespace {
 
-static bool use_mfma(const pf_pool* pool, int32_t num_q_heads) {
+struct Plan {
+  bool mfma;
+  bool balanced;
+  int32_t split;     // grid schedule: tokens per split
+  int64_t splits;    // grid schedule: splits of the longest context
+  int32_t waves;     // balanced schedule: waves in the grid
+  int64_t records;   // partial records
+  int64_t items;     // balanced schedule: items (for the meta array)
+  int32_t items_per_seq, rows_per_item;
+};
+
+bool use_mfma(const pf_pool* pool, int32_t num_q_heads) {
   const pf_geometry& g = pool->g;
   if (!pool->gqa_mfma || g.dtype == PF_F32) return false;
   const int group = num_q_heads / g.num_kv_heads;
   return group > 1 && group <= 16 && mfma_supports(g.head_dim);
 }
+
+// Grid schedule split: the largest split (64 pages) unless that leaves fewer
+// work items than about two per SIMD, then halve down to 4 pages.  Measured on
+// the 13B-style and GQA workloads: fewer, longer splits win, since each work
+// item pays a prologue and a partial write.
+int32_t grid_split(const pf_pool* pool, bool mfma, int32_t n, int32_t num_q_heads, int32_t max_ctx) {
+  if (pool->split_tokens > 0) return pool->split_tokens;
+  const int64_t heads = mfma ? pool->g.num_kv_heads : num_q_heads;
+  const int64_t want = 2 * 4 * 256;
+  int32_t st = 64 * kBlock;
+  while (st > 4 * kBlock && (int64_t)n * heads * ((max_ctx + st - 1) / st) < want) st /= 2;
+  return st;
+}
+
+Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_ctx) {
+  Plan p{};
+  const pf_geometry& g = pool->g;
+  p.mfma = use_mfma(pool, num_q_heads);
+  p.items_per_seq = p.mfma ? g.num_kv_heads : num_q_heads;
+  p.rows_per_item = p.mfma ? num_q_heads / g.num_kv_heads : 1;
+  const int sched = pool->schedule;
+  p.balanced = sched == 2 || (sched == 0 && n <= kMaxSeqsBalanced);
+  if (n > kMaxSeqsBalanced) p.balanced = false;
+  if (p.balanced) {
+    // Waves: 8 per CU (two per SIMD), or fewer if the kernel's occupancy is
+    // lower, and no more than one wave per 4 pages of the longest possible
+    // stream; whole workgroups.  Measured on the 13B-style and GQA workloads:
+    // 8 per CU is as fast as the full resident capacity for the first and
+    // clearly faster for the second (fewer pieces, fewer partial records).
+    int per_cu = pool->waves_per_cu;
+    if (per_cu <= 0) {
+      int occ;
+      if (p.mfma) {
+        occ = mfma_balanced_waves_per_cu(g.dtype, g.head_dim);
+      } else {
+        const void* k = g.dtype == PF_F32 ? valu_ptr_dtype<ElF32>(g.head_dim)
+                        : (g.dtype == PF_F16 ? valu_ptr_dtype<ElF16>(g.head_dim) : valu_ptr_dtype<ElBF16>(g.head_dim));
+        occ = occupancy_waves(k, 0);
+      }
+      per_cu = occ > 0 && occ < 8 ? occ : 8;
+    }
+    const int64_t wpg = kSchedThreads / kWave;
+    const int64_t upper = (int64_t)n * p.items_per_seq * ((max_ctx + kBlock - 1) / kBlock);
+    int64_t waves = (int64_t)device_cus() * per_cu;
+    const int64_t cap = (upper + 3) / 4;
+    if (waves > cap) waves = cap;
+    waves = ((waves + wpg - 1) / wpg) * wpg;
+    if (waves < wpg) waves = wpg;
+    p.waves = (int32_t)waves;
+    p.items = (int64_t)n * p.items_per_seq;
+    p.records = (p.items + waves) * p.rows_per_item;
+  } else {
+    p.split = grid_split(pool, p.mfma, n, num_q_heads, max_ctx);
+    p.splits = max_ctx <= 0 ? 1 : (max_ctx + p.split - 1) / p.split;
+    p.records = p.splits > 1 ? (int64_t)n * num_q_heads * p.splits : 0;
+  }
+  return p;
+}
+
+size_t plan_workspace(const Plan& p, int head_dim) {
+  if (p.records == 0) return 0;
+  size_t bytes = (size_t)p.records * head_dim * 4 + (size_t)p.records * 8;
+  if (p.balanced) bytes += (size_t)p.items * 8;
+  return bytes;
+}
+
+}  // namespace
 
 extern "C" int32_t pf_attention_kernel(const pf_pool* pool, int32_t num_q_heads) {
   if (!pool || num_q_heads <= 0 || num_q_heads % pool->g.num_kv_heads != 0) return -1;
@@ -323,23 +569,23 @@ extern "C" int32_t pf_attention_kernel(const pf_pool* pool, int32_t num_q_heads)
 
 extern "C" int32_t pf_attention_split_tokens(const pf_pool* pool, int32_t n, int32_t num_q_heads,
                                              int32_t max_context_len) {
-  (void)n;
-  if (!pool || num_q_heads <= 0) return 0;
-  return split_tokens_for(pool, use_mfma(pool, num_q_heads), max_context_len);
+  if (!pool || num_q_heads <= 0 || num_q_heads % pool->g.num_kv_heads != 0) return 0;
+  const Plan p = make_plan(pool, n, num_q_heads, max_context_len);
+  return p.balanced ? 0 : p.split;
 }
 
-static int64_t max_splits_for(int32_t max_ctx, int32_t split) {
-  return max_ctx <= 0 ? 1 : (max_ctx + split - 1) / split;
+extern "C" int32_t pf_attention_waves(const pf_pool* pool, int32_t n, int32_t num_q_heads,
+                                      int32_t max_context_len) {
+  if (!pool || num_q_heads <= 0 || num_q_heads % pool->g.num_kv_heads != 0) return 0;
+  const Plan p = make_plan(pool, n, num_q_heads, max_context_len);
+  return p.balanced ? p.waves : 0;
 }
 
 extern "C" size_t pf_attention_workspace_bytes(const pf_pool* pool, int32_t n, int32_t num_q_heads,
                                                int32_t max_context_len) {
-  if (!pool || n <= 0 || num_q_heads <= 0 || max_context_len <= 0) return 0;
-  const int32_t split = split_tokens_for(pool, use_mfma(pool, num_q_heads), max_context_len);
-  const int64_t S = max_splits_for(max_context_len, split);
-  if (S <= 1) return 0;
-  const int64_t recs = (int64_t)n * num_q_heads * S;
-  return (size_t)(recs * pool->g.head_dim * 4 + recs * 8);
+  if (!pool || n <= 0 || num_q_heads <= 0 || max_context_len <= 0 || num_q_heads % pool->g.num_kv_heads != 0)
+    return 0;
+  return plan_workspace(make_plan(pool, n, num_q_heads, max_context_len), pool->g.head_dim);
 }
 
 extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
@@ -364,7 +610,8 @@ extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, con
   if (reinterpret_cast<uintptr_t>(q) % qa != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return PF_ERR_INVALID;
 
-  const bool mfma = use_mfma(pool, num_q_heads);
+  const Plan p = make_plan(pool, n, num_q_heads, max_context_len);
+  if (!p.balanced && p.splits > 65535) return PF_ERR_INVALID;
   AttnArgs a{};
   a.pool = pool->dev;
   a.q = q;
@@ -380,43 +627,44 @@ extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, con
   a.max_blocks = max_blocks;
   a.max_ctx = max_context_len;
   a.n = n;
-  a.split_tokens = split_tokens_for(pool, mfma, max_context_len);
-  const int64_t S = max_splits_for(max_context_len, a.split_tokens);
-  if (S > 65535) return PF_ERR_INVALID;
-  a.max_splits = (int32_t)S;
+  a.split_tokens = p.balanced ? kBlock : p.split;
+  a.max_splits = p.balanced ? 1 : (int32_t)p.splits;
+  a.waves = p.waves;
   const float sc = scale > 0.f ? scale : 1.f / std::sqrt((float)g.head_dim);
   a.qscale = sc * kLog2e;
   a.out_f32 = out_dtype == PF_F32 && g.dtype != PF_F32 ? 1 : 0;
 
-  const size_t need = pf_attention_workspace_bytes(pool, n, num_q_heads, max_context_len);
+  const size_t need = plan_workspace(p, g.head_dim);
   if (need > 0) {
     if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
       return PF_ERR_WORKSPACE;
-    const int64_t recs = (int64_t)n * num_q_heads * S;
-    a.ws_acc = static_cast<float*>(workspace);
-    a.ws_ml = reinterpret_cast<float2*>(static_cast<uint8_t*>(workspace) + recs * g.head_dim * 4);
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(w);
+    a.ws_ml = reinterpret_cast<float2*>(w + p.records * g.head_dim * 4);
+    a.ws_meta = reinterpret_cast<int2*>(w + p.records * g.head_dim * 4 + p.records * 8);
   }
+  if (p.balanced && need == 0) return PF_ERR_WORKSPACE;
 
   hipStream_t st = (hipStream_t)hip_stream;
   if (pool->ev_start) hipEventRecord((hipEvent_t)pool->ev_start, st);
   int rc;
-  if (mfma) {
-    rc = g.dtype == PF_F16 ? launch_mfma_f16(a, g.head_dim, st) : launch_mfma_bf16(a, g.head_dim, st);
+  if (p.mfma) {
+    rc = launch_mfma(a, g.dtype, g.head_dim, p.balanced, st);
   } else {
     switch (g.dtype) {
-      case PF_F32: rc = dispatch_valu<ElF32>(a, g.head_dim, st); break;
-      case PF_F16: rc = dispatch_valu<ElF16>(a, g.head_dim, st); break;
-      default: rc = dispatch_valu<ElBF16>(a, g.head_dim, st); break;
+      case PF_F32: rc = dispatch_valu<ElF32>(a, g.head_dim, p.balanced, st); break;
+      case PF_F16: rc = dispatch_valu<ElF16>(a, g.head_dim, p.balanced, st); break;
+      default: rc = dispatch_valu<ElBF16>(a, g.head_dim, p.balanced, st); break;
     }
   }
   if (rc != PF_OK) return rc;
   if (hipGetLastError() != hipSuccess) return PF_ERR_HIP;
   if (pool->ev_stop) hipEventRecord((hipEvent_t)pool->ev_stop, st);
-  if (S > 1) {
+  if (p.records > 0) {
     switch (g.dtype) {
-      case PF_F32: launch_merge<ElF32>(a, g.head_dim, st); break;
-      case PF_F16: launch_merge<ElF16>(a, g.head_dim, st); break;
-      default: launch_merge<ElBF16>(a, g.head_dim, st); break;
+      case PF_F32: launch_merge<ElF32>(a, g.head_dim, p.balanced, p.items_per_seq, p.rows_per_item, st); break;
+      case PF_F16: launch_merge<ElF16>(a, g.head_dim, p.balanced, p.items_per_seq, p.rows_per_item, st); break;
+      default: launch_merge<ElBF16>(a, g.head_dim, p.balanced, p.items_per_seq, p.rows_per_item, st); break;
     }
     if (hipGetLastError() != hipSuccess) return PF_ERR_HIP;
   }

@@ -28,6 +28,7 @@
 #include "pf_attn.h"
 #include "pf_common.h"
 #include "pf_internal.h"
+#include "pf_sched.h"
 
 namespace pf {
 
@@ -93,83 +94,75 @@ __device__ inline void store_vec4(void* out, int64_t idx, const float* v) {
   }
 }
 
+// Per-wave state of the matrix-core kernel: the current piece's online
+// softmax for the 16 score columns (query heads of one kv head, padded).
 template <class T, int D, bool OUT_F32>
-__global__ __launch_bounds__(kWave) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int ES = 2;
-  constexpr int KC = D / 32;              // 32-dim chunks of the score product
-  constexpr int DB = D / 16;              // 16-dim blocks of the value product
-  constexpr int VCH = D * ES / 16;        // 16-byte chunks per token row
-  constexpr int VL = kBlock * VCH / kWave;  // 16-byte V loads per lane per page
-  constexpr int PITCH = D * ES + 8;       // LDS row pitch in bytes (bank spread)
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kBlock * PITCH];
-
-  const int split = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int s = blockIdx.z;
-  const int lane = threadIdx.x;
-  const int col = lane % 16;   // token (K operand) / head (score columns)
-  const int grp = lane / 16;   // k-group
-  const int g = a.group;
-  const int head = hk * g + col;  // query head of this lane's score column
-  const bool head_ok = col < g;
-
-  int ctx = a.ctx[s];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
-  if (ctx == 0) {
-    if (split == 0 && head_ok) {
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-        store_vec4<T, OUT_F32>(a.out, ((int64_t)s * a.hq + head) * D + 16 * b + 4 * grp, z);
-    }
-    return;
-  }
-  if (split >= nsplit) return;
-
-  // Q^T operand: head col, dims 32c + 8*grp .. +8 (zero rows past the group)
+struct MfmaWave {
+  static constexpr int ES = 2;
+  static constexpr int KC = D / 32;                // 32-dim chunks of the score product
+  static constexpr int DB = D / 16;                // 16-dim blocks of the value product
+  static constexpr int VCH = D * ES / 16;          // 16-byte chunks per token row
+  static constexpr int VL = kBlock * VCH / kWave;  // 16-byte V loads per lane per page
+  static constexpr int PITCH = D * ES + 8;         // LDS row pitch in bytes (bank spread)
+  static constexpr int TILE_BYTES = kBlock * PITCH;
+  struct Tile {
+    uint4 k[KC];
+    uint4 v[VL];
+  };
+  const AttnArgs& a;
+  uint8_t* vt;  // this wave's V staging tile in LDS
+  const int lane, col, grp;
+  const bool head_ok;
+  const uint8_t* pool;
   uint4 qop[KC];
-  {
+  float m, l;  // running max (log2 units) of head col; this lane's share of the sum
+  f4 acc[DB];
+
+  __device__ MfmaWave(const AttnArgs& args, uint8_t* stage, int ln)
+      : a(args), vt(stage), lane(ln), col(ln % 16), grp(ln / 16), head_ok(ln % 16 < args.group),
+        pool(static_cast<const uint8_t*>(args.pool)) {}
+
+  // Start a piece of (sequence s, kv head hk): the Q^T operand (head col, dims
+  // 32c + 8*grp .. +8; zero rows past the group) and an empty state.
+  __device__ inline void begin(int s, int hk) {
+    const int head = hk * a.group + col;
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (((int64_t)s * a.hq + (head_ok ? head : 0)) * D) * ES;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       uint4 v = *reinterpret_cast<const uint4*>(qp + (32 * c + 8 * grp) * ES);
       qop[c] = head_ok ? v : make_uint4(0, 0, 0, 0);
     }
-  }
-
-  const int tok0 = split * a.split_tokens;
-  const int tok_end = min(ctx, tok0 + a.split_tokens);
-  const int pg0 = tok0 / kBlock;
-  const int npg = (tok_end - tok0 + kBlock - 1) / kBlock;
-  const int my_page = lane < npg ? a.bt[(int64_t)s * a.max_blocks + pg0 + lane] : -1;
-
-  const uint8_t* pool = static_cast<const uint8_t*>(a.pool);
-  const int64_t head_off = ((int64_t)a.layer * a.hkv + hk) * 2 * kBlock * D;  // elements
-  const float c2 = a.qscale;  // scale * log2(e)
-
-  float m = -INFINITY;  // running max (log2 units) of head col
-  float l = 0.f;        // this lane's share of the running sum
-  f4 acc[DB];
-#pragma unroll
-  for (int b = 0; b < DB; ++b) acc[b] = f4{0.f, 0.f, 0.f, 0.f};
-
-  uint4 ka[KC], va[VL], kb[KC], vb[VL];
-
-  auto page_base = [&](int i, bool* ok) -> const uint8_t* {
-    const int page = __builtin_amdgcn_readlane(my_page, i);
-    *ok = (unsigned)page < (unsigned)a.num_pages;
-    return pool + ((int64_t)(*ok ? page : 0) * a.page_elems + head_off) * ES;
-  };
-  auto load_tile = [&](const uint8_t* p, uint4* kt, uint4* vr) {
+    // Pin q in registers, complete, here: begin() runs on a rarely taken
+    // branch inside the page loop.  Left alone, the compiler re-loads q at
+    // every page (or leaves the load pending where the branch rejoins), and
+    // each page then waits for all outstanding loads, prefetch included.
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      kt[c] = *reinterpret_cast<const uint4*>(p + (col * D + 32 * c + 8 * grp) * ES);
+      asm volatile("" : "+v"(qop[c].x), "+v"(qop[c].y), "+v"(qop[c].z), "+v"(qop[c].w));
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Issue page `page`'s loads for kv head hk: K as score-product operands, V
+  // as 16-byte coalesced chunks.  An entry that is not a valid page reads
+  // page 0 instead (in bounds) and reports false.
+  __device__ inline bool load(int page, int hk, Tile& t) const {
+    const bool ok = (unsigned)page < (unsigned)a.num_pages;
+    const int64_t head_off = ((int64_t)a.layer * a.hkv + hk) * 2 * kBlock * D;
+    const uint8_t* p = pool + ((int64_t)(ok ? page : 0) * a.page_elems + head_off) * ES;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      t.k[c] = *reinterpret_cast<const uint4*>(p + (col * D + 32 * c + 8 * grp) * ES);
 #pragma unroll
     for (int r = 0; r < VL; ++r)
-      vr[r] = *reinterpret_cast<const uint4*>(p + kBlock * D * ES + (r * kWave + lane) * 16);
-  };
-  auto process = [&](const uint4* kt, const uint4* vr, int nvalid) {
+      t.v[r] = *reinterpret_cast<const uint4*>(p + kBlock * D * ES + (r * kWave + lane) * 16);
+    return ok;
+  }
+
+  // One page: nvalid of its 16 tokens are below the length.
+  __device__ inline void page(const Tile& t, int nvalid) {
     const bool full = nvalid >= kBlock;
     // stage V (row-major, padded rows; tokens past the length as zeros)
 #pragma unroll
@@ -177,7 +170,7 @@ __global__ __launch_bounds__(kWave) void attn_mfma_kernel(AttnArgs a) {
       const int f = r * kWave + lane;
       const int tok = f / VCH;
       const int ch = f % VCH;
-      uint4 v = vr[r];
+      uint4 v = t.v[r];
       if (!full && tok >= nvalid) v = make_uint4(0, 0, 0, 0);
       uint8_t* dst = vt + tok * PITCH + ch * 16;
       *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
@@ -187,11 +180,11 @@ __global__ __launch_bounds__(kWave) void attn_mfma_kernel(AttnArgs a) {
     // scores S^T: token 4*grp + r, head col
     f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < KC; ++c) sc = Mfma<T>::qk(kt[c], qop[c], sc);
+    for (int c = 0; c < KC; ++c) sc = Mfma<T>::qk(t.k[c], qop[c], sc);
     float z[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      z[r] = sc[r] * c2;
+      z[r] = sc[r] * a.qscale;
       if (!full && 4 * grp + r >= nvalid) z[r] = -INFINITY;
     }
     float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -221,67 +214,199 @@ __global__ __launch_bounds__(kWave) void attn_mfma_kernel(AttnArgs a) {
       acc[b] = Mfma<T>::pv(vop, plo, acc[b]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  };
-  auto nvalid_of = [&](int i) { return min(kBlock, tok_end - (pg0 + i) * kBlock); };
-
-  bool ok_a, ok_b;
-  load_tile(page_base(0, &ok_a), ka, va);
-  int i = 0;
-  for (; i + 2 < npg; i += 2) {
-    load_tile(page_base(i + 1, &ok_b), kb, vb);
-    if (ok_a) process(ka, va, kBlock);
-    load_tile(page_base(i + 2, &ok_a), ka, va);
-    if (ok_b) process(kb, vb, kBlock);
-  }
-  if (i + 1 < npg) {
-    load_tile(page_base(i + 1, &ok_b), kb, vb);
-    if (ok_a) process(ka, va, kBlock);
-    if (ok_b) process(kb, vb, nvalid_of(i + 1));
-  } else {
-    if (ok_a) process(ka, va, nvalid_of(i));
   }
 
-  // the four k-groups hold disjoint tokens of the same heads: add their sums
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-  if (!head_ok) return;
-  const int64_t row = (int64_t)s * a.hq + head;
-  if (nsplit == 1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+  // Close the piece of (sequence s, kv head hk): the group's final outputs if
+  // the piece is the whole context, else the partial record rec_base +
+  // col * rec_mul of each query head.
+  __device__ inline void finish(int s, int hk, bool whole, int64_t rec_base, int64_t rec_mul) {
+    // the four k-groups hold disjoint tokens of the same heads: add their sums
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (!head_ok) return;
+    const int64_t row = (int64_t)s * a.hq + hk * a.group + col;
+    if (whole) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      const float o[4] = {acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv};
-      store_vec4<T, OUT_F32>(a.out, row * D + 16 * b + 4 * grp, o);
+      for (int b = 0; b < DB; ++b) {
+        const float o[4] = {acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv, acc[b][3] * inv};
+        store_vec4<T, OUT_F32>(a.out, row * D + 16 * b + 4 * grp, o);
+      }
+    } else {
+      const int64_t rec = rec_base + col * rec_mul;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+        *reinterpret_cast<float4*>(a.ws_acc + rec * D + 16 * b + 4 * grp) =
+            make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+      if (grp == 0) a.ws_ml[rec] = make_float2(m, l);
     }
-  } else {
-    const int64_t rec = row * a.max_splits + split;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-      *reinterpret_cast<float4*>(a.ws_acc + rec * D + 16 * b + 4 * grp) =
-          make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
-    if (grp == 0) a.ws_ml[rec] = make_float2(m, l);
   }
+};
+
+// Grid schedule: one wave per (split, kv head, sequence).
+template <class T, int D, int U, bool OUT_F32>
+__global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
+  using Wv = MfmaWave<T, D, OUT_F32>;
+  using Tile = typename Wv::Tile;
+  __shared__ __attribute__((aligned(16))) uint8_t vt[Wv::TILE_BYTES];
+  const int split = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int s = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int split_pages = a.split_tokens / kBlock;
+  const int pg0 = split * split_pages;
+  const int my_page =
+      (lane < split_pages && pg0 + lane < a.max_blocks) ? a.bt[(int64_t)s * a.max_blocks + pg0 + lane] : -1;
+  const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
+  const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
+  Wv w(a, vt, lane);
+  if (ctx == 0) {
+    if (split == 0 && w.head_ok) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < Wv::DB; ++b)
+        store_vec4<T, OUT_F32>(a.out, ((int64_t)s * a.hq + hk * a.group + w.col) * D + 16 * b + 4 * w.grp, z);
+    }
+    return;
+  }
+  if (split >= nsplit) return;
+  const int tok_end = min(ctx, (split + 1) * a.split_tokens);
+  const int npg = (tok_end - split * a.split_tokens + kBlock - 1) / kBlock;
+  w.begin(s, hk);
+  page_pipeline<U, Tile>(
+      npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), hk, t); },
+      [&](int i, const Tile& t, bool ok) {
+        if (ok) w.page(t, min(kBlock, tok_end - (pg0 + i) * kBlock));
+      });
+  w.finish(s, hk, nsplit == 1, ((int64_t)s * a.hq + hk * a.group) * a.max_splits + split, a.max_splits);
+}
+
+// Balanced schedule (pf_sched.h): four waves per workgroup, items are kv
+// heads (each covering its group of query heads).
+template <class T, int D, int U, bool OUT_F32>
+__global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) {
+  using Wv = MfmaWave<T, D, OUT_F32>;
+  using Tile = typename Wv::Tile;
+  __shared__ SchedLds L;
+  __shared__ __attribute__((aligned(16))) uint8_t vt[kSchedThreads / kWave][Wv::TILE_BYTES];
+  sched_build(a, L);
+  if (blockIdx.x == 0) {  // zero rows of empty sequences: one thread per sequence
+    const int64_t row_elems = (int64_t)a.hq * D;
+    for (int s0 = threadIdx.x; s0 < a.n; s0 += kSchedThreads) {
+      if (L.ctx[s0] != 0) continue;
+      for (int64_t e = 0; e < row_elems; ++e) {
+        if constexpr (OUT_F32) static_cast<float*>(a.out)[s0 * row_elems + e] = 0.f;
+        else static_cast<uint16_t*>(a.out)[s0 * row_elems + e] = 0;
+      }
+    }
+  }
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int gw = blockIdx.x * (kSchedThreads / kWave) + wave;
+  const int X = a.hkv;
+  const int64_t total = (int64_t)X * L.pfx[a.n];
+  if (total == 0) return;
+  const int64_t chunk = (total + a.waves - 1) / a.waves;
+  const int64_t wa = (int64_t)gw * chunk;
+  const int64_t wb = min(wa + chunk, total);
+  if (wa >= wb) return;
+
+  Wv w(a, vt[wave], lane);
+  int cur = -1, cs = 0, cx = 0, cP = 0, cp0 = 0, cplast = 0;
+  auto close_piece = [&]() {
+    const bool first = cp0 == 0, last = cplast == cP - 1;
+    const int item = cs * X + cx;
+    w.finish(cs, cx, first && last, ((int64_t)item + gw) * a.group, 1);
+    if (last && lane == 0) {
+      const int64_t start = (int64_t)X * L.pfx[cs] + (int64_t)cx * cP;
+      const int wf = (int)(start / chunk), wl = (int)((start + cP - 1) / chunk);
+      a.ws_meta[item] = make_int2(item + wf, wl - wf + 1);
+    }
+  };
+  for (int64_t base = wa; base < wb; base += kWave) {
+    const int cnt = (int)min((int64_t)kWave, wb - base);
+    int ls = 0, lx = 0, lp = 0, lP = 1, lpage = -1, lnv = 0;
+    if (lane < cnt) {
+      const PagePos pp = sched_locate(L, a.n, X, base + lane);
+      ls = pp.s;
+      lx = pp.x;
+      lp = pp.p;
+      lP = pp.P;
+      lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
+      lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
+    }
+    page_pipeline<U, Tile>(
+        cnt,
+        [&](int i, Tile& t) {
+          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(lx, i), t);
+        },
+        [&](int i, const Tile& t, bool ok) {
+          const int s = __builtin_amdgcn_readlane(ls, i);
+          const int x = __builtin_amdgcn_readlane(lx, i);
+          const int p = __builtin_amdgcn_readlane(lp, i);
+          if (s * X + x != cur) {
+            if (cur >= 0) close_piece();
+            cur = s * X + x;
+            cs = s;
+            cx = x;
+            cP = __builtin_amdgcn_readlane(lP, i);
+            cp0 = p;
+            w.begin(s, x);
+          }
+          cplast = p;
+          if (ok) w.page(t, __builtin_amdgcn_readlane(lnv, i));
+        });
+  }
+  if (cur >= 0) close_piece();
 }
 
 bool mfma_supports(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
+// One page per prefetch unit (two pages in flight per wave): measured faster
+// than two-page units, which cost a wave of occupancy.
+template <class T, int D, bool OUT_F32>
+static void launch_d(const AttnArgs& a, bool balanced, hipStream_t st) {
+  if (balanced)
+    hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, OUT_F32>), dim3(a.waves / (kSchedThreads / kWave)),
+                       dim3(kSchedThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_grid<T, D, 1, OUT_F32>), dim3(a.max_splits, a.hkv, a.n), dim3(kWave), 0, st, a);
+}
+
 template <class T>
-static int launch(const AttnArgs& a, int D, hipStream_t st) {
-  const dim3 grid(a.max_splits, a.hkv, a.n);
+static int launch_t(const AttnArgs& a, int D, bool balanced, hipStream_t st) {
   if (D == 64) {
-    if (a.out_f32) hipLaunchKernelGGL((attn_mfma_kernel<T, 64, true>), grid, dim3(kWave), 0, st, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<T, 64, false>), grid, dim3(kWave), 0, st, a);
+    if (a.out_f32) launch_d<T, 64, true>(a, balanced, st);
+    else launch_d<T, 64, false>(a, balanced, st);
     return PF_OK;
   }
   if (D == 128) {
-    if (a.out_f32) hipLaunchKernelGGL((attn_mfma_kernel<T, 128, true>), grid, dim3(kWave), 0, st, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<T, 128, false>), grid, dim3(kWave), 0, st, a);
+    if (a.out_f32) launch_d<T, 128, true>(a, balanced, st);
+    else launch_d<T, 128, false>(a, balanced, st);
     return PF_OK;
   }
   return PF_ERR_UNSUPPORTED;
 }
 
-int launch_mfma_f16(const AttnArgs& a, int D, hipStream_t st) { return launch<ElF16>(a, D, st); }
-int launch_mfma_bf16(const AttnArgs& a, int D, hipStream_t st) { return launch<ElBF16>(a, D, st); }
+int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, hipStream_t st) {
+  return dtype == PF_F16 ? launch_t<ElF16>(a, head_dim, balanced, st) : launch_t<ElBF16>(a, head_dim, balanced, st);
+}
+
+int mfma_balanced_waves_per_cu(int dtype, int head_dim) {
+  const void* k = nullptr;
+  if (head_dim == 64)
+    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 64, 1, false>)
+                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 64, 1, false>);
+  else if (head_dim == 128)
+    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 128, 1, false>)
+                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 128, 1, false>);
+  int blocks = 0;
+  if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, kSchedThreads, 0) != hipSuccess ||
+      blocks <= 0) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return blocks * (kSchedThreads / kWave);
+}
 
 }  // namespace pf

@@ -123,4 +123,46 @@ __device__ inline float strided_reduce(float v) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Streams npg pages through registers, U pages per unit, two units in flight:
+// the next unit's loads are issued before the current unit is used.  The
+// steady-state loop issues its prefetch unconditionally (so the compiler's
+// memory-counter waits only cover the unit being used); the last one or two
+// units are peeled.  load(i, tile) issues the loads of page i and returns
+// whether page i's table entry is a valid page; pages past npg load page
+// npg-1 again and are not used.  proc(i, tile, ok) is called for every page
+// in order.
+template <int U, class Tile, class LoadF, class ProcF>
+__device__ inline void page_pipeline(int npg, LoadF&& load, ProcF&& proc) {
+  Tile ta[U], tb[U];
+  bool oka[U], okb[U];
+  auto load_unit = [&](int j, Tile* t, bool* ok) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = j * U + u;
+      ok[u] = load(i < npg ? i : npg - 1, t[u]);
+    }
+  };
+  auto proc_unit = [&](int j, Tile* t, const bool* ok) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j * U + u < npg) proc(j * U + u, t[u], ok[u]);
+  };
+  const int nu = (npg + U - 1) / U;
+  load_unit(0, ta, oka);
+  int j = 0;
+  for (; j + 2 < nu; j += 2) {
+    load_unit(j + 1, tb, okb);
+    proc_unit(j, ta, oka);
+    load_unit(j + 2, ta, oka);
+    proc_unit(j + 1, tb, okb);
+  }
+  if (j + 1 < nu) {
+    load_unit(j + 1, tb, okb);
+    proc_unit(j, ta, oka);
+    proc_unit(j + 1, tb, okb);
+  } else {
+    proc_unit(j, ta, oka);
+  }
+}
+
 }  // namespace pf

@@ -210,6 +210,20 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
   return PF_OK;
 }
 
+}  // extern "C"
+
+int pf_fill_meta(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out) {
+  if (!pool || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
+  int32_t* lens = out + (size_t)n * (size_t)max_blocks;
+  const int st = pf_block_tables(pool, seq_ids, n, max_blocks, out, lens);
+  if (st != PF_OK) return st;
+  int32_t* last = lens + n;
+  for (int32_t i = 0; i < n; ++i) last[i] = lens[i] - 1;
+  return PF_OK;
+}
+
+extern "C" {
+
 int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {
   if (!pool) return PF_ERR_INVALID;
   std::lock_guard<std::mutex> lk(pool->mu);
@@ -224,6 +238,14 @@ int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {
       if (value != 0 && value != 1) return PF_ERR_INVALID;
       pool->gqa_mfma = value;
       return PF_OK;
+    case PF_OPT_SCHEDULE:
+      if (value < 0 || value > 2) return PF_ERR_INVALID;
+      pool->schedule = value;
+      return PF_OK;
+    case PF_OPT_WAVES_PER_CU:
+      if (value < 0 || value > 64) return PF_ERR_INVALID;
+      pool->waves_per_cu = value;
+      return PF_OK;
     default:
       return PF_ERR_INVALID;
   }
@@ -235,6 +257,8 @@ int pf_pool_get_option(const pf_pool* pool, int32_t option, int32_t* value) {
   switch (option) {
     case PF_OPT_SPLIT_TOKENS: *value = pool->split_tokens; return PF_OK;
     case PF_OPT_GQA_MFMA: *value = pool->gqa_mfma; return PF_OK;
+    case PF_OPT_SCHEDULE: *value = pool->schedule; return PF_OK;
+    case PF_OPT_WAVES_PER_CU: *value = pool->waves_per_cu; return PF_OK;
     default: return PF_ERR_INVALID;
   }
 }

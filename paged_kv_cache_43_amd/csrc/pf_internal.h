@@ -29,9 +29,15 @@ struct pf_pool {
   // Tuning options (pf_pool_set_option).
   int32_t split_tokens = 0;
   int32_t gqa_mfma = 1;
+  int32_t schedule = 0;       // 0 automatic, 1 fixed splits, 2 balanced
+  int32_t waves_per_cu = 0;   // balanced schedule: 0 = resident capacity
   // Instrumentation events around the partition kernel (hipEvent_t).
   void* ev_start = nullptr;
   void* ev_stop = nullptr;
 };
 
 size_t pf_elem_bytes(int32_t dtype);
+
+// Fill [n][max_blocks] tables, [n] lengths and [n] newest positions into
+// out (host memory) under the pool lock.  Same errors as pf_block_tables.
+int pf_fill_meta(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out);

@@ -80,6 +80,16 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(KvArgs a) {
   }
 }
 
+// Copy words from pinned host memory to device memory: 16 bytes per thread,
+// read over the bus by the kernel itself.
+__global__ __launch_bounds__(256) void upload_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                     int64_t n16, const int32_t* __restrict__ tail_src,
+                                                     int32_t* __restrict__ tail_dst, int tail) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) dst[i] = src[i];
+  if (i < tail) tail_dst[i] = tail_src[i];
+}
+
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 static int launch_grid(int64_t total, int* blocks) {
@@ -163,5 +173,25 @@ extern "C" int pf_gather_kv(const pf_pool* pool, int32_t layer, const int32_t* b
   int blocks;
   launch_grid(a.total, &blocks);
   hipLaunchKernelGGL(gather_kv_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream, a);
+  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}
+
+extern "C" int pf_export_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                                int32_t* staging_host, int32_t* meta_dev, void* hip_stream) {
+  using namespace pf;
+  if (!pool || n < 0 || max_blocks < 0) return PF_ERR_INVALID;
+  if (n == 0) return PF_OK;
+  if (!staging_host || !meta_dev || !aligned16(staging_host) || !aligned16(meta_dev)) return PF_ERR_INVALID;
+  const int st = pf_fill_meta(pool, seq_ids, n, max_blocks, staging_host);
+  if (st != PF_OK) return st;
+  const int64_t words = (int64_t)n * max_blocks + 2 * (int64_t)n;
+  const int64_t n16 = words / 4;
+  const int tail = (int)(words - n16 * 4);
+  const int64_t threads = n16 > tail ? n16 : tail;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return PF_ERR_INVALID;
+  hipLaunchKernelGGL(upload_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream,
+                     reinterpret_cast<const uint4*>(staging_host), reinterpret_cast<uint4*>(meta_dev), n16,
+                     staging_host + n16 * 4, meta_dev + n16 * 4, tail);
   return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
 }

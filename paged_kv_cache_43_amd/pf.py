@@ -31,6 +31,8 @@ PF_ERR_UNSUPPORTED = -7
 
 PF_OPT_SPLIT_TOKENS = 0
 PF_OPT_GQA_MFMA = 1
+PF_OPT_SCHEDULE = 2
+PF_OPT_WAVES_PER_CU = 3
 
 
 class pf_geometry(ctypes.Structure):
@@ -58,6 +60,7 @@ _SIGS = {
     "pf_num_seqs": (_i32, [_vp]),
     "pf_seq_len": (_i32, [_vp, _u64, _pi32]),
     "pf_block_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _pi32, _pi32]),
+    "pf_export_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _vp, _vp]),
     "pf_scatter_kv": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
     "pf_gather_kv": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pf_attention_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
@@ -68,6 +71,7 @@ _SIGS = {
     "pf_attention_split_tokens": (_i32, [_vp, _i32, _i32, _i32]),
     "pf_pool_set_timing_events": (_i32, [_vp, _vp, _vp]),
     "pf_attention_kernel": (_i32, [_vp, _i32]),
+    "pf_attention_waves": (_i32, [_vp, _i32, _i32, _i32]),
     "pf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -217,6 +221,14 @@ def pf_status_string(status):
 
 
 # ------------------------------------------------------------------ kernels
+def pf_export_tables(pool, seq_ids, max_blocks, staging_host, meta_dev, stream=None):
+    """``seq_ids`` a uint64 numpy array; ``staging_host`` a pinned int32 torch
+    tensor of at least n*max_blocks + 2n words; ``meta_dev`` a device tensor."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
+    return lib.pf_export_tables(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
+                                _dev(staging_host), _dev(meta_dev), _stream(stream))
+
+
 def pf_scatter_kv(pool, layer, k, v, tok_seq, tok_pos, num_tokens, bt_dev, num_rows, max_blocks,
                   stream=None):
     return lib.pf_scatter_kv(pool, layer, _dev(k), _dev(v), _dev(tok_seq), _dev(tok_pos), num_tokens,
@@ -234,6 +246,10 @@ def pf_attention_workspace_bytes(pool, n, num_q_heads, max_context_len):
 
 def pf_attention_kernel(pool, num_q_heads):
     return lib.pf_attention_kernel(pool, num_q_heads)
+
+
+def pf_attention_waves(pool, n, num_q_heads, max_context_len):
+    return lib.pf_attention_waves(pool, n, num_q_heads, max_context_len)
 
 
 def pf_attention_split_tokens(pool, n, num_q_heads, max_context_len):

@@ -81,25 +81,18 @@ class PagedKV:
         return t.pin_memory() if torch.cuda.is_available() else t
 
     def export_tables(self):
-        """Block tables, lengths and newest positions of sequences 0..n-1 into a
-        pinned staging buffer (a ring of four, so the host can run ahead), then
-        one asynchronous copy to the device on the current stream."""
-        w = self.w
+        """Block tables, lengths and newest positions of sequences 0..n-1 to the
+        device (pf_export_tables: pinned staging, one upload kernel on the
+        current stream).  A ring of four staging buffers lets the host run
+        ahead; a slot is reused only after its upload has run."""
         slot = self.ring_i
         self.ring_i = (slot + 1) % len(self.ring)
         if self.ring_ev[slot] is not None:
-            self.ring_ev[slot].synchronize()   # the copy that last read this slot is done
-        host = self.ring[slot].numpy()
-        nb = w.n * self.max_blocks
-        bt = host[:nb].reshape(w.n, self.max_blocks)
-        lens = host[nb:nb + w.n]
-        st, _, _ = pf.pf_block_tables(self.h, self.ids, self.max_blocks, bt, lens)
-        pf.check(st, "pf_block_tables")
-        np.subtract(lens, 1, out=host[nb + w.n:nb + 2 * w.n])
-        self.meta.copy_(self.ring[slot], non_blocking=True)
+            self.ring_ev[slot].synchronize()
+        st = pf.pf_export_tables(self.h, self.ids, self.max_blocks, self.ring[slot], self.meta)
+        pf.check(st, "pf_export_tables")
         if self.ring_ev[slot] is not None:
             self.ring_ev[slot].record()
-        return lens
 
     # --------------------------------------------------------------- kernels
     def scatter(self, layer, k, v, tok_seq, tok_pos, stream=None):

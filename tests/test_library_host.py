@@ -167,6 +167,11 @@ def test_errors_and_all_or_nothing():
     assert pf.pf_pool_set_option(h, pf.PF_OPT_SPLIT_TOKENS, 128) == pf.PF_OK
     assert pf.pf_pool_get_option(h, pf.PF_OPT_SPLIT_TOKENS) == (pf.PF_OK, 128)
     assert pf.pf_pool_set_option(h, 99, 1) == pf.PF_ERR_INVALID
+    for v, ok in ((0, True), (1, True), (2, True), (3, False), (-1, False)):
+        assert (pf.pf_pool_set_option(h, pf.PF_OPT_SCHEDULE, v) == pf.PF_OK) == ok
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_WAVES_PER_CU, 65) == pf.PF_ERR_INVALID
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_WAVES_PER_CU, 8) == pf.PF_OK
+    assert pf.pf_pool_get_option(h, pf.PF_OPT_WAVES_PER_CU) == (pf.PF_OK, 8)
     pf.pf_pool_destroy(h)
 
 
@@ -191,12 +196,26 @@ def test_kernel_entry_points_validate_before_launch():
     assert call(mc=17) == pf.PF_ERR_INVALID            # beyond max_blocks * B
     assert call(od="bf16") == pf.PF_ERR_INVALID         # neither f32 nor the pool dtype
     assert call(n=0) == pf.PF_OK                        # nothing to do
-    # needs a workspace: 2 splits
+    # needs a workspace: the balanced schedule always keeps partial records
     assert pf.pf_attention_workspace_bytes(h, 1, 1, 16 * 64) > 0
+    assert pf.pf_attention_waves(h, 1, 1, 16 * 64) > 0
     assert call(mb=64, mc=16 * 64) == pf.PF_ERR_WORKSPACE
+    # fixed splits: one split needs none, two splits need one
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SCHEDULE, 1) == pf.PF_OK
+    assert pf.pf_attention_waves(h, 1, 1, 16 * 64) == 0
+    assert pf.pf_attention_workspace_bytes(h, 1, 1, 16) == 0
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SPLIT_TOKENS, 16) == pf.PF_OK
+    assert pf.pf_attention_split_tokens(h, 1, 1, 32) == 16
+    assert pf.pf_attention_workspace_bytes(h, 1, 1, 32) > 0
+    assert call(mb=64, mc=32) == pf.PF_ERR_WORKSPACE
     assert pf.pf_scatter_kv(h, 3, A, A, A, A, 1, A, 1, 1, stream=0) == pf.PF_ERR_INVALID
     assert pf.pf_scatter_kv(h, 0, A + 8, A, A, A, 1, A, 1, 1, stream=0) == pf.PF_ERR_INVALID
     assert pf.pf_scatter_kv(h, 0, A, A, A, A, 0, A, 1, 1, stream=0) == pf.PF_OK   # no tokens
+    # table export: checked before any launch
+    stage = np.zeros(64, dtype=np.int32)
+    assert pf.pf_export_tables(h, np.array([5], dtype=np.uint64), 4, A, A, stream=0) == pf.PF_ERR_UNKNOWN_SEQ
+    assert pf.pf_export_tables(h, np.array([], dtype=np.uint64), 4, A, A, stream=0) == pf.PF_OK
+    assert pf.pf_export_tables(h, np.array([5], dtype=np.uint64), 4, A + 4, A, stream=0) == pf.PF_ERR_INVALID
     pf.pf_pool_destroy(h)
     # unsupported kernel shapes are reported, not launched
     st, h2 = pf.pf_pool_create(8, 8, 1, 1, 16, "f16")
