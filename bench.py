@@ -2,9 +2,9 @@
 
 A step is one pass of the whole hot path over the batch: grow every sequence
 by one token in the host allocator (one batched call), export the block tables
-and lengths (pinned host -> device copy), scatter the new tokens' K/V into
-their page slots for every layer, and run paged decode attention for every
-layer (partition kernel + split merge).  Inputs are resident in HBM when the
+and lengths and scatter the new tokens' K/V into their page slots for every
+layer (one fused launch reading pinned staging), and run paged decode
+attention for every layer (partition kernel + merge).  Inputs are resident in HBM when the
 timed region starts.  Sequences keep growing over the steps; bytes are counted
 from the actual lengths.
 
@@ -39,12 +39,16 @@ WORKLOADS = {
 }
 
 
+# Sources that define the attention partition kernels (the roofline kernel).
+ATTN_SOURCES = ("pf_attn.hip", "pf_attn_mfma.hip", "pf_sched.h", "pf_common.h", "pf_attn.h")
+
+
 def kernel_source_hash():
-    """Hash of the HIP/C++ sources the library is built from."""
+    """Hash of the sources of the attention partition kernels."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "paged_kv_cache_43_amd", "csrc")
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
+        if f in ATTN_SOURCES:
             h.update(f.encode())
             h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
@@ -86,7 +90,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
 
     dev = "cuda"
     w = inputs.Workload(name, frames=frames)
-    kv = runner.PagedKV(w, device=dev, sentinel=False, extra_tokens=steps + warmup + 1)
+    kv = runner.PagedKV(w, device=dev, sentinel=False, extra_tokens=2 * steps + warmup + 1)
     q = runner.fill_workload(kv, device=dev)
     stream = torch.cuda.current_stream()
     rng = np.random.default_rng(123)
@@ -96,10 +100,9 @@ def run_gpu(args, name, frames, steps, warmup, flush):
                         device=dev)
     ids = np.arange(w.n, dtype=np.uint64)
     base = w.ctx.astype(np.int64)
-    total_steps = warmup + steps
+    total_steps = warmup + 2 * steps   # warmup, K timed steps, K steps with kernel events
     max_ctx_final = int(base.max()) + total_steps
     kv.ensure_workspace(max_ctx_final)
-    tok_seq = torch.arange(w.n, dtype=torch.int32, device=dev)
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
     ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
     ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
@@ -111,38 +114,46 @@ def run_gpu(args, name, frames, steps, warmup, flush):
     torch.cuda.synchronize()
     ctx_per_step = []
 
-    def step(t):
+    def step(t, events):
         new_lens = (base + t + 1).astype(np.int32)
         st, _ = pf.pf_alloc_for_seqs(kv.h, ids, new_lens)
         pf.check(st, "pf_alloc_for_seqs")
         if flush:
             flush_buf.zero_()
-        ev_step[t][0].record(stream)
-        kv.export_tables()
+        if events:
+            ev_step[t][0].record(stream)
+        kv.decode_prepare(newk, newv)          # tables + every layer's new token, one launch
         mc = int(new_lens.max())
         for layer in range(w.layers):
-            kv.scatter(layer, newk[layer], newv[layer], tok_seq, kv.last_pos)
-        for layer in range(w.layers):
-            pf.check(pf.pf_pool_set_timing_events(kv.h, ev_a[t][layer].cuda_event,
-                                                  ev_b[t][layer].cuda_event))
+            if events:
+                pf.check(pf.pf_pool_set_timing_events(kv.h, ev_a[t][layer].cuda_event,
+                                                      ev_b[t][layer].cuda_event))
             kv.attention(layer, q[layer], out_t[layer], mc)
-        ev_step[t][1].record(stream)
+        if events:
+            pf.check(pf.pf_pool_set_timing_events(kv.h, None, None))
+            ev_step[t][1].record(stream)
         ctx_per_step.append(new_lens.astype(np.int64))
 
     for t in range(warmup):
-        step(t)
+        step(t, False)
     torch.cuda.synchronize()
+    # the K timed steps: no events in the stream
     t0 = time.perf_counter()
-    for t in range(warmup, total_steps):
-        step(t)
+    for t in range(warmup, warmup + steps):
+        step(t, flush)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pf.check(pf.pf_pool_set_timing_events(kv.h, None, None))
+    # K more steps with HIP events around every partition kernel (roofline)
+    for t in range(warmup + steps, total_steps):
+        step(t, True)
+    torch.cuda.synchronize()
 
-    timed = range(warmup, total_steps)
-    step_ms = [ev_step[t][0].elapsed_time(ev_step[t][1]) for t in timed]
-    part_ms = [ev_a[t][l].elapsed_time(ev_b[t][l]) for t in timed for l in range(w.layers)]
+    timed = range(warmup, warmup + steps)
+    evsteps = range(warmup + steps, total_steps)
+    step_ms = [ev_step[t][0].elapsed_time(ev_step[t][1]) for t in (timed if flush else evsteps)]
+    part_ms = [ev_a[t][l].elapsed_time(ev_b[t][l]) for t in evsteps for l in range(w.layers)]
     attn_bytes = [alg_bytes_attention(ctx_per_step[t], w, w.es) for t in timed]
+    part_bytes = [alg_bytes_attention(ctx_per_step[t], w, w.es) for t in evsteps]
     step_bytes = [b * w.layers + alg_bytes_scatter(w) * w.layers for b in attn_bytes]
     # free everything: the pool must come back whole
     for s in range(w.n):
@@ -158,7 +169,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
     # only when --flush is given, then from per-step events)
     ms_step = ms_step_events if flush else ms_step_wall
     avg_step_bytes = float(np.mean(step_bytes))
-    avg_attn_bytes = float(np.mean(attn_bytes))
+    avg_attn_bytes = float(np.mean(part_bytes))
     part_avg_ms = float(np.mean(part_ms))
     achieved = avg_attn_bytes / (part_avg_ms * 1e-3) / 1e9
     return dict(
@@ -224,7 +235,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="13b", choices=sorted(WORKLOADS))
     ap.add_argument("--frames", default="shuffled", choices=["shuffled", "ordered"])
-    ap.add_argument("--also", default="gqa", help="comma list of extra configs reported beside the headline")
+    ap.add_argument("--also", default="gqa,mixed,gpt2,tiny",
+                    help="comma list of extra configs reported beside the headline (both frame orders)")
     ap.add_argument("--flush", action="store_true", help="zero 1 GiB between steps (outside the step events)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -250,14 +262,27 @@ def main():
         del src, dst
     head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, args.flush)
     others = {}
+    head_ordered = run_gpu(args, args.config, "ordered" if args.frames == "shuffled" else "shuffled",
+                           args.steps, args.warmup, args.flush)
+    runs = [(args.config, head_ordered)]
     for extra in [x for x in args.also.split(",") if x and x != args.config]:
         for fr in ("shuffled", "ordered"):
-            r = run_gpu(args, extra, fr, args.steps, args.warmup, args.flush)
-            others["%s_%s" % (extra, fr)] = {
-                "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
-                "seqs_per_ms": round(r["seqs_per_ms"], 2), "ms_per_step": round(r["ms_step"], 4),
-                "attn_partition_avg_us": round(r["part_avg_us"], 2),
-                "attn_partition_GBps": round(r["achieved"], 1), "config": describe(r)}
+            runs.append((extra, run_gpu(args, extra, fr, args.steps, args.warmup, args.flush)))
+    for name, r in runs:
+        others["%s_%s" % (name, r["frames"])] = {
+            "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
+            "seqs_per_ms": round(r["seqs_per_ms"], 2), "ms_per_step": round(r["ms_step"], 4),
+            "attn_partition_avg_us": round(r["part_avg_us"], 2),
+            "attn_partition_GBps": round(r["achieved"], 1), "config": describe(r)}
+    # PageFault's pending "cost of scattering pages": shuffled / ordered attention time
+    cost = {}
+    for name in dict.fromkeys(n for n, _ in runs):
+        sh = head if name == args.config else None
+        key_s, key_o = "%s_shuffled" % name, "%s_ordered" % name
+        t_s = sh["part_avg_us"] if sh is not None and args.frames == "shuffled" else others.get(key_s, {}).get("attn_partition_avg_us")
+        t_o = others.get(key_o, {}).get("attn_partition_avg_us")
+        if t_s and t_o:
+            cost[name] = round(t_s / t_o, 3)
     w = head["w"]
     line = {
         "metric": "paged decode attention KV GB/s (% of MI355X HBM peak) + sequences/ms",
@@ -283,6 +308,7 @@ def main():
                      "median_launch_us": round(head["part_med_us"], 2),
                      "alg_bytes_per_launch": int(head["attn_bytes"])},
         "others": others,
+        "shuffled_over_ordered": cost,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)

@@ -144,6 +144,18 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
 int pf_export_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
                      int32_t* staging_host, int32_t* meta_dev, void* hip_stream);
 
+/* One decode step's host -> device work in one launch: pf_export_tables of
+ * seq_ids into meta_dev (same staging layout, followed by [n] destination
+ * pages, so staging_host needs n*max_blocks + 3n words) together with the
+ * scatter of each sequence's newest token (position length - 1) for layers
+ * layer0 .. layer0 + num_layers - 1, as pf_scatter_kv would do it.
+ *   k, v  device [num_layers][n][H][D] in the pool dtype, 16-byte aligned.
+ * Sequences of length 0 scatter nothing.  Errors: as pf_export_tables, plus
+ * PF_ERR_UNBOUND and PF_ERR_INVALID for a bad layer range or pointers. */
+int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                      int32_t* staging_host, int32_t* meta_dev, const void* k, const void* v,
+                      int32_t layer0, int32_t num_layers, void* hip_stream);
+
 /* Write num_tokens tokens' K and V into their page slots for one layer.
  *   k, v     device [num_tokens][H][D] in the pool dtype.
  *   tok_seq  device [num_tokens] int32: row of bt_dev holding the token's table.

@@ -222,6 +222,17 @@ int pf_fill_meta(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_
   return PF_OK;
 }
 
+int pf_fill_meta_step(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out) {
+  const int st = pf_fill_meta(pool, seq_ids, n, max_blocks, out);
+  if (st != PF_OK) return st;
+  const int32_t B = pool->g.block_size;
+  const int32_t* lens = out + (size_t)n * (size_t)max_blocks;
+  int32_t* dst = out + (size_t)n * (size_t)max_blocks + 2 * (size_t)n;
+  for (int32_t i = 0; i < n; ++i)
+    dst[i] = lens[i] > 0 ? out[(size_t)i * (size_t)max_blocks + (size_t)((lens[i] - 1) / B)] : -1;
+  return PF_OK;
+}
+
 extern "C" {
 
 int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {

@@ -41,3 +41,7 @@ size_t pf_elem_bytes(int32_t dtype);
 // Fill [n][max_blocks] tables, [n] lengths and [n] newest positions into
 // out (host memory) under the pool lock.  Same errors as pf_block_tables.
 int pf_fill_meta(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out);
+
+// As pf_fill_meta, followed by [n] pages holding each sequence's newest token
+// (-1 for length 0).
+int pf_fill_meta_step(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out);

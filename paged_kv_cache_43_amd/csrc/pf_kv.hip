@@ -90,6 +90,59 @@ __global__ __launch_bounds__(256) void upload_kernel(const uint4* __restrict__ s
   if (i < tail) tail_dst[i] = tail_src[i];
 }
 
+// Table upload (as upload_kernel) and the scatter of each sequence's newest
+// token for a range of layers, in one launch.  Threads [0, up_threads) copy
+// 16-byte words of the staging into the device table; the rest each move one
+// 16-byte column of one (layer, sequence, head, K|V) row, with the destination
+// page read from the staging (host memory) rather than the device table, so
+// the two halves do not depend on each other.
+struct PrepArgs {
+  const uint4* src;
+  uint4* dst;
+  int64_t n16;
+  const int32_t* tail_src;
+  int32_t* tail_dst;
+  int tail;
+  int64_t up_threads;
+  uint8_t* pool;
+  const uint8_t* k;
+  const uint8_t* v;
+  const int32_t* lens_host;  // staging: lengths
+  const int32_t* page_host;  // staging: newest token's page
+  int64_t page_elems;
+  int64_t sc_threads;
+  int32_t n, layer0, H, D, B, es, num_pages;
+};
+
+__global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < a.up_threads) {
+    if (i < a.n16) a.dst[i] = a.src[i];
+    if (i < a.tail) a.tail_dst[i] = a.tail_src[i];
+    return;
+  }
+  int64_t r = i - a.up_threads;
+  if (r >= a.sc_threads) return;
+  const int cols = a.D * a.es / 16;
+  const int col = (int)(r % cols);
+  r /= cols;
+  const int kind = (int)(r % 2);
+  r /= 2;
+  const int h = (int)(r % a.H);
+  r /= a.H;
+  const int s = (int)(r % a.n);
+  const int l = (int)(r / a.n);
+  const int32_t len = a.lens_host[s];
+  const int32_t page = a.page_host[s];
+  if (len <= 0 || page < 0 || page >= a.num_pages) return;
+  const int pos = len - 1;
+  const int64_t dst_el = (int64_t)page * a.page_elems +
+                         ((((int64_t)(a.layer0 + l) * a.H + h) * 2 + kind) * a.B + pos % a.B) * a.D;
+  const int64_t src_el = (((int64_t)l * a.n + s) * a.H + h) * (int64_t)a.D;
+  *reinterpret_cast<uint4*>(a.pool + dst_el * a.es + col * 16) =
+      *reinterpret_cast<const uint4*>((kind ? a.v : a.k) + src_el * a.es + col * 16);
+}
+
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 static int launch_grid(int64_t total, int* blocks) {
@@ -193,5 +246,48 @@ extern "C" int pf_export_tables(const pf_pool* pool, const uint64_t* seq_ids, in
   hipLaunchKernelGGL(upload_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream,
                      reinterpret_cast<const uint4*>(staging_host), reinterpret_cast<uint4*>(meta_dev), n16,
                      staging_host + n16 * 4, meta_dev + n16 * 4, tail);
+  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}
+
+extern "C" int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                                 int32_t* staging_host, int32_t* meta_dev, const void* k, const void* v,
+                                 int32_t layer0, int32_t num_layers, void* hip_stream) {
+  using namespace pf;
+  if (!pool || n < 0 || max_blocks < 0 || num_layers < 0) return PF_ERR_INVALID;
+  if (!pool->dev) return PF_ERR_UNBOUND;
+  const pf_geometry& g = pool->g;
+  if (layer0 < 0 || layer0 + num_layers > g.num_layers) return PF_ERR_INVALID;
+  if ((size_t)g.head_dim * pool->elem_bytes % 16 != 0) return PF_ERR_UNSUPPORTED;
+  if (n == 0) return PF_OK;
+  if (!staging_host || !meta_dev || !aligned16(staging_host) || !aligned16(meta_dev)) return PF_ERR_INVALID;
+  if (num_layers > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return PF_ERR_INVALID;
+  const int st = pf_fill_meta_step(pool, seq_ids, n, max_blocks, staging_host);
+  if (st != PF_OK) return st;
+  PrepArgs a{};
+  const int64_t words = (int64_t)n * max_blocks + 2 * (int64_t)n;
+  a.n16 = words / 4;
+  a.tail = (int)(words - a.n16 * 4);
+  a.src = reinterpret_cast<const uint4*>(staging_host);
+  a.dst = reinterpret_cast<uint4*>(meta_dev);
+  a.tail_src = staging_host + a.n16 * 4;
+  a.tail_dst = meta_dev + a.n16 * 4;
+  a.up_threads = a.n16 > a.tail ? a.n16 : a.tail;
+  a.pool = static_cast<uint8_t*>(pool->dev);
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.lens_host = staging_host + (int64_t)n * max_blocks;
+  a.page_host = staging_host + (int64_t)n * max_blocks + 2 * (int64_t)n;
+  a.page_elems = (int64_t)pool->page_elems;
+  a.n = n;
+  a.layer0 = layer0;
+  a.H = g.num_kv_heads;
+  a.D = g.head_dim;
+  a.B = g.block_size;
+  a.es = (int32_t)pool->elem_bytes;
+  a.num_pages = g.num_pages;
+  a.sc_threads = (int64_t)num_layers * n * g.num_kv_heads * 2 * (g.head_dim * a.es / 16);
+  const int64_t blocks = (a.up_threads + a.sc_threads + 255) / 256;
+  if (blocks > 0x7fffffff) return PF_ERR_INVALID;
+  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, a);
   return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
 }

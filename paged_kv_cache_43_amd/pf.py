@@ -61,6 +61,7 @@ _SIGS = {
     "pf_seq_len": (_i32, [_vp, _u64, _pi32]),
     "pf_block_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _pi32, _pi32]),
     "pf_export_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _vp, _vp]),
+    "pf_decode_prepare": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "pf_scatter_kv": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
     "pf_gather_kv": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pf_attention_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
@@ -227,6 +228,16 @@ def pf_export_tables(pool, seq_ids, max_blocks, staging_host, meta_dev, stream=N
     ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
     return lib.pf_export_tables(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
                                 _dev(staging_host), _dev(meta_dev), _stream(stream))
+
+
+def pf_decode_prepare(pool, seq_ids, max_blocks, staging_host, meta_dev, k, v, layer0, num_layers,
+                      stream=None):
+    """``staging_host`` pinned int32 with >= n*max_blocks + 3n words; ``k``, ``v``
+    device [num_layers][n][H][D]."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
+    return lib.pf_decode_prepare(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
+                                 _dev(staging_host), _dev(meta_dev), _dev(k), _dev(v), layer0, num_layers,
+                                 _stream(stream))
 
 
 def pf_scatter_kv(pool, layer, k, v, tok_seq, tok_pos, num_tokens, bt_dev, num_rows, max_blocks,

@@ -46,6 +46,7 @@ class PagedKV:
         # [n][max_blocks], lengths [n], and each sequence's newest position [n].
         nb = w.n * self.max_blocks
         self.meta_elems = nb + 2 * w.n
+        self.stage_elems = nb + 3 * w.n
         self.meta = torch.empty(max(self.meta_elems, 1), dtype=torch.int32, device=device)
         self.bt = self.meta[:nb].view(w.n, self.max_blocks)
         self.ctx = self.meta[nb:nb + w.n]
@@ -77,7 +78,7 @@ class PagedKV:
                 pf.check(pf.pf_free_seq(self.h, op[1]), "pf_free_seq")
 
     def _host_meta(self):
-        t = torch.empty(max(self.meta_elems, 1), dtype=torch.int32)
+        t = torch.empty(max(self.stage_elems, 1), dtype=torch.int32)
         return t.pin_memory() if torch.cuda.is_available() else t
 
     def export_tables(self):
@@ -91,6 +92,20 @@ class PagedKV:
             self.ring_ev[slot].synchronize()
         st = pf.pf_export_tables(self.h, self.ids, self.max_blocks, self.ring[slot], self.meta)
         pf.check(st, "pf_export_tables")
+        if self.ring_ev[slot] is not None:
+            self.ring_ev[slot].record()
+
+    def decode_prepare(self, k_new, v_new, layer0=0, num_layers=None):
+        """Export the tables and scatter every sequence's newest token for
+        layers layer0.. (k_new, v_new: device [layers][n][H][D]) in one launch."""
+        num_layers = self.w.layers - layer0 if num_layers is None else num_layers
+        slot = self.ring_i
+        self.ring_i = (slot + 1) % len(self.ring)
+        if self.ring_ev[slot] is not None:
+            self.ring_ev[slot].synchronize()
+        st = pf.pf_decode_prepare(self.h, self.ids, self.max_blocks, self.ring[slot], self.meta, k_new, v_new,
+                                  layer0, num_layers)
+        pf.check(st, "pf_decode_prepare")
         if self.ring_ev[slot] is not None:
             self.ring_ev[slot].record()
 
