@@ -14,9 +14,10 @@
 //    32c..) -- exactly the A operand of v_mfma_f32_16x16x32 -- straight from
 //    HBM into registers.
 //  * V: loaded with 16-byte coalesced loads and staged through LDS (a padded
-//    row-major tile, one per wave) so each lane can pick the four tokens x one
-//    dim that the A operand of v_mfma_f32_16x16x16 wants (V^T).  Tokens past
-//    the length are written to LDS as zeros (their K rows are masked to -inf).
+//    row-major tile, one per wave); one transposing LDS read (ds_read_b64_tr_b16)
+//    per 16-dim block gives each lane the four tokens x one dim that the A
+//    operand of v_mfma_f32_16x16x16 wants (V^T).  Tokens past the length are
+//    written to LDS as zeros (their K rows are masked to -inf).
 //  * The score accumulator puts tokens 4*(lane/16)+r of head lane%16 in each
 //    lane, which is exactly the B operand layout (P^T) of the value product,
 //    so probabilities never leave registers.  They are split into a 16-bit
@@ -68,18 +69,13 @@ struct Mfma<ElF16> {
 // fp32 -> (high, remainder) 16-bit patterns of type T, packed two per word.
 template <class T>
 __device__ inline void split_pack(const float* p, uint2* hi, uint2* lo) {
-  uint32_t h[4], r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = T::narrow_bits(p[i]);
-    float back[2];
-    T::widen(h[i], back);  // low half of the word holds the value
-    r[i] = T::narrow_bits(p[i] - back[0]);
-  }
-  hi->x = h[0] | (h[1] << 16);
-  hi->y = h[2] | (h[3] << 16);
-  lo->x = r[0] | (r[1] << 16);
-  lo->y = r[2] | (r[3] << 16);
+  hi->x = T::narrow2(p[0], p[1]);
+  hi->y = T::narrow2(p[2], p[3]);
+  float b[4];
+  T::widen(hi->x, b);
+  T::widen(hi->y, b + 2);
+  lo->x = T::narrow2(p[0] - b[0], p[1] - b[1]);
+  lo->y = T::narrow2(p[2] - b[2], p[3] - b[3]);
 }
 
 template <class T, bool OUT_F32>
@@ -88,8 +84,8 @@ __device__ inline void store_vec4(void* out, int64_t idx, const float* v) {
     *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
     uint2 w;
-    w.x = T::narrow_bits(v[0]) | (T::narrow_bits(v[1]) << 16);
-    w.y = T::narrow_bits(v[2]) | (T::narrow_bits(v[3]) << 16);
+    w.x = T::narrow2(v[0], v[1]);
+    w.y = T::narrow2(v[2], v[3]);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = w;
   }
 }
@@ -103,7 +99,9 @@ struct MfmaWave {
   static constexpr int DB = D / 16;                // 16-dim blocks of the value product
   static constexpr int VCH = D * ES / 16;          // 16-byte chunks per token row
   static constexpr int VL = kBlock * VCH / kWave;  // 16-byte V loads per lane per page
-  static constexpr int PITCH = D * ES + 8;         // LDS row pitch in bytes (bank spread)
+  // LDS row pitch in bytes: 16-byte aligned rows, and a pitch of 8 (mod 32)
+  // dwords so the transposed reads of one 16-lane group hit 32 distinct banks.
+  static constexpr int PITCH = D * ES + 32;
   static constexpr int TILE_BYTES = kBlock * PITCH;
   struct Tile {
     uint4 k[KC];
@@ -172,9 +170,7 @@ struct MfmaWave {
       const int ch = f % VCH;
       uint4 v = t.v[r];
       if (!full && tok >= nvalid) v = make_uint4(0, 0, 0, 0);
-      uint8_t* dst = vt + tok * PITCH + ch * 16;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
-      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(v.z, v.w);
+      *reinterpret_cast<uint4*>(vt + tok * PITCH + ch * 16) = v;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     // scores S^T: token 4*grp + r, head col
@@ -187,29 +183,39 @@ struct MfmaWave {
       z[r] = sc[r] * a.qscale;
       if (!full && 4 * grp + r >= nvalid) z[r] = -INFINITY;
     }
-    float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    pm = fmaxf(pm, shfl_xor(pm, 16));
-    pm = fmaxf(pm, shfl_xor(pm, 32));
-    const float mn = fmaxf(m, pm);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
+    // The reference max m moves only when some score exceeds it by more than
+    // 8 (log2 units): probabilities then stay below 2^8, and the cross-group
+    // max and the rescale are skipped for most pages.
+    const float lim = m + 8.f;
+    const bool over = (z[0] > lim) | (z[1] > lim) | (z[2] > lim) | (z[3] > lim);
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      pm = fmaxf(pm, shfl_xor(pm, 16));
+      pm = fmaxf(pm, shfl_xor(pm, 32));
+      const float mn = fmaxf(m, pm);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) acc[b] *= alpha;
+    }
     float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[r] - mn);
-    l = l * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[r] - m);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
     uint2 phi, plo;
     split_pack<T>(p, &phi, &plo);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // V^T operands with transposed LDS reads: in each 16-lane group, lane i
+    // receives element i%4 of the 8-byte chunk addressed by lane 4k + i/4
+    // (k = 0..3), so lane 4k + m points at row 4*grp + k, dims 16b + 4m.., and
+    // lane col ends up with dim 16b + col of tokens 4*grp .. 4*grp + 3.
+    const uint8_t* tsrc = vt + (4 * grp + col / 4) * PITCH + (4 * (col % 4)) * ES;
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      // V^T operand: dim 16b + col, tokens 4*grp + j
-      const uint8_t* src = vt + (4 * grp) * PITCH + (16 * b + col) * ES;
-      const uint32_t v0 = *reinterpret_cast<const uint16_t*>(src);
-      const uint32_t v1 = *reinterpret_cast<const uint16_t*>(src + PITCH);
-      const uint32_t v2 = *reinterpret_cast<const uint16_t*>(src + 2 * PITCH);
-      const uint32_t v3 = *reinterpret_cast<const uint16_t*>(src + 3 * PITCH);
-      const uint2 vop = make_uint2(v0 | (v1 << 16), v2 | (v3 << 16));
-      acc[b] *= alpha;
+      const s4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s4*)(tsrc + 16 * b * ES));
+      const uint2 vop = __builtin_bit_cast(uint2, vv);
       acc[b] = Mfma<T>::pv(vop, phi, acc[b]);
       acc[b] = Mfma<T>::pv(vop, plo, acc[b]);
     }

@@ -35,20 +35,24 @@ struct ElF16 {
   __device__ static inline uint32_t narrow_bits(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
   }
+  __device__ static inline uint32_t narrow2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, h2));
+  }
 };
 
 struct ElBF16 {
   static constexpr int es = 2;
   static constexpr int per_word = 2;
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
   __device__ static inline void widen(uint32_t w, float* o) {
     o[0] = __uint_as_float(w << 16);
     o[1] = __uint_as_float(w & 0xffff0000u);
   }
-  __device__ static inline uint32_t narrow_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;  // NaN stays NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                                  // nearest even
-    return u >> 16;
+  // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+  __device__ static inline uint32_t narrow_bits(float f) { return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f); }
+  __device__ static inline uint32_t narrow2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
   }
 };
 
