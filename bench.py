@@ -103,7 +103,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
     total_steps = warmup + 2 * steps   # warmup, K timed steps, K steps with kernel events
     max_ctx_final = int(base.max()) + total_steps
     kv.ensure_workspace(max_ctx_final)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if flush else None
+    flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev) if flush else None
     ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
     ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
     ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -119,7 +119,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         st, _ = pf.pf_alloc_for_seqs(kv.h, ids, new_lens)
         pf.check(st, "pf_alloc_for_seqs")
         if flush:
-            flush_buf.zero_()
+            flush_buf.amax()   # read 1 GiB: evicts the K/V from L2 and the 256 MB MALL, leaves nothing dirty
         if events:
             ev_step[t][0].record(stream)
         kv.decode_prepare(newk, newv)          # tables + every layer's new token, one launch
@@ -177,8 +177,68 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         ms_step_events=ms_step_events, value=avg_step_bytes / (ms_step * 1e-3) / 1e9,
         seqs_per_ms=w.n / ms_step, part_avg_us=part_avg_ms * 1e3,
         part_med_us=float(np.median(part_ms)) * 1e3, part_min_us=float(np.min(part_ms)) * 1e3,
+        part_sd_us=float(np.std(part_ms)) * 1e3,
         attn_bytes=avg_attn_bytes, achieved=achieved, split=split, waves=waves, mfma=bool(mfma),
         kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers))
+
+
+def run_twin(name, frames, reps):
+    """Paged attention vs the contiguous-cache twin (the same kernels with no
+    table walk) on one layer of the workload at its measured step: partition
+    kernel times from HIP events, alternating the two, and the largest output
+    difference (the twin must return the same bits)."""
+    import torch
+    from paged_kv_cache_43_amd import inputs, pf, runner
+
+    w = inputs.Workload(name, frames=frames)
+    kv = runner.PagedKV(w, sentinel=False)
+    q = runner.fill_workload(kv)
+    mc = int(w.ctx.max())
+    max_len = -(-mc // 16) * 16
+    k, v = kv.gather(0, max_len)
+    kh = k.permute(0, 2, 1, 3).contiguous()
+    vh = v.permute(0, 2, 1, 3).contiguous()
+    layouts = {"head_major": (kh.permute(0, 2, 1, 3), vh.permute(0, 2, 1, 3)), "token_major": (k, v)}
+    dt = torch.int32 if w.es == 4 else torch.int16
+    outs = {x: torch.empty((w.n, w.hq, w.d), dtype=dt, device="cuda") for x in ["paged"] + list(layouts)}
+    kv.ensure_workspace(mc)
+    # back to back, alternating, one event pair per launch; synchronized once
+    order = [x for _ in range(reps + 3) for x in outs]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in order]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for (a, b), x in zip(ev, order):
+        pf.check(pf.pf_pool_set_timing_events(kv.h, a.cuda_event, b.cuda_event))
+        if x == "paged":
+            kv.attention(0, q[0], outs[x], mc)
+        else:
+            kv.contiguous_attention(layouts[x][0], layouts[x][1], q[0], outs[x], mc)
+    pf.check(pf.pf_pool_set_timing_events(kv.h, None, None))
+    torch.cuda.synchronize()
+    times = {x: [] for x in outs}
+    for i, ((a, b), x) in enumerate(zip(ev, order)):
+        if i >= 3 * len(outs):
+            times[x].append(a.elapsed_time(b) * 1e3)
+    as_float = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    ref = outs["paged"]
+    res = {"paged_us": round(float(np.median(times["paged"])), 2)}
+    diff = 0.0
+    for x in layouts:
+        t = float(np.median(times[x]))
+        res["contiguous_%s_us" % x] = round(t, 2)
+        res["paged_slowdown_vs_%s" % x] = round(res["paged_us"] / t, 4)
+        got = outs[x]
+        d = (got.view(as_float).double() - ref.view(as_float).double()).abs().max().item()
+        diff = max(diff, float(d))
+        res["bitwise_equal_%s" % x] = bool(torch.equal(got, ref))
+    res["max_abs_paged_minus_contiguous"] = diff
+    res["alg_kv_bytes"] = int(w.ctx.sum()) * w.hkv * w.d * 2 * w.es
+    res["frames"] = frames
+    res["median_of"] = reps
+    kv.close()
+    return res
 
 
 def cpu_baseline(name, budget_s):
@@ -237,7 +297,11 @@ def main():
     ap.add_argument("--frames", default="shuffled", choices=["shuffled", "ordered"])
     ap.add_argument("--also", default="gqa,mixed,gpt2,tiny",
                     help="comma list of extra configs reported beside the headline (both frame orders)")
-    ap.add_argument("--flush", action="store_true", help="zero 1 GiB between steps (outside the step events)")
+    ap.add_argument("--flush", choices=["on", "off"], default="on",
+                    help="read a 1 GiB buffer before every step, outside the step's events (default on)")
+    ap.add_argument("--twin", default="13b,gqa",
+                    help="comma list of configs for the paged vs contiguous-cache comparison (shuffled frames)")
+    ap.add_argument("--twin-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -260,14 +324,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, args.flush)
+    head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, args.flush == "on")
     others = {}
     head_ordered = run_gpu(args, args.config, "ordered" if args.frames == "shuffled" else "shuffled",
-                           args.steps, args.warmup, args.flush)
+                           args.steps, args.warmup, args.flush == "on")
     runs = [(args.config, head_ordered)]
     for extra in [x for x in args.also.split(",") if x and x != args.config]:
         for fr in ("shuffled", "ordered"):
-            runs.append((extra, run_gpu(args, extra, fr, args.steps, args.warmup, args.flush)))
+            runs.append((extra, run_gpu(args, extra, fr, args.steps, args.warmup, args.flush == "on")))
     for name, r in runs:
         others["%s_%s" % (name, r["frames"])] = {
             "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
@@ -306,10 +370,17 @@ def main():
                      "traffic": measured_traffic(args.config),
                      "kernel": "attention partition", "avg_launch_us": round(head["part_avg_us"], 2),
                      "median_launch_us": round(head["part_med_us"], 2),
+                     "min_launch_us": round(head["part_min_us"], 2),
+                     "sd_launch_us": round(head["part_sd_us"], 2),
                      "alg_bytes_per_launch": int(head["attn_bytes"])},
         "others": others,
         "shuffled_over_ordered": cost,
     }
+    twin = {}
+    for name in [x for x in args.twin.split(",") if x]:
+        twin[name] = run_twin(name, "shuffled", args.twin_reps)
+    if twin:
+        line["paged_vs_contiguous"] = twin
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(line), flush=True)

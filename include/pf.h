@@ -214,6 +214,32 @@ int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
                               int32_t out_dtype, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
 
+/* The same attention over a contiguous per-sequence cache, with no table walk
+ * (PageFault, "Four stages": stage 1's contiguous cache is the baseline that
+ * stage 3's paged kernel is checked and timed against).  The kernels,
+ * schedule, split and merge are those of pf_paged_decode_attention; only the
+ * address of a 16-token block differs, so for the same K/V values, lengths and
+ * handle options the two entry points return the same bits.
+ *   pool     supplies the dtype, H, D and the kernel options only; it need not
+ *            be bound and its memory is not read.
+ *   k, v     device, pool dtype, 16-byte aligned.  Element d of kv head h of
+ *            token t of sequence i is k[i*seq_stride + t*token_stride +
+ *            h*head_stride + d] (strides in elements; each stride times the
+ *            element size a multiple of 16 bytes).  [n][max_len][H][D] (the
+ *            layout pf_gather_kv writes) and [n][H][max_len][D] are both of
+ *            this form.  The kernel reads tokens t < round_up(length, B) of
+ *            every sequence, all within max_len.
+ *   max_len  tokens per sequence in the cache, a positive multiple of B.
+ *   q, ctx_dev, n, max_context_len (<= max_len), scale, out, out_dtype,
+ *   workspace (sized by pf_attention_workspace_bytes): as
+ *            pf_paged_decode_attention.
+ * Errors: PF_ERR_INVALID, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED, PF_ERR_HIP. */
+int pf_contiguous_decode_attention(const pf_pool* pool, const void* q, int32_t num_q_heads, const void* k,
+                                   const void* v, int64_t seq_stride, int64_t token_stride, int64_t head_stride,
+                                   int32_t max_len, const int32_t* ctx_dev, int32_t n, int32_t max_context_len,
+                                   float scale, void* out, int32_t out_dtype, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------ options */
 
 typedef enum {

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "pf_common.h"
+
 namespace pf {
 
 struct AttnArgs {
@@ -22,11 +24,44 @@ struct AttnArgs {
   int32_t split_tokens, max_splits, out_f32;
   int32_t waves;           // balanced schedule: waves in the grid
   float qscale;            // scale * log2(e)
+  // Contiguous cache (no table): element (s, t, h, d) of K is
+  // kc[s*c_seq + t*c_tok + h*c_head + d], of V likewise in vc.
+  const void* kc;
+  const void* vc;
+  int64_t c_seq, c_tok, c_head;
 };
 
+// Where the 16 tokens of block p of sequence s live for kv head hk: byte
+// addresses of the K and V rows of the block's first token and the byte step
+// from one token to the next.  Paged: the block is pool page `page` (the
+// table entry), whose K and V tiles are adjacent 16 x D runs; an entry that is
+// not a valid page addresses page 0 instead (in bounds) and reports ok =
+// false.  Contiguous: the block sits in the caller's per-sequence cache.
+struct BlockAddr {
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t tok;
+  bool ok;
+};
+
+template <bool CONTIG, int D, int ES>
+__device__ inline BlockAddr block_addr(const AttnArgs& a, int page, int s, int p, int hk) {
+  if constexpr (CONTIG) {
+    const int64_t off = ((int64_t)s * a.c_seq + (int64_t)p * kBlock * a.c_tok + (int64_t)hk * a.c_head) * ES;
+    return {static_cast<const uint8_t*>(a.kc) + off, static_cast<const uint8_t*>(a.vc) + off, a.c_tok * ES, true};
+  } else {
+    const bool ok = (unsigned)page < (unsigned)a.num_pages;
+    const int64_t off =
+        ((int64_t)(ok ? page : 0) * a.page_elems + ((int64_t)a.layer * a.hkv + hk) * 2 * kBlock * D) * ES;
+    const uint8_t* k = static_cast<const uint8_t*>(a.pool) + off;
+    return {k, k + kBlock * D * ES, (int64_t)D * ES, ok};
+  }
+}
+
 bool mfma_supports(int head_dim);
-// Launch the matrix-core partition kernel (balanced or grid schedule).
-int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, hipStream_t st);
+// Launch the matrix-core partition kernel (balanced or grid schedule) over
+// the paged pool or, with contig, over a contiguous cache.
+int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, bool contig, hipStream_t st);
 // Resident waves per CU of the balanced matrix-core kernel (0 if unknown).
 int mfma_balanced_waves_per_cu(int dtype, int head_dim);
 

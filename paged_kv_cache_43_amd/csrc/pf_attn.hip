@@ -82,7 +82,8 @@ __device__ inline void zero_empty_rows(const AttnArgs& a, const SchedLds& L, int
 }
 
 // Per-wave state of the vector kernel: the current piece's online softmax.
-template <class T, int D, bool OUT_F32>
+// CONTIG: blocks come from a contiguous cache instead of pool pages.
+template <class T, int D, bool OUT_F32, bool CONTIG>
 struct ValuWave {
   using S = ValuShape<T, D>;
   struct Tile {
@@ -90,14 +91,10 @@ struct ValuWave {
   };
   const AttnArgs& a;
   const int lane, dc, tq;
-  const uint8_t* pool;
-  int64_t lane_off;  // elements
   float qf[S::VEC];
   float m, l, acc[S::VEC];
 
-  __device__ ValuWave(const AttnArgs& args, int ln)
-      : a(args), lane(ln), dc(ln % S::LPT), tq(ln / S::LPT),
-        pool(static_cast<const uint8_t*>(args.pool)), lane_off((int64_t)(tq * D + dc * S::VEC)) {}
+  __device__ ValuWave(const AttnArgs& args, int ln) : a(args), lane(ln), dc(ln % S::LPT), tq(ln / S::LPT) {}
 
   // Start a piece of (sequence s, query head h): q in log2 units, empty state.
   __device__ inline void begin(int s, int h) {
@@ -117,18 +114,17 @@ struct ValuWave {
     for (int i = 0; i < S::VEC; ++i) acc[i] = 0.f;
   }
 
-  // Issue the K and V loads of page `page` for query head h; an entry that is
-  // not a valid page reads page 0 (in bounds) and reports false.
-  __device__ inline bool load(int page, int h, Tile& t) const {
-    const bool ok = (unsigned)page < (unsigned)a.num_pages;
-    const int64_t head_off = ((int64_t)a.layer * a.hkv + h / a.group) * 2 * kBlock * D;
-    const uint8_t* p = pool + ((int64_t)(ok ? page : 0) * a.page_elems + head_off + lane_off) * S::ES;
+  // Issue the K and V loads of block p of sequence s (pool page `page`) for
+  // query head h; false if the table entry is not a valid page (page 0 is
+  // read instead, in bounds).
+  __device__ inline bool load(int page, int s, int p, int h, Tile& t) const {
+    const BlockAddr b = block_addr<CONTIG, D, S::ES>(a, page, s, p, h / a.group);
+    const int64_t lo = (int64_t)tq * b.tok + dc * S::VEC * S::ES;
 #pragma unroll
-    for (int r = 0; r < S::ROWS; ++r) t.k[r] = load_raw<S::NW>(p + (int64_t)r * S::TPI * D * S::ES);
+    for (int r = 0; r < S::ROWS; ++r) t.k[r] = load_raw<S::NW>(b.k + lo + r * S::TPI * b.tok);
 #pragma unroll
-    for (int r = 0; r < S::ROWS; ++r)
-      t.v[r] = load_raw<S::NW>(p + ((int64_t)kBlock * D + r * S::TPI * D) * S::ES);
-    return ok;
+    for (int r = 0; r < S::ROWS; ++r) t.v[r] = load_raw<S::NW>(b.v + lo + r * S::TPI * b.tok);
+    return b.ok;
   }
 
   // One page: nvalid of its 16 tokens are below the length.
@@ -195,9 +191,9 @@ struct ValuWave {
 };
 
 // Grid schedule: one wave per (split, query head, sequence).
-template <class T, int D, int U, bool OUT_F32>
+template <class T, int D, int U, bool OUT_F32, bool CONTIG>
 __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
-  using Wv = ValuWave<T, D, OUT_F32>;
+  using Wv = ValuWave<T, D, OUT_F32, CONTIG>;
   using Tile = typename Wv::Tile;
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -207,8 +203,9 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
   // the length load).
   const int split_pages = a.split_tokens / kBlock;
   const int pg0 = split * split_pages;
-  const int my_page =
-      (lane < split_pages && pg0 + lane < a.max_blocks) ? a.bt[(int64_t)s * a.max_blocks + pg0 + lane] : -1;
+  int my_page = -1;
+  if constexpr (!CONTIG)
+    if (lane < split_pages && pg0 + lane < a.max_blocks) my_page = a.bt[(int64_t)s * a.max_blocks + pg0 + lane];
   const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
   const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
   Wv w(a, lane);
@@ -225,7 +222,7 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
   const int npg = (tok_end - split * a.split_tokens + kBlock - 1) / kBlock;
   w.begin(s, h);
   page_pipeline<U, Tile>(
-      npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), h, t); },
+      npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), s, pg0 + i, h, t); },
       [&](int i, const Tile& t, bool ok) {
         if (ok) w.page(t, min(kBlock, tok_end - (pg0 + i) * kBlock));
       });
@@ -234,9 +231,9 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
 
 // Balanced schedule (pf_sched.h): four waves per workgroup, items are query
 // heads.
-template <class T, int D, int U, bool OUT_F32>
+template <class T, int D, int U, bool OUT_F32, bool CONTIG>
 __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) {
-  using Wv = ValuWave<T, D, OUT_F32>;
+  using Wv = ValuWave<T, D, OUT_F32, CONTIG>;
   using Tile = typename Wv::Tile;
   __shared__ SchedLds L;
   sched_build(a, L);
@@ -272,13 +269,14 @@ __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) 
       lx = pp.x;
       lp = pp.p;
       lP = pp.P;
-      lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
+      if constexpr (!CONTIG) lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
       lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
     }
     page_pipeline<U, Tile>(
         cnt,
         [&](int i, Tile& t) {
-          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(lx, i), t);
+          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
+                        __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
         },
         [&](int i, const Tile& t, bool ok) {
           const int s = __builtin_amdgcn_readlane(ls, i);
@@ -372,31 +370,31 @@ struct ValuUnit {
 template <class T, int D, bool OUT_F32>
 static const void* valu_kernel_ptr(bool balanced) {
   constexpr int U = ValuUnit<T, D>::U;
-  return balanced ? reinterpret_cast<const void*>(&attn_valu_balanced<T, D, U, OUT_F32>)
-                  : reinterpret_cast<const void*>(&attn_valu_grid<T, D, U, OUT_F32>);
+  return balanced ? reinterpret_cast<const void*>(&attn_valu_balanced<T, D, U, OUT_F32, false>)
+                  : reinterpret_cast<const void*>(&attn_valu_grid<T, D, U, OUT_F32, false>);
 }
 
-template <class T, int D, bool OUT_F32>
+template <class T, int D, bool OUT_F32, bool CONTIG>
 static void launch_valu(const AttnArgs& a, bool balanced, hipStream_t st) {
   constexpr int U = ValuUnit<T, D>::U;
   if (balanced)
-    hipLaunchKernelGGL((attn_valu_balanced<T, D, U, OUT_F32>), dim3(a.waves / (kSchedThreads / kWave)),
+    hipLaunchKernelGGL((attn_valu_balanced<T, D, U, OUT_F32, CONTIG>), dim3(a.waves / (kSchedThreads / kWave)),
                        dim3(kSchedThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_valu_grid<T, D, U, OUT_F32>), dim3(a.max_splits, a.hq, a.n), dim3(kWave), 0, st,
-                       a);
+    hipLaunchKernelGGL((attn_valu_grid<T, D, U, OUT_F32, CONTIG>), dim3(a.max_splits, a.hq, a.n), dim3(kWave),
+                       0, st, a);
 }
 
-template <class T, bool OUT_F32>
+template <class T, bool OUT_F32, bool CONTIG>
 static int dispatch_valu_d(const AttnArgs& a, int D, bool balanced, hipStream_t st) {
   switch (D) {
-    case 16: launch_valu<T, 16, OUT_F32>(a, balanced, st); return PF_OK;
-    case 32: launch_valu<T, 32, OUT_F32>(a, balanced, st); return PF_OK;
-    case 64: launch_valu<T, 64, OUT_F32>(a, balanced, st); return PF_OK;
-    case 128: launch_valu<T, 128, OUT_F32>(a, balanced, st); return PF_OK;
+    case 16: launch_valu<T, 16, OUT_F32, CONTIG>(a, balanced, st); return PF_OK;
+    case 32: launch_valu<T, 32, OUT_F32, CONTIG>(a, balanced, st); return PF_OK;
+    case 64: launch_valu<T, 64, OUT_F32, CONTIG>(a, balanced, st); return PF_OK;
+    case 128: launch_valu<T, 128, OUT_F32, CONTIG>(a, balanced, st); return PF_OK;
     case 256:
       if constexpr (T::es == 2) {
-        launch_valu<T, 256, OUT_F32>(a, balanced, st);
+        launch_valu<T, 256, OUT_F32, CONTIG>(a, balanced, st);
         return PF_OK;
       }
       return PF_ERR_UNSUPPORTED;
@@ -405,8 +403,12 @@ static int dispatch_valu_d(const AttnArgs& a, int D, bool balanced, hipStream_t 
 }
 
 template <class T>
-static int dispatch_valu(const AttnArgs& a, int D, bool balanced, hipStream_t st) {
-  return a.out_f32 ? dispatch_valu_d<T, true>(a, D, balanced, st) : dispatch_valu_d<T, false>(a, D, balanced, st);
+static int dispatch_valu(const AttnArgs& a, int D, bool balanced, bool contig, hipStream_t st) {
+  if (contig)
+    return a.out_f32 ? dispatch_valu_d<T, true, true>(a, D, balanced, st)
+                     : dispatch_valu_d<T, false, true>(a, D, balanced, st);
+  return a.out_f32 ? dispatch_valu_d<T, true, false>(a, D, balanced, st)
+                   : dispatch_valu_d<T, false, false>(a, D, balanced, st);
 }
 
 template <class T>
@@ -588,43 +590,34 @@ extern "C" size_t pf_attention_workspace_bytes(const pf_pool* pool, int32_t n, i
   return plan_workspace(make_plan(pool, n, num_q_heads, max_context_len), pool->g.head_dim);
 }
 
-extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
-                                         int32_t num_q_heads, const int32_t* bt_dev,
-                                         int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
-                                         int32_t max_context_len, float scale, void* out,
-                                         int32_t out_dtype, void* workspace, size_t workspace_bytes,
-                                         void* hip_stream) {
-  if (!pool) return PF_ERR_INVALID;
-  if (!pool->dev) return PF_ERR_UNBOUND;
+namespace {
+
+// Checks shared by both entry points, then plan, workspace and launches.  The
+// caller has filled the block source of `a` (pool and table, or contiguous
+// cache) and validated it.
+int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t num_q_heads,
+           const int32_t* ctx_dev, int32_t n, int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+           void* workspace, size_t workspace_bytes, void* hip_stream) {
   const pf_geometry& g = pool->g;
-  if (layer < 0 || layer >= g.num_layers || n < 0 || num_q_heads <= 0 ||
-      num_q_heads % g.num_kv_heads != 0 || max_blocks <= 0 || max_context_len < 0 ||
-      (int64_t)max_context_len > (int64_t)max_blocks * g.block_size)
+  if (n < 0 || num_q_heads <= 0 || num_q_heads % g.num_kv_heads != 0 || max_context_len < 0)
     return PF_ERR_INVALID;
   if (out_dtype != PF_F32 && out_dtype != g.dtype) return PF_ERR_INVALID;
   if (g.block_size != kBlock || !valu_supports(g.dtype, g.head_dim)) return PF_ERR_UNSUPPORTED;
   if (n == 0) return PF_OK;
   if (n > 65535 || num_q_heads > 65535) return PF_ERR_INVALID;
-  if (!q || !bt_dev || !ctx_dev || !out) return PF_ERR_INVALID;
+  if (!q || !ctx_dev || !out) return PF_ERR_INVALID;
   const size_t qa = (size_t)g.head_dim * pool->elem_bytes >= 16 ? 16 : 8;
   if (reinterpret_cast<uintptr_t>(q) % qa != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return PF_ERR_INVALID;
 
   const Plan p = make_plan(pool, n, num_q_heads, max_context_len);
   if (!p.balanced && p.splits > 65535) return PF_ERR_INVALID;
-  AttnArgs a{};
-  a.pool = pool->dev;
   a.q = q;
   a.out = out;
-  a.bt = bt_dev;
   a.ctx = ctx_dev;
-  a.page_elems = (int64_t)pool->page_elems;
-  a.layer = layer;
   a.hkv = g.num_kv_heads;
   a.hq = num_q_heads;
   a.group = num_q_heads / g.num_kv_heads;
-  a.num_pages = g.num_pages;
-  a.max_blocks = max_blocks;
   a.max_ctx = max_context_len;
   a.n = n;
   a.split_tokens = p.balanced ? kBlock : p.split;
@@ -649,12 +642,12 @@ extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, con
   if (pool->ev_start) hipEventRecord((hipEvent_t)pool->ev_start, st);
   int rc;
   if (p.mfma) {
-    rc = launch_mfma(a, g.dtype, g.head_dim, p.balanced, st);
+    rc = launch_mfma(a, g.dtype, g.head_dim, p.balanced, contig, st);
   } else {
     switch (g.dtype) {
-      case PF_F32: rc = dispatch_valu<ElF32>(a, g.head_dim, p.balanced, st); break;
-      case PF_F16: rc = dispatch_valu<ElF16>(a, g.head_dim, p.balanced, st); break;
-      default: rc = dispatch_valu<ElBF16>(a, g.head_dim, p.balanced, st); break;
+      case PF_F32: rc = dispatch_valu<ElF32>(a, g.head_dim, p.balanced, contig, st); break;
+      case PF_F16: rc = dispatch_valu<ElF16>(a, g.head_dim, p.balanced, contig, st); break;
+      default: rc = dispatch_valu<ElBF16>(a, g.head_dim, p.balanced, contig, st); break;
     }
   }
   if (rc != PF_OK) return rc;
@@ -669,4 +662,57 @@ extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, con
     if (hipGetLastError() != hipSuccess) return PF_ERR_HIP;
   }
   return PF_OK;
+}
+
+}  // namespace
+
+extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
+                                         int32_t num_q_heads, const int32_t* bt_dev,
+                                         int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
+                                         int32_t max_context_len, float scale, void* out,
+                                         int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                         void* hip_stream) {
+  if (!pool) return PF_ERR_INVALID;
+  if (!pool->dev) return PF_ERR_UNBOUND;
+  const pf_geometry& g = pool->g;
+  if (layer < 0 || layer >= g.num_layers || max_blocks <= 0 || max_context_len < 0 ||
+      (int64_t)max_context_len > (int64_t)max_blocks * g.block_size)
+    return PF_ERR_INVALID;
+  if (n > 0 && !bt_dev) return PF_ERR_INVALID;
+  AttnArgs a{};
+  a.pool = pool->dev;
+  a.bt = bt_dev;
+  a.page_elems = (int64_t)pool->page_elems;
+  a.layer = layer;
+  a.num_pages = g.num_pages;
+  a.max_blocks = max_blocks;
+  return attend(pool, a, false, q, num_q_heads, ctx_dev, n, max_context_len, scale, out, out_dtype, workspace,
+                workspace_bytes, hip_stream);
+}
+
+extern "C" int pf_contiguous_decode_attention(const pf_pool* pool, const void* q, int32_t num_q_heads,
+                                              const void* k, const void* v, int64_t seq_stride,
+                                              int64_t token_stride, int64_t head_stride, int32_t max_len,
+                                              const int32_t* ctx_dev, int32_t n, int32_t max_context_len,
+                                              float scale, void* out, int32_t out_dtype, void* workspace,
+                                              size_t workspace_bytes, void* hip_stream) {
+  if (!pool) return PF_ERR_INVALID;
+  const pf_geometry& g = pool->g;
+  if (max_len <= 0 || max_len % kBlock != 0 || max_context_len < 0 || max_context_len > max_len)
+    return PF_ERR_INVALID;
+  const int64_t es = (int64_t)pool->elem_bytes;
+  if (seq_stride <= 0 || token_stride <= 0 || head_stride <= 0 || (seq_stride * es) % 16 != 0 ||
+      (token_stride * es) % 16 != 0 || (head_stride * es) % 16 != 0)
+    return PF_ERR_INVALID;
+  if (n > 0 && (!k || !v || reinterpret_cast<uintptr_t>(k) % 16 != 0 || reinterpret_cast<uintptr_t>(v) % 16 != 0))
+    return PF_ERR_INVALID;
+  AttnArgs a{};
+  a.kc = k;
+  a.vc = v;
+  a.c_seq = seq_stride;
+  a.c_tok = token_stride;
+  a.c_head = head_stride;
+  a.max_blocks = max_len / kBlock;
+  return attend(pool, a, true, q, num_q_heads, ctx_dev, n, max_context_len, scale, out, out_dtype, workspace,
+                workspace_bytes, hip_stream);
 }

@@ -92,7 +92,8 @@ __device__ inline void store_vec4(void* out, int64_t idx, const float* v) {
 
 // Per-wave state of the matrix-core kernel: the current piece's online
 // softmax for the 16 score columns (query heads of one kv head, padded).
-template <class T, int D, bool OUT_F32>
+// CONTIG: blocks come from a contiguous cache instead of pool pages.
+template <class T, int D, bool OUT_F32, bool CONTIG>
 struct MfmaWave {
   static constexpr int ES = 2;
   static constexpr int KC = D / 32;                // 32-dim chunks of the score product
@@ -111,14 +112,12 @@ struct MfmaWave {
   uint8_t* vt;  // this wave's V staging tile in LDS
   const int lane, col, grp;
   const bool head_ok;
-  const uint8_t* pool;
   uint4 qop[KC];
   float m, l;  // running max (log2 units) of head col; this lane's share of the sum
   f4 acc[DB];
 
   __device__ MfmaWave(const AttnArgs& args, uint8_t* stage, int ln)
-      : a(args), vt(stage), lane(ln), col(ln % 16), grp(ln / 16), head_ok(ln % 16 < args.group),
-        pool(static_cast<const uint8_t*>(args.pool)) {}
+      : a(args), vt(stage), lane(ln), col(ln % 16), grp(ln / 16), head_ok(ln % 16 < args.group) {}
 
   // Start a piece of (sequence s, kv head hk): the Q^T operand (head col, dims
   // 32c + 8*grp .. +8; zero rows past the group) and an empty state.
@@ -143,20 +142,20 @@ struct MfmaWave {
     for (int b = 0; b < DB; ++b) acc[b] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Issue page `page`'s loads for kv head hk: K as score-product operands, V
-  // as 16-byte coalesced chunks.  An entry that is not a valid page reads
-  // page 0 instead (in bounds) and reports false.
-  __device__ inline bool load(int page, int hk, Tile& t) const {
-    const bool ok = (unsigned)page < (unsigned)a.num_pages;
-    const int64_t head_off = ((int64_t)a.layer * a.hkv + hk) * 2 * kBlock * D;
-    const uint8_t* p = pool + ((int64_t)(ok ? page : 0) * a.page_elems + head_off) * ES;
+  // Issue the loads of block p of sequence s (pool page `page`) for kv head
+  // hk: K as score-product operands, V as 16-byte coalesced chunks.  False if
+  // the table entry is not a valid page (page 0 is read instead, in bounds).
+  __device__ inline bool load(int page, int s, int p, int hk, Tile& t) const {
+    const BlockAddr b = block_addr<CONTIG, D, ES>(a, page, s, p, hk);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      t.k[c] = *reinterpret_cast<const uint4*>(p + (col * D + 32 * c + 8 * grp) * ES);
+      t.k[c] = *reinterpret_cast<const uint4*>(b.k + col * b.tok + (32 * c + 8 * grp) * ES);
 #pragma unroll
-    for (int r = 0; r < VL; ++r)
-      t.v[r] = *reinterpret_cast<const uint4*>(p + kBlock * D * ES + (r * kWave + lane) * 16);
-    return ok;
+    for (int r = 0; r < VL; ++r) {
+      const int f = r * kWave + lane;  // token f / VCH, 16-byte chunk f % VCH
+      t.v[r] = *reinterpret_cast<const uint4*>(b.v + (f / VCH) * b.tok + (f % VCH) * 16);
+    }
+    return b.ok;
   }
 
   // One page: nvalid of its 16 tokens are below the length.
@@ -250,9 +249,9 @@ struct MfmaWave {
 };
 
 // Grid schedule: one wave per (split, kv head, sequence).
-template <class T, int D, int U, bool OUT_F32>
+template <class T, int D, int U, bool OUT_F32, bool CONTIG>
 __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
-  using Wv = MfmaWave<T, D, OUT_F32>;
+  using Wv = MfmaWave<T, D, OUT_F32, CONTIG>;
   using Tile = typename Wv::Tile;
   __shared__ __attribute__((aligned(16))) uint8_t vt[Wv::TILE_BYTES];
   const int split = blockIdx.x;
@@ -261,8 +260,9 @@ __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
   const int lane = threadIdx.x;
   const int split_pages = a.split_tokens / kBlock;
   const int pg0 = split * split_pages;
-  const int my_page =
-      (lane < split_pages && pg0 + lane < a.max_blocks) ? a.bt[(int64_t)s * a.max_blocks + pg0 + lane] : -1;
+  int my_page = -1;
+  if constexpr (!CONTIG)
+    if (lane < split_pages && pg0 + lane < a.max_blocks) my_page = a.bt[(int64_t)s * a.max_blocks + pg0 + lane];
   const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
   const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
   Wv w(a, vt, lane);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
   const int npg = (tok_end - split * a.split_tokens + kBlock - 1) / kBlock;
   w.begin(s, hk);
   page_pipeline<U, Tile>(
-      npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), hk, t); },
+      npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), s, pg0 + i, hk, t); },
       [&](int i, const Tile& t, bool ok) {
         if (ok) w.page(t, min(kBlock, tok_end - (pg0 + i) * kBlock));
       });
@@ -289,9 +289,9 @@ __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
 
 // Balanced schedule (pf_sched.h): four waves per workgroup, items are kv
 // heads (each covering its group of query heads).
-template <class T, int D, int U, bool OUT_F32>
+template <class T, int D, int U, bool OUT_F32, bool CONTIG>
 __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) {
-  using Wv = MfmaWave<T, D, OUT_F32>;
+  using Wv = MfmaWave<T, D, OUT_F32, CONTIG>;
   using Tile = typename Wv::Tile;
   __shared__ SchedLds L;
   __shared__ __attribute__((aligned(16))) uint8_t vt[kSchedThreads / kWave][Wv::TILE_BYTES];
@@ -338,13 +338,14 @@ __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) 
       lx = pp.x;
       lp = pp.p;
       lP = pp.P;
-      lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
+      if constexpr (!CONTIG) lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
       lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
     }
     page_pipeline<U, Tile>(
         cnt,
         [&](int i, Tile& t) {
-          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(lx, i), t);
+          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
+                        __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
         },
         [&](int i, const Tile& t, bool ok) {
           const int s = __builtin_amdgcn_readlane(ls, i);
@@ -370,42 +371,50 @@ bool mfma_supports(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
 // One page per prefetch unit (two pages in flight per wave): measured faster
 // than two-page units, which cost a wave of occupancy.
-template <class T, int D, bool OUT_F32>
+template <class T, int D, bool OUT_F32, bool CONTIG>
 static void launch_d(const AttnArgs& a, bool balanced, hipStream_t st) {
   if (balanced)
-    hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, OUT_F32>), dim3(a.waves / (kSchedThreads / kWave)),
+    hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, OUT_F32, CONTIG>), dim3(a.waves / (kSchedThreads / kWave)),
                        dim3(kSchedThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_grid<T, D, 1, OUT_F32>), dim3(a.max_splits, a.hkv, a.n), dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_grid<T, D, 1, OUT_F32, CONTIG>), dim3(a.max_splits, a.hkv, a.n), dim3(kWave), 0,
+                       st, a);
+}
+
+template <class T, int D, bool CONTIG>
+static void launch_o(const AttnArgs& a, bool balanced, hipStream_t st) {
+  if (a.out_f32) launch_d<T, D, true, CONTIG>(a, balanced, st);
+  else launch_d<T, D, false, CONTIG>(a, balanced, st);
 }
 
 template <class T>
-static int launch_t(const AttnArgs& a, int D, bool balanced, hipStream_t st) {
+static int launch_t(const AttnArgs& a, int D, bool balanced, bool contig, hipStream_t st) {
   if (D == 64) {
-    if (a.out_f32) launch_d<T, 64, true>(a, balanced, st);
-    else launch_d<T, 64, false>(a, balanced, st);
+    if (contig) launch_o<T, 64, true>(a, balanced, st);
+    else launch_o<T, 64, false>(a, balanced, st);
     return PF_OK;
   }
   if (D == 128) {
-    if (a.out_f32) launch_d<T, 128, true>(a, balanced, st);
-    else launch_d<T, 128, false>(a, balanced, st);
+    if (contig) launch_o<T, 128, true>(a, balanced, st);
+    else launch_o<T, 128, false>(a, balanced, st);
     return PF_OK;
   }
   return PF_ERR_UNSUPPORTED;
 }
 
-int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, hipStream_t st) {
-  return dtype == PF_F16 ? launch_t<ElF16>(a, head_dim, balanced, st) : launch_t<ElBF16>(a, head_dim, balanced, st);
+int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, bool contig, hipStream_t st) {
+  return dtype == PF_F16 ? launch_t<ElF16>(a, head_dim, balanced, contig, st)
+                         : launch_t<ElBF16>(a, head_dim, balanced, contig, st);
 }
 
 int mfma_balanced_waves_per_cu(int dtype, int head_dim) {
   const void* k = nullptr;
   if (head_dim == 64)
-    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 64, 1, false>)
-                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 64, 1, false>);
+    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 64, 1, false, false>)
+                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 64, 1, false, false>);
   else if (head_dim == 128)
-    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 128, 1, false>)
-                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 128, 1, false>);
+    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 128, 1, false, false>)
+                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 128, 1, false, false>);
   int blocks = 0;
   if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, kSchedThreads, 0) != hipSuccess ||
       blocks <= 0) {

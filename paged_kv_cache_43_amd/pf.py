@@ -67,6 +67,9 @@ _SIGS = {
     "pf_attention_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
     "pf_paged_decode_attention": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
                                          ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
+    "pf_contiguous_decode_attention": (_i32, [_vp, _vp, _i32, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int64, _i32, _vp, _i32, _i32, ctypes.c_float, _vp,
+                                              _i32, _vp, _sz, _vp]),
     "pf_pool_set_option": (_i32, [_vp, _i32, _i32]),
     "pf_pool_get_option": (_i32, [_vp, _i32, _pi32]),
     "pf_attention_split_tokens": (_i32, [_vp, _i32, _i32, _i32]),
@@ -274,3 +277,13 @@ def pf_paged_decode_attention(pool, layer, q, num_q_heads, bt_dev, max_blocks, c
                                          _dev(ctx_dev), n, max_context_len, float(scale), _dev(out),
                                          DTYPES.get(out_dtype, out_dtype), _dev(workspace),
                                          workspace_bytes, _stream(stream))
+
+
+def pf_contiguous_decode_attention(pool, q, num_q_heads, k, v, seq_stride, token_stride, head_stride,
+                                   max_len, ctx_dev, n, max_context_len, scale, out, out_dtype, workspace,
+                                   workspace_bytes, stream=None):
+    return lib.pf_contiguous_decode_attention(pool, _dev(q), num_q_heads, _dev(k), _dev(v), seq_stride,
+                                              token_stride, head_stride, max_len, _dev(ctx_dev), n,
+                                              max_context_len, float(scale), _dev(out),
+                                              DTYPES.get(out_dtype, out_dtype), _dev(workspace),
+                                              workspace_bytes, _stream(stream))

@@ -18,6 +18,12 @@ def bits_to_device(bits, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(signed)).to(device)
 
 
+def _signed_bits(bits, dtype):
+    """A raw bit pattern as the signed integer torch stores for it."""
+    return int(np.array(bits, dtype=np.uint32 if inputs.DTYPE_BYTES[dtype] == 4 else np.uint16)
+               .view(_BITS_NP[dtype]))
+
+
 def bits_from_device(t):
     a = t.cpu().numpy()
     return a.view(np.uint32 if a.dtype == np.int32 else np.uint16)
@@ -36,9 +42,7 @@ class PagedKV:
         self.pool = torch.empty(nbytes // inputs.DTYPE_BYTES[w.dtype], dtype=_BITS_TORCH[w.dtype],
                                 device=device)
         if sentinel:
-            nan = inputs.NAN_BITS[w.dtype]
-            self.pool.fill_(int(np.array(nan, dtype=np.uint32 if w.es == 4 else np.uint16)
-                                .view(_BITS_NP[w.dtype])))
+            self.pool.fill_(_signed_bits(inputs.NAN_BITS[w.dtype], w.dtype))
         pf.check(pf.pf_pool_bind(self.h, self.pool, nbytes), "pf_pool_bind")
         self.max_blocks = max_blocks or w.max_blocks(extra_tokens)
         self.ids = np.arange(w.n, dtype=np.uint64)
@@ -130,10 +134,29 @@ class PagedKV:
                                           out_dtype or self.w.dtype, self.ws, self.ws_bytes, stream)
         pf.check(st, "pf_paged_decode_attention")
 
-    def gather(self, layer, max_len, stream=None):
+    def contiguous_attention(self, k, v, q, out, max_ctx, out_dtype=None, scale=0.0, stream=None, hq=None):
+        """pf_contiguous_decode_attention over k, v viewed as [n][max_len][H][D]
+        (any strides with the last dimension dense: the gather output, or a
+        [n][H][max_len][D] buffer permuted to that view), with this pool's
+        geometry, options and lengths."""
+        hq = hq or self.w.hq
+        assert k.shape == v.shape and k.stride() == v.stride() and k.stride(3) == 1
+        self.ensure_workspace(max_ctx, hq)
+        st = pf.pf_contiguous_decode_attention(self.h, q, hq, k, v, k.stride(0), k.stride(1), k.stride(2),
+                                               k.shape[1], self.ctx, self.w.n, max_ctx, scale, out,
+                                               out_dtype or self.w.dtype, self.ws, self.ws_bytes, stream)
+        pf.check(st, "pf_contiguous_decode_attention")
+
+    def gather(self, layer, max_len, stream=None, fill=None):
+        """Read-back into [n][max_len][H][D]; positions past a length keep
+        ``fill`` (raw bits) if given, else whatever the buffer held."""
         w = self.w
-        k = torch.empty((w.n, max_len, w.hkv, w.d), dtype=_BITS_TORCH[w.dtype], device=self.device)
-        v = torch.empty_like(k)
+        if fill is None:
+            k = torch.empty((w.n, max_len, w.hkv, w.d), dtype=_BITS_TORCH[w.dtype], device=self.device)
+        else:
+            k = torch.full((w.n, max_len, w.hkv, w.d), _signed_bits(fill, w.dtype), dtype=_BITS_TORCH[w.dtype],
+                           device=self.device)
+        v = torch.empty_like(k) if fill is None else k.clone()
         st = pf.pf_gather_kv(self.h, layer, self.bt, self.ctx, w.n, self.max_blocks, max_len, k, v,
                              stream)
         pf.check(st, "pf_gather_kv")

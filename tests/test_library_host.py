@@ -175,6 +175,37 @@ def test_errors_and_all_or_nothing():
     pf.pf_pool_destroy(h)
 
 
+def test_contiguous_entry_validates_before_launch():
+    """pf_contiguous_decode_attention: the pool (H=1, D=16, f16) gives only the
+    geometry and options, so an unbound pool is fine; every bad argument is
+    refused before any launch."""
+    h = _make(8)
+    A = 1 << 40                  # fake, never dereferenced, aligned address
+    D = 16
+
+    def call(**kw):
+        return pf.pf_contiguous_decode_attention(
+            h, A, kw.get("hq", 1), kw.get("k", A), kw.get("v", A), kw.get("ss", 64 * D), kw.get("ts", D),
+            kw.get("hs", D), kw.get("ml", 64), A, kw.get("n", 1), kw.get("mc", 16), 0.0, A,
+            kw.get("od", "f16"), kw.get("ws", None), kw.get("wsb", 0), stream=0)
+    assert call(ml=40) == pf.PF_ERR_INVALID            # not a multiple of B
+    assert call(ml=0) == pf.PF_ERR_INVALID
+    assert call(mc=80) == pf.PF_ERR_INVALID            # beyond max_len
+    assert call(mc=-1) == pf.PF_ERR_INVALID
+    assert call(ts=4) == pf.PF_ERR_INVALID             # 8 bytes: not a multiple of 16
+    assert call(hs=0) == pf.PF_ERR_INVALID
+    assert call(ss=-64 * D) == pf.PF_ERR_INVALID
+    assert call(k=A + 8) == pf.PF_ERR_INVALID          # misaligned
+    assert call(v=None) == pf.PF_ERR_INVALID
+    assert call(hq=0) == pf.PF_ERR_INVALID
+    assert call(od="bf16") == pf.PF_ERR_INVALID        # neither f32 nor the pool dtype
+    assert call(n=0) == pf.PF_OK                       # nothing to do
+    assert call(n=0, k=None, v=None) == pf.PF_OK
+    assert call(ml=1024, mc=1024) == pf.PF_ERR_WORKSPACE   # balanced schedule keeps partials
+    assert pf.pf_contiguous_decode_attention(None, A, 1, A, A, 64 * D, D, D, 64, A, 1, 16, 0.0, A, "f16",
+                                             None, 0, stream=0) == pf.PF_ERR_INVALID
+
+
 def test_kernel_entry_points_validate_before_launch():
     h = _make(8)
     # unbound pool
