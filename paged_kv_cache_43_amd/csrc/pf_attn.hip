@@ -94,6 +94,8 @@ struct ValuWave {
   float qf[S::VEC];
   float m, l, acc[S::VEC];
 
+  static constexpr bool kContig = CONTIG;
+
   __device__ ValuWave(const AttnArgs& args, int ln) : a(args), lane(ln), dc(ln % S::LPT), tq(ln / S::LPT) {}
 
   // Start a piece of (sequence s, query head h): q in log2 units, empty state.
@@ -170,6 +172,9 @@ struct ValuWave {
     }
   }
 
+  // Balanced schedule: items are query heads, one record per slot.
+  __device__ inline void finish_slot(int s, int h, bool whole, int64_t slot) { finish(s, h, whole, slot); }
+
   // Close the piece of row (s, h): the final output if the piece is the whole
   // context, else partial record `rec`.
   __device__ inline void finish(int s, int h, bool whole, int64_t rec) {
@@ -234,68 +239,12 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
 template <class T, int D, int U, bool OUT_F32, bool CONTIG>
 __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) {
   using Wv = ValuWave<T, D, OUT_F32, CONTIG>;
-  using Tile = typename Wv::Tile;
   __shared__ SchedLds L;
   sched_build(a, L);
   zero_empty_rows<T, OUT_F32>(a, L, D);
   const int lane = threadIdx.x % kWave;
-  const int gw = blockIdx.x * (kSchedThreads / kWave) + threadIdx.x / kWave;
-  const int X = a.hq;
-  const int64_t total = (int64_t)X * L.pfx[a.n];
-  if (total == 0) return;
-  const int64_t chunk = (total + a.waves - 1) / a.waves;
-  const int64_t wa = (int64_t)gw * chunk;
-  const int64_t wb = min(wa + chunk, total);
-  if (wa >= wb) return;
-
   Wv w(a, lane);
-  int cur = -1, cs = 0, cx = 0, cP = 0, cp0 = 0, cplast = 0;
-  auto close_piece = [&]() {
-    const bool first = cp0 == 0, last = cplast == cP - 1;
-    const int item = cs * X + cx;
-    w.finish(cs, cx, first && last, (int64_t)item + gw);
-    if (last && lane == 0) {
-      const int64_t start = (int64_t)X * L.pfx[cs] + (int64_t)cx * cP;
-      const int wf = (int)(start / chunk), wl = (int)((start + cP - 1) / chunk);
-      a.ws_meta[item] = make_int2(item + wf, wl - wf + 1);
-    }
-  };
-  for (int64_t base = wa; base < wb; base += kWave) {
-    const int cnt = (int)min((int64_t)kWave, wb - base);
-    int ls = 0, lx = 0, lp = 0, lP = 1, lpage = -1, lnv = 0;
-    if (lane < cnt) {
-      const PagePos pp = sched_locate(L, a.n, X, base + lane);
-      ls = pp.s;
-      lx = pp.x;
-      lp = pp.p;
-      lP = pp.P;
-      if constexpr (!CONTIG) lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
-      lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
-    }
-    page_pipeline<U, Tile>(
-        cnt,
-        [&](int i, Tile& t) {
-          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
-                        __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
-        },
-        [&](int i, const Tile& t, bool ok) {
-          const int s = __builtin_amdgcn_readlane(ls, i);
-          const int x = __builtin_amdgcn_readlane(lx, i);
-          const int p = __builtin_amdgcn_readlane(lp, i);
-          if (s * X + x != cur) {
-            if (cur >= 0) close_piece();
-            cur = s * X + x;
-            cs = s;
-            cx = x;
-            cP = __builtin_amdgcn_readlane(lP, i);
-            cp0 = p;
-            w.begin(s, x);
-          }
-          cplast = p;
-          if (ok) w.page(t, __builtin_amdgcn_readlane(lnv, i));
-        });
-  }
-  if (cur >= 0) close_piece();
+  sched_run<U>(a, L, a.hq, w, lane);
 }
 
 // Merge the pieces of every output row that was split: M = max m_j,
@@ -555,6 +504,8 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
   return p;
 }
 
+// Workspace: fp32 accumulators [records][D], (max, sum) pairs [records], and
+// for the balanced schedule the per-item (first record, pieces) pairs.
 size_t plan_workspace(const Plan& p, int head_dim) {
   if (p.records == 0) return 0;
   size_t bytes = (size_t)p.records * head_dim * 4 + (size_t)p.records * 8;
@@ -639,7 +590,7 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   if (p.balanced && need == 0) return PF_ERR_WORKSPACE;
 
   hipStream_t st = (hipStream_t)hip_stream;
-  if (pool->ev_start) hipEventRecord((hipEvent_t)pool->ev_start, st);
+  if (pool->ev_start) (void)hipEventRecord((hipEvent_t)pool->ev_start, st);
   int rc;
   if (p.mfma) {
     rc = launch_mfma(a, g.dtype, g.head_dim, p.balanced, contig, st);
@@ -652,7 +603,7 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   }
   if (rc != PF_OK) return rc;
   if (hipGetLastError() != hipSuccess) return PF_ERR_HIP;
-  if (pool->ev_stop) hipEventRecord((hipEvent_t)pool->ev_stop, st);
+  if (pool->ev_stop) (void)hipEventRecord((hipEvent_t)pool->ev_stop, st);
   if (p.records > 0) {
     switch (g.dtype) {
       case PF_F32: launch_merge<ElF32>(a, g.head_dim, p.balanced, p.items_per_seq, p.rows_per_item, st); break;

@@ -119,6 +119,8 @@ struct MfmaWave {
   __device__ MfmaWave(const AttnArgs& args, uint8_t* stage, int ln)
       : a(args), vt(stage), lane(ln), col(ln % 16), grp(ln / 16), head_ok(ln % 16 < args.group) {}
 
+  static constexpr bool kContig = CONTIG;
+
   // Start a piece of (sequence s, kv head hk): the Q^T operand (head col, dims
   // 32c + 8*grp .. +8; zero rows past the group) and an empty state.
   __device__ inline void begin(int s, int hk) {
@@ -221,6 +223,12 @@ struct MfmaWave {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 
+  // Balanced schedule: items are kv heads; slot k holds the group's records
+  // k * group .. k * group + group - 1.
+  __device__ inline void finish_slot(int s, int hk, bool whole, int64_t slot) {
+    finish(s, hk, whole, slot * a.group, 1);
+  }
+
   // Close the piece of (sequence s, kv head hk): the group's final outputs if
   // the piece is the whole context, else the partial record rec_base +
   // col * rec_mul of each query head.
@@ -292,7 +300,6 @@ __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
 template <class T, int D, int U, bool OUT_F32, bool CONTIG>
 __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) {
   using Wv = MfmaWave<T, D, OUT_F32, CONTIG>;
-  using Tile = typename Wv::Tile;
   __shared__ SchedLds L;
   __shared__ __attribute__((aligned(16))) uint8_t vt[kSchedThreads / kWave][Wv::TILE_BYTES];
   sched_build(a, L);
@@ -308,63 +315,8 @@ __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) 
   }
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int gw = blockIdx.x * (kSchedThreads / kWave) + wave;
-  const int X = a.hkv;
-  const int64_t total = (int64_t)X * L.pfx[a.n];
-  if (total == 0) return;
-  const int64_t chunk = (total + a.waves - 1) / a.waves;
-  const int64_t wa = (int64_t)gw * chunk;
-  const int64_t wb = min(wa + chunk, total);
-  if (wa >= wb) return;
-
   Wv w(a, vt[wave], lane);
-  int cur = -1, cs = 0, cx = 0, cP = 0, cp0 = 0, cplast = 0;
-  auto close_piece = [&]() {
-    const bool first = cp0 == 0, last = cplast == cP - 1;
-    const int item = cs * X + cx;
-    w.finish(cs, cx, first && last, ((int64_t)item + gw) * a.group, 1);
-    if (last && lane == 0) {
-      const int64_t start = (int64_t)X * L.pfx[cs] + (int64_t)cx * cP;
-      const int wf = (int)(start / chunk), wl = (int)((start + cP - 1) / chunk);
-      a.ws_meta[item] = make_int2(item + wf, wl - wf + 1);
-    }
-  };
-  for (int64_t base = wa; base < wb; base += kWave) {
-    const int cnt = (int)min((int64_t)kWave, wb - base);
-    int ls = 0, lx = 0, lp = 0, lP = 1, lpage = -1, lnv = 0;
-    if (lane < cnt) {
-      const PagePos pp = sched_locate(L, a.n, X, base + lane);
-      ls = pp.s;
-      lx = pp.x;
-      lp = pp.p;
-      lP = pp.P;
-      if constexpr (!CONTIG) lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
-      lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
-    }
-    page_pipeline<U, Tile>(
-        cnt,
-        [&](int i, Tile& t) {
-          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
-                        __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
-        },
-        [&](int i, const Tile& t, bool ok) {
-          const int s = __builtin_amdgcn_readlane(ls, i);
-          const int x = __builtin_amdgcn_readlane(lx, i);
-          const int p = __builtin_amdgcn_readlane(lp, i);
-          if (s * X + x != cur) {
-            if (cur >= 0) close_piece();
-            cur = s * X + x;
-            cs = s;
-            cx = x;
-            cP = __builtin_amdgcn_readlane(lP, i);
-            cp0 = p;
-            w.begin(s, x);
-          }
-          cplast = p;
-          if (ok) w.page(t, __builtin_amdgcn_readlane(lnv, i));
-        });
-  }
-  if (cur >= 0) close_piece();
+  sched_run<U>(a, L, a.hkv, w, lane);
 }
 
 bool mfma_supports(int head_dim) { return head_dim == 64 || head_dim == 128; }

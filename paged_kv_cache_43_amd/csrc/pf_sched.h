@@ -15,6 +15,13 @@
 // pair for the merge kernel.  Slices depend only on the lengths, so the work
 // split, and with it every rounding, is the same for any physical page order.
 //
+// On MI355X waves given equal slices finish far apart (the slowest XCD's
+// about a quarter of the kernel time after the average), but handing out the
+// stream at run time does not shorten the kernel: claiming finer chunks from
+// counters (one global counter, one per 32-wave group, or one per workgroup in
+// LDS) was measured equal or slower, since the kernel is bound by the chip's
+// total HBM throughput and extra chunks add pieces and partial records.
+//
 // Each workgroup of four waves computes the page-count prefix of all
 // sequences once, in LDS; waves then resolve their pages by binary search.
 #pragma once
@@ -98,6 +105,72 @@ __device__ inline PagePos sched_locate(const SchedLds& L, int n, int X, int64_t 
   r.x = (int)(rem / r.P);
   r.p = (int)(rem - (int64_t)r.x * r.P);
   return r;
+}
+
+// The balanced schedule's driver, shared by both kernels.  Wv provides
+// begin(s, x), load(page, s, p, x, tile) -> bool, page(tile, nvalid),
+// finish_slot(s, x, whole, slot) and kContig (no table).
+// The balanced schedule's driver, shared by both kernels: this wave's slice
+// of the stream, piece by piece.  Wv provides begin(s, x), load(page, s, p, x,
+// tile) -> bool, page(tile, nvalid), finish_slot(s, x, whole, slot) and
+// kContig (blocks addressed without a table).
+template <int U, class Wv>
+__device__ inline void sched_run(const AttnArgs& a, const SchedLds& L, int X, Wv& w, int lane) {
+  using Tile = typename Wv::Tile;
+  const int gw = blockIdx.x * (kSchedThreads / kWave) + threadIdx.x / kWave;
+  const int64_t total = (int64_t)X * L.pfx[a.n];
+  if (total == 0) return;
+  const int64_t chunk = (total + a.waves - 1) / a.waves;
+  const int64_t wa = (int64_t)gw * chunk;
+  const int64_t wb = min(wa + chunk, total);
+  if (wa >= wb) return;
+  int cur = -1, cs = 0, cx = 0, cP = 0, cp0 = 0, cplast = 0;
+  auto close_piece = [&]() {
+    const bool first = cp0 == 0, last = cplast == cP - 1;
+    const int item = cs * X + cx;
+    w.finish_slot(cs, cx, first && last, (int64_t)item + gw);
+    if (last && lane == 0) {
+      const int64_t start = (int64_t)X * L.pfx[cs] + (int64_t)cx * cP;
+      const int wf = (int)(start / chunk), wl = (int)((start + cP - 1) / chunk);
+      a.ws_meta[item] = make_int2(item + wf, wl - wf + 1);
+    }
+  };
+  for (int64_t base = wa; base < wb; base += kWave) {
+    const int cnt = (int)min((int64_t)kWave, wb - base);
+    int ls = 0, lx = 0, lp = 0, lP = 1, lpage = -1, lnv = 0;
+    if (lane < cnt) {
+      const PagePos pp = sched_locate(L, a.n, X, base + lane);
+      ls = pp.s;
+      lx = pp.x;
+      lp = pp.p;
+      lP = pp.P;
+      if constexpr (!Wv::kContig) lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
+      lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
+    }
+    page_pipeline<U, Tile>(
+        cnt,
+        [&](int i, Tile& t) {
+          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
+                        __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
+        },
+        [&](int i, const Tile& t, bool ok) {
+          const int s = __builtin_amdgcn_readlane(ls, i);
+          const int x = __builtin_amdgcn_readlane(lx, i);
+          const int p = __builtin_amdgcn_readlane(lp, i);
+          if (s * X + x != cur) {
+            if (cur >= 0) close_piece();
+            cur = s * X + x;
+            cs = s;
+            cx = x;
+            cP = __builtin_amdgcn_readlane(lP, i);
+            cp0 = p;
+            w.begin(s, x);
+          }
+          cplast = p;
+          if (ok) w.page(t, __builtin_amdgcn_readlane(lnv, i));
+        });
+  }
+  if (cur >= 0) close_piece();
 }
 
 }  // namespace pf
