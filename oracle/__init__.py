@@ -13,11 +13,15 @@ Modules, and the passages each one follows:
   (PageForge, "Four layers, one pointer moving through all of them" and
   "Five techniques": free-list allocator + block table; mini-infer,
   "Implementation Walkthrough": the free-list stack; PagedAttention blog,
-  "Architecture": allocate a new block only when the last one is full).
+  "Architecture": allocate a new block only when the last one is full), with
+  copy-on-write sharing: reference counts, fork, and a grow that copies a
+  shared block before writing into it (PagedAttention blog, "Copy-on-Write
+  for Parallel Sampling").
 * ``layout``       -- the pool image: element address of a token's K/V inside
   a page, the scatter of new tokens, and the read-back (gather) of a
   sequence's pages into contiguous K/V (PageFault, "The OS analogy": the
-  page-table walk; PageForge, "Four layers": K and V combined in one pool).
+  page-table walk; PageForge, "Four layers": K and V combined in one pool),
+  and the whole-page copies of copy-on-write.
 * ``attention``    -- the plain definition softmax(q.K^T.scale).V on contiguous
   read-back K/V, two-pass, no splitting (PagedAttention blog, "The Attention
   Kernel"; PageFault, "Four stages", stage 1 and 3), plus a pure-Python brute

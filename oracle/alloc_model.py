@@ -26,12 +26,33 @@ Readings where the pages are silent:
   holds no random number generator.
 * ``alloc(seq, new_len)`` takes the sequence's new total length; a new id
   creates the entry; a shorter length is invalid; on OOM nothing changes.
+
+Copy-on-write sharing (PagedAttention blog, "Copy-on-Write for Parallel
+Sampling"): several tables may hold the same physical page; a reference count
+per page says how many.  ``fork`` gives a new sequence the parent's table,
+raising every count by one.  ``free`` lowers the counts and returns a page to
+the stack only when its count reaches zero.  A write into a shared page first
+copies it: ``grow`` takes a fresh page, reports the (source, destination) copy,
+and puts the destination into the writing sequence's table only.  Readings
+where the blog is silent:
+
+* Tokens are only ever appended, so the only page a growth writes into is the
+  sequence's last page, and only if that page is partly filled; full shared
+  pages stay shared for good.  A grow therefore makes at most one copy.
+* The copy page is taken from the stack before the new pages of the same
+  grow, and it counts towards the all-or-nothing page need.
+* Plain ``alloc`` does no copying: if its growth would write into a shared
+  page it refuses (SHARED) and changes nothing, so a caller that does not
+  know about sharing can never overwrite another sequence's tokens.
+* The last holder of a page frees it; pages are pushed in the order the
+  freeing sequence's table lists them, last first, skipping pages still held.
 """
 
 OK = "ok"
 OOM = "oom"
 UNKNOWN_SEQ = "unknown_seq"
 INVALID = "invalid"
+SHARED = "shared"
 
 
 def blocks_for(length, block_size):
@@ -54,8 +75,17 @@ class AllocModel:
         self.stack = list(reversed(order))
         self.tables = {}
         self.lengths = {}
+        self.refs = [0] * num_pages
 
     # -- operations -----------------------------------------------------------
+    def _writes_shared(self, seq_id, new_len):
+        """True if growing to new_len writes into a partly filled last page
+        that another table also holds."""
+        table = self.tables.get(seq_id, [])
+        current = self.lengths.get(seq_id, 0)
+        return (new_len > current and current % self.block_size != 0
+                and self.refs[table[-1]] > 1)
+
     def alloc(self, seq_id, new_len):
         """Grow ``seq_id`` to ``new_len`` tokens.  Returns (status, n_new_pages)."""
         if new_len < 0:
@@ -64,20 +94,95 @@ class AllocModel:
         current = self.lengths.get(seq_id, 0)
         if new_len < current:
             return INVALID, 0
+        if self._writes_shared(seq_id, new_len):
+            return SHARED, 0
         need = blocks_for(new_len, self.block_size) - len(table)
         if need > len(self.stack):
             return OOM, 0
         new_pages = [self.stack.pop() for _ in range(need)]
+        for p in new_pages:
+            self.refs[p] = 1
         self.tables[seq_id] = table + new_pages
         self.lengths[seq_id] = new_len
         return OK, need
 
+    def fork(self, parent, child):
+        """``child`` starts as a copy of ``parent``'s table and length, sharing
+        every page.  Returns a status."""
+        if parent not in self.tables:
+            return UNKNOWN_SEQ
+        if child in self.tables:
+            return INVALID
+        self.tables[child] = list(self.tables[parent])
+        self.lengths[child] = self.lengths[parent]
+        for p in self.tables[child]:
+            self.refs[p] += 1
+        return OK
+
+    def grow(self, seq_id, new_len):
+        """Copy-on-write growth.  Returns (status, n_new_pages, copy) where
+        copy is (source page, destination page) or None; n_new_pages counts
+        every page taken from the stack, the copy's destination included."""
+        if new_len < 0:
+            return INVALID, 0, None
+        table = self.tables.get(seq_id, [])
+        current = self.lengths.get(seq_id, 0)
+        if new_len < current:
+            return INVALID, 0, None
+        cow = self._writes_shared(seq_id, new_len)
+        need = blocks_for(new_len, self.block_size) - len(table) + (1 if cow else 0)
+        if need > len(self.stack):
+            return OOM, 0, None
+        table = list(table)
+        copy = None
+        if cow:
+            src = table[-1]
+            dst = self.stack.pop()
+            self.refs[src] -= 1
+            self.refs[dst] = 1
+            table[-1] = dst
+            copy = (src, dst)
+        while len(table) < blocks_for(new_len, self.block_size):
+            p = self.stack.pop()
+            self.refs[p] = 1
+            table.append(p)
+        self.tables[seq_id] = table
+        self.lengths[seq_id] = new_len
+        return OK, need, copy
+
+    def grow_many(self, entries):
+        """Batch copy-on-write growth, all or nothing: ``entries`` is a list of
+        (seq_id, new_len) applied in order.  Returns (status, [n_new_pages],
+        [copies in entry order]).  A length below what the earlier entries
+        leave is INVALID (checked over the whole batch first); otherwise the
+        batch is OOM if the pages run out anywhere.  On failure nothing
+        changes."""
+        lens = dict(self.lengths)
+        for seq_id, new_len in entries:
+            if new_len < 0 or new_len < lens.get(seq_id, 0):
+                return INVALID, [0] * len(entries), []
+            lens[seq_id] = new_len
+        saved = (self.stack[:], {k: v[:] for k, v in self.tables.items()}, dict(self.lengths), self.refs[:])
+        counts, copies = [], []
+        for seq_id, new_len in entries:
+            st, nn, copy = self.grow(seq_id, new_len)
+            if st != OK:
+                self.stack, self.tables, self.lengths, self.refs = saved
+                return st, [0] * len(entries), []
+            counts.append(nn)
+            if copy is not None:
+                copies.append(copy)
+        return OK, counts, copies
+
     def free(self, seq_id):
-        """Return every page of ``seq_id`` to the pool and forget the sequence."""
+        """Drop ``seq_id``'s hold on its pages, returning those no other table
+        holds to the pool, and forget the sequence."""
         if seq_id not in self.tables:
             return UNKNOWN_SEQ
         for page in reversed(self.tables[seq_id]):
-            self.stack.append(page)
+            self.refs[page] -= 1
+            if self.refs[page] == 0:
+                self.stack.append(page)
         del self.tables[seq_id]
         del self.lengths[seq_id]
         return OK
@@ -92,6 +197,12 @@ class AllocModel:
     def seq_len(self, seq_id):
         return self.lengths[seq_id]
 
+    def refcount(self, page):
+        return self.refs[page]
+
+    def pages_in_use(self):
+        return self.num_pages - len(self.stack)
+
     def block_tables(self, seq_ids, max_blocks):
         """Dense int32-style table rows (padded with -1) and the lengths, as lists."""
         rows, lens = [], []
@@ -105,23 +216,28 @@ class AllocModel:
 
     # -- invariants (checked by the tests after every op) ----------------------
     def check_invariants(self):
-        live = []
+        holders = [0] * self.num_pages
         for s, t in self.tables.items():
             n = self.lengths[s]
             assert len(t) == blocks_for(n, self.block_size), "ceil(len/B) blocks per sequence"
             assert self.block_size * len(t) - n <= self.block_size - 1, "waste at most B-1 slots"
-            live.extend(t)
-        assert len(live) == len(set(live)), "a page is owned by two sequences"
-        assert not set(live) & set(self.stack), "a live page is also on the free list"
+            assert len(t) == len(set(t)), "a page twice in one table"
+            for p in t:
+                holders[p] += 1
+        assert holders == self.refs, "reference counts differ from the tables holding each page"
+        live = {p for p in range(self.num_pages) if holders[p] > 0}
+        assert not live & set(self.stack), "a live page is also on the free list"
         assert len(self.stack) + len(live) == self.num_pages, "pages leaked or duplicated"
         assert len(set(self.stack)) == len(self.stack), "page pushed twice"
 
 
 def replay(num_pages, block_size, initial_free_order, ops):
-    """Replay an op log ``[("alloc", seq, new_len) | ("free", seq), ...]``.
+    """Replay an op log ``[("alloc", seq, new_len) | ("free", seq) |
+    ("fork", parent, child) | ("grow", seq, new_len), ...]``.
 
-    Returns the model and, per op, ``(status, n_new_pages, free_pages)`` so a
-    log recorded from another implementation can be compared op by op.
+    Returns the model and, per op, ``(status, n_new_pages, free_pages)`` (for
+    "grow" a fourth item, the copy or None) so a log recorded from another
+    implementation can be compared op by op.
     """
     m = AllocModel(num_pages, block_size, initial_free_order)
     trace = []
@@ -130,6 +246,12 @@ def replay(num_pages, block_size, initial_free_order, ops):
             st, nn = m.alloc(op[1], op[2])
         elif op[0] == "free":
             st, nn = m.free(op[1]), 0
+        elif op[0] == "fork":
+            st, nn = m.fork(op[1], op[2]), 0
+        elif op[0] == "grow":
+            st, nn, copy = m.grow(op[1], op[2])
+            trace.append((st, nn, m.free_pages(), copy))
+            continue
         else:
             raise ValueError(op)
         trace.append((st, nn, m.free_pages()))

@@ -83,6 +83,24 @@ def scatter(pool, g, layer, k_bits, v_bits, tok_seq, tok_pos, tables):
     return out
 
 
+def copy_pages(pool, g, pairs):
+    """Copy-on-write page copies (PagedAttention blog, "Copy-on-Write for
+    Parallel Sampling": the new block gets the shared block's contents).  For
+    each (source, destination) pair in order, every element of the source page
+    -- all layers, heads, K and V, every slot -- is copied to the destination
+    page.  Returns a new pool image."""
+    out = pool.copy()
+    for src, dst in pairs:
+        for layer in range(g.L):
+            for h in range(g.H):
+                for kind in (K_KIND, V_KIND):
+                    for slot in range(g.B):
+                        a = elem_offset(g, src, layer, h, kind, slot, 0)
+                        b = elem_offset(g, dst, layer, h, kind, slot, 0)
+                        out[b:b + g.D] = out[a:a + g.D]
+    return out
+
+
 def readback(pool, g, layer, table, length):
     """Gather one sequence's K and V into contiguous ``[length][H][D]`` bit arrays."""
     kc = np.empty((length, g.H, g.D), dtype=pool.dtype)

@@ -163,6 +163,149 @@ def pin_lifo_reuse_order(o):
     assert m.table(2) == t
 
 
+def pin_cow_blog_tables(o):
+    """The blog's three sampled sequences: prefix blocks 7 and 13 held once by
+    all three tables (count 3), private blocks 2, 5, 9 after the divergence;
+    the prefix returns to the pool only with its last holder."""
+    g = GOLDEN["cow_tables_7_13"]
+    am = o.alloc_model
+    B = g["block_size"]
+    order = [7, 13, 2, 5, 9] + [p for p in range(32) if p not in (7, 13, 2, 5, 9)]
+    m = am.AllocModel(32, B, order)
+    assert m.alloc(0, 2 * B) == (am.OK, 2)
+    assert m.fork(0, 1) == am.OK and m.fork(0, 2) == am.OK
+    assert m.fork(0, 1) == am.INVALID and m.fork(9, 3) == am.UNKNOWN_SEQ
+    for p in g["shared"]:
+        assert m.refcount(p) == 3
+    assert m.pages_in_use() == 2                       # the prefix is stored once
+    for s in range(3):                                 # full last page: no copy, one new page each
+        assert m.grow(s, 2 * B + 1) == (am.OK, 1, None)
+    assert [m.table(s) for s in range(3)] == g["tables"]
+    m.check_invariants()
+    m.free(0)
+    assert m.refcount(7) == 2 and m.refcount(2) == 0 and m.free_pages() == 32 - 4
+    m.free(1)
+    m.free(2)
+    assert m.free_pages() == 32 and all(m.refcount(p) == 0 for p in range(32))
+    m.check_invariants()
+
+
+def pin_cow_beam_saving(o):
+    """Beam width 4 over a 1024-token prefix: the prefix pages exist once, so
+    sharing saves three copies of the prefix against private tables."""
+    g = GOLDEN["cow_beam4_prefix1024"]
+    am = o.alloc_model
+    B, W, P = g["block_size"], g["beam_width"], g["prefix_tokens"]
+    shared = am.AllocModel(1024, B)
+    shared.alloc(0, P)
+    for b in range(1, W):
+        shared.fork(0, b)
+    private = am.AllocModel(1024, B)
+    for b in range(W):
+        private.alloc(b, P)
+    prefix_pages = am.blocks_for(P, B)
+    assert private.pages_in_use() - shared.pages_in_use() == g["copies_saved"] * prefix_pages
+    for b in range(W):                                 # one decoded token each
+        assert shared.grow(b, P + 1)[0] == am.OK
+    assert shared.pages_in_use() == prefix_pages + W
+    shared.check_invariants()
+
+
+def pin_cow_copy_on_partial_page(o):
+    """A 20-token prefix (last page holds 4 tokens) shared three ways: the
+    first two writers into that page get copies, the last holder writes in
+    place; plain alloc refuses the shared write; every sequence reads back its
+    own history through the pool image, the copies included."""
+    am, L = o.alloc_model, o.layout
+    rng = _rng(21)
+    g = L.Geometry(12, 16, 2, 2, 4, 2)
+    m = am.AllocModel(12, 16, rng.permutation(12))
+    pool = L.empty_pool(g, 0x7E00)
+    hist = {}
+    prefix = rng.integers(0, 1 << 15, size=(20, g.H, g.D), dtype=np.uint16)
+    assert m.alloc(0, 20)[0] == am.OK
+    for layer in range(g.L):
+        pool = L.scatter(pool, g, layer, prefix, prefix ^ 0x1111, [0] * 20, list(range(20)), {0: m.table(0)})
+    m.fork(0, 1)
+    m.fork(0, 2)
+    before = (m.table(1), m.free_pages())
+    assert m.alloc(1, 21) == (am.SHARED, 0) and (m.table(1), m.free_pages()) == before
+    old_last = m.table(0)[1]
+    for s, expect_copy in ((1, True), (2, True), (0, False)):
+        st, nn, copy = m.grow(s, 21)
+        assert st == am.OK and nn == (1 if expect_copy else 0)
+        if expect_copy:
+            assert copy[0] == old_last and copy[1] == m.table(s)[1] and copy[1] != old_last
+            pool = L.copy_pages(pool, g, [copy])
+        else:
+            assert copy is None and m.table(s)[1] == old_last
+        tok = rng.integers(0, 1 << 15, size=(1, g.H, g.D), dtype=np.uint16)
+        hist[s] = tok
+        for layer in range(g.L):
+            pool = L.scatter(pool, g, layer, tok, tok ^ 0x1111, [s], [20], {s: m.table(s)})
+    assert m.refcount(old_last) == 1 and m.refcount(m.table(0)[0]) == 3
+    m.check_invariants()
+    for s in range(3):
+        want = np.concatenate([prefix, hist[s]])
+        for layer in range(g.L):
+            kc, vc = L.readback(pool, g, layer, m.table(s), 21)
+            assert np.array_equal(kc, want) and np.array_equal(vc, want ^ 0x1111)
+
+
+def pin_cow_batch_all_or_nothing(o):
+    """Batch grow: the copies count towards the page need; on OOM or an
+    invalid entry nothing changes; copies are reported in entry order."""
+    am = o.alloc_model
+    m = am.AllocModel(6, 16)
+    m.alloc(0, 20)                                     # pages 0, 1; page 1 partly filled
+    for c in (1, 2, 3):
+        m.fork(0, c)
+    snap = (dict((s, m.table(s)) for s in range(4)), m.free_pages(), [m.refcount(p) for p in range(6)])
+    st, counts, copies = m.grow_many([(s, 21) for s in range(4)] + [(0, 40)])   # 3 copies + 1 page > 4 free? no: 4 free
+    assert st == am.OK and counts == [1, 1, 1, 0, 1] and [c[0] for c in copies] == [1, 1, 1]
+    m2 = am.AllocModel(6, 16)
+    m2.alloc(0, 20)
+    for c in (1, 2, 3):
+        m2.fork(0, c)
+    st, counts, copies = m2.grow_many([(s, 21) for s in range(4)] + [(0, 60)])  # 3 copies + 2 pages > 4
+    assert st == am.OOM and copies == [] and counts == [0] * 5
+    assert (dict((s, m2.table(s)) for s in range(4)), m2.free_pages(), [m2.refcount(p) for p in range(6)]) == snap
+    st, _, _ = m2.grow_many([(1, 21), (1, 20)])
+    assert st == am.INVALID and m2.free_pages() == snap[1]
+
+
+def pin_cow_random_ops_invariants(o):
+    """Random fork / grow / alloc / free: reference counts equal the number of
+    tables holding each page after every op, nothing leaks, and the pool comes
+    back whole."""
+    am = o.alloc_model
+    rng = _rng(22)
+    m = am.AllocModel(96, 16, rng.permutation(96))
+    live, nxt = [], 0
+    for step in range(1500):
+        r = rng.random()
+        if not live or r < 0.2:
+            if m.alloc(nxt, int(rng.integers(1, 60)))[0] == am.OK:
+                live.append(nxt)
+            nxt += 1
+        elif r < 0.4:
+            if m.fork(int(rng.choice(live)), nxt) == am.OK:
+                live.append(nxt)
+            nxt += 1
+        elif r < 0.8:
+            s = int(rng.choice(live))
+            st, nn, copy = m.grow(s, m.seq_len(s) + int(rng.integers(0, 20)))
+            assert st in (am.OK, am.OOM)
+        else:
+            s = live.pop(int(rng.integers(len(live))))
+            assert m.free(s) == am.OK
+        m.check_invariants()
+    for s in live:
+        m.free(s)
+    assert m.free_pages() == 96 and not m.tables
+    m.check_invariants()
+
+
 # ----------------------------------------------------------------------------
 # O2 / O3 layout
 # ----------------------------------------------------------------------------

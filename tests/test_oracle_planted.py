@@ -124,6 +124,48 @@ class _LeakyModel(oracle.alloc_model.AllocModel):
         return oracle.alloc_model.OK
 
 
+class _CowKeepsSourceModel(oracle.alloc_model.AllocModel):
+    def grow(self, seq_id, new_len):
+        cow = self._writes_shared(seq_id, new_len) if seq_id in self.tables else False
+        st, nn, copy = super().grow(seq_id, new_len)
+        if cow and copy is not None:
+            self.refs[copy[0]] += 1                             # the source keeps the writer's hold
+        return st, nn, copy
+
+
+class _FreeIgnoresRefsModel(oracle.alloc_model.AllocModel):
+    def free(self, seq_id):
+        if seq_id not in self.tables:
+            return oracle.alloc_model.UNKNOWN_SEQ
+        for page in reversed(self.tables[seq_id]):
+            self.refs[page] = max(self.refs[page] - 1, 0)
+            if page not in self.stack:
+                self.stack.append(page)                         # shared pages freed too early
+        del self.tables[seq_id]
+        del self.lengths[seq_id]
+        return oracle.alloc_model.OK
+
+
+class _ForkWithoutRefsModel(oracle.alloc_model.AllocModel):
+    def fork(self, parent, child):
+        if parent not in self.tables:
+            return oracle.alloc_model.UNKNOWN_SEQ
+        if child in self.tables:
+            return oracle.alloc_model.INVALID
+        self.tables[child] = list(self.tables[parent])          # counts not raised
+        self.lengths[child] = self.lengths[parent]
+        return oracle.alloc_model.OK
+
+
+class _GrowInPlaceModel(oracle.alloc_model.AllocModel):
+    def _writes_shared(self, seq_id, new_len):
+        return False                                            # never copies
+
+
+def _copy_nothing(pool, g, pairs):
+    return pool.copy()
+
+
 MUTANTS = {
     "attention_without_scale": (oracle.attention, "attention", _no_scale),
     "attention_wrong_sign": (oracle.attention, "attention", _wrong_sign),
@@ -138,6 +180,11 @@ MUTANTS = {
     "fifo_free_list": (oracle.alloc_model, "AllocModel", _FifoModel),
     "free_pushes_forward": (oracle.alloc_model, "AllocModel", _ForwardPushModel),
     "free_leaks_a_page": (oracle.alloc_model, "AllocModel", _LeakyModel),
+    "cow_source_keeps_hold": (oracle.alloc_model, "AllocModel", _CowKeepsSourceModel),
+    "free_ignores_refcounts": (oracle.alloc_model, "AllocModel", _FreeIgnoresRefsModel),
+    "fork_without_refcounts": (oracle.alloc_model, "AllocModel", _ForkWithoutRefsModel),
+    "grow_writes_shared_page": (oracle.alloc_model, "AllocModel", _GrowInPlaceModel),
+    "copy_pages_copies_nothing": (oracle.layout, "copy_pages", _copy_nothing),
 }
 
 
