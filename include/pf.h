@@ -54,7 +54,8 @@ typedef enum {
   PF_ERR_UNBOUND = -4,      /* kernel call before pf_pool_bind */
   PF_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
   PF_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
-  PF_ERR_UNSUPPORTED = -7   /* valid but not built: block size / head dim */
+  PF_ERR_UNSUPPORTED = -7,  /* valid but not built: block size / head dim */
+  PF_ERR_SHARED = -8        /* growth would write into a page another table shares */
 } pf_status;
 
 typedef struct {
@@ -97,20 +98,57 @@ int pf_pool_bind(pf_pool* pool, void* dev_ptr, size_t bytes);
  * sequence.  *n_new_pages (nullable) receives the number of pages taken.
  * Errors: PF_ERR_INVALID (new_len < 0 or below the current length),
  * PF_ERR_OOM (not enough free pages: all or nothing, nothing changes; PageFault,
- * "Test": exhaustion and all-or-nothing).  O(1) per page. */
+ * "Test": exhaustion and all-or-nothing), PF_ERR_SHARED (the growth would
+ * write into the sequence's partly filled last page while another sequence
+ * shares it, see pf_fork_seq; nothing changes: use pf_grow_seqs, which copies
+ * it first).  Checked in the order INVALID, SHARED, OOM.  O(1) per page. */
 int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n_new_pages);
 
 /* Batch form of pf_alloc_for_seq for one decode step: grow seq_ids[i] to
  * new_lens[i] for i = 0..n-1, in order, under one lock.  All or nothing over
  * the whole batch: if any entry is invalid (PF_ERR_INVALID, checked first,
  * against the lengths earlier entries would leave) or the pages do not suffice
- * (PF_ERR_OOM), nothing changes.  n_new_pages (nullable) is [n].
+ * (PF_ERR_OOM), nothing changes; PF_ERR_SHARED as pf_alloc_for_seq, checked
+ * after INVALID and before OOM.  n_new_pages (nullable) is [n].
  * A sequence may appear more than once; later entries see earlier growth. */
 int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
                       int32_t* n_new_pages);
 
-/* Return every page of seq_id to the free stack (last page first, so the
- * sequence's first page ends on top) and forget the sequence.
+/* Copy-on-write sharing (PagedAttention blog, "Copy-on-Write for Parallel
+ * Sampling": sequences sampled from one prompt hold the prompt's blocks once,
+ * a reference count per block tracks the sharing, and a block is copied only
+ * when a sequence writes into it).
+ *
+ * Fork: child gets parent's table and length; every page of it is now held by
+ * one more table.  No page is taken or copied.  Errors: PF_ERR_UNKNOWN_SEQ
+ * (parent not live), PF_ERR_INVALID (child already live). */
+int pf_fork_seq(pf_pool* pool, uint64_t parent, uint64_t child);
+
+/* Copy-on-write form of pf_alloc_for_seqs.  Entry i grows seq_ids[i] to
+ * new_lens[i] (an unknown id creates the sequence).  If the growth writes
+ * into the sequence's partly filled last page while another table holds that
+ * page, a fresh page is taken first, the pair (shared page, fresh page) is
+ * appended to copies, and the fresh page replaces the shared one in this
+ * sequence's table only (the shared page's count drops by one); then new pages
+ * are appended as usual.  At most one copy per entry, taken before that
+ * entry's new pages.  The caller must run the copies (pf_copy_pages) before
+ * anything writes into the fresh pages.
+ *   n_new_pages  nullable [n]: pages taken by entry i, its copy included.
+ *   copies       [2n] int32, filled with *n_copies (source, destination) pairs
+ *                in entry order.
+ * All or nothing over the batch: PF_ERR_INVALID (a length below what earlier
+ * entries leave, checked first), PF_ERR_OOM (pages, copies included, do not
+ * suffice); on error nothing changes and *n_copies = 0. */
+int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
+                 int32_t* n_new_pages, int32_t* copies, int32_t* n_copies);
+
+/* Number of tables holding page (0 = on the free stack); -1 for a bad page id
+ * or a NULL handle. */
+int32_t pf_page_refcount(const pf_pool* pool, int32_t page);
+
+/* Release seq_id's hold on each of its pages and forget the sequence; pages no
+ * other table holds go back on the free stack, last page first (so the
+ * sequence's first page ends on top).
  * Errors: PF_ERR_UNKNOWN_SEQ (never allocated or already freed). */
 int pf_free_seq(pf_pool* pool, uint64_t seq_id);
 
@@ -168,6 +206,17 @@ int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, i
 int pf_scatter_kv(const pf_pool* pool, int32_t layer, const void* k, const void* v,
                   const int32_t* tok_seq, const int32_t* tok_pos, int32_t num_tokens,
                   const int32_t* bt_dev, int32_t num_rows, int32_t max_blocks, void* hip_stream);
+
+/* Run copy-on-write copies: for j < n, page pairs[2j] is copied to page
+ * pairs[2j+1] -- the whole page, every layer, head, K and V, all slots.
+ *   pairs  int32 [n][2], 8-byte aligned, in device memory or in pinned host
+ *          memory (read by the kernel when it runs: keep it unchanged until
+ *          the stream has passed this call); as pf_grow_seqs reports them.
+ * A pair with an id outside the pool copies nothing.  A destination that is
+ * also another pair's source or destination races.
+ * Errors: PF_ERR_INVALID, PF_ERR_UNBOUND, PF_ERR_UNSUPPORTED (page size not a
+ * multiple of 16 bytes), PF_ERR_HIP. */
+int pf_copy_pages(const pf_pool* pool, const int32_t* pairs, int32_t n, void* hip_stream);
 
 /* Read back sequences' K and V through their tables into contiguous buffers
  * k_out, v_out: device [n][max_len][H][D] in the pool dtype (PageForge, "Five

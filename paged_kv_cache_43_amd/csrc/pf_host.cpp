@@ -11,6 +11,14 @@
 // checked).  Freed pages go back last-page-first so a sequence of the same shape
 // allocated next gets the same pages in the same order (PageForge, "Does the
 // pool actually come back to zero?": batch 2 claims batch 1's pages).
+//
+// Copy-on-write sharing (PagedAttention blog, "Copy-on-Write for Parallel
+// Sampling"): tables may hold the same page; refs[page] counts them.  A fork
+// shares the parent's whole table; a free returns only pages nobody else
+// holds; a growth that would write into a shared page (only a partly filled
+// last page can be written: tokens are appended) either copies it first
+// (pf_grow_seqs, which reports the copy for pf_copy_pages) or is refused
+// (pf_alloc_for_seq / pf_alloc_for_seqs, PF_ERR_SHARED).
 #include <cstring>
 #include <limits>
 #include <new>
@@ -24,6 +32,20 @@ size_t pf_elem_bytes(int32_t dtype) {
     case PF_BF16: return 2;
     default: return 0;
   }
+}
+
+// True if growing e (length len) to new_len writes into its last page while
+// another table holds that page too.
+static bool writes_shared(const pf_pool* pool, const pf_seq_entry& e, int32_t new_len) {
+  return new_len > e.len && e.len % pool->g.block_size != 0 && !e.pages.empty() &&
+         pool->refs[(size_t)e.pages.back()] > 1;
+}
+
+static int32_t pop_page(pf_pool* pool) {
+  const int32_t p = pool->stack.back();
+  pool->stack.pop_back();
+  pool->refs[(size_t)p] = 1;
+  return p;
 }
 
 static bool mul_ok(size_t a, size_t b, size_t* out) {
@@ -55,6 +77,7 @@ int pf_pool_create(const pf_geometry* geom, const int32_t* initial_free_order, p
   p->elem_bytes = pf_elem_bytes(g.dtype);
   p->page_elems = pe;
   p->stack.resize((size_t)g.num_pages);
+  p->refs.assign((size_t)g.num_pages, 0);
   if (initial_free_order) {
     std::vector<uint8_t> seen((size_t)g.num_pages, 0);
     for (int32_t i = 0; i < g.num_pages; ++i) {
@@ -99,16 +122,14 @@ int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n
   const int32_t cur_len = it == pool->seqs.end() ? 0 : it->second.len;
   const size_t have = it == pool->seqs.end() ? 0 : it->second.pages.size();
   if (new_len < cur_len) return PF_ERR_INVALID;
+  if (it != pool->seqs.end() && writes_shared(pool, it->second, new_len)) return PF_ERR_SHARED;
   const int64_t B = pool->g.block_size;
   const size_t want = (size_t)(((int64_t)new_len + B - 1) / B);
   const size_t need = want - have;
   if (need > pool->stack.size()) return PF_ERR_OOM;  // all or nothing
   pf_seq_entry& e = it == pool->seqs.end() ? pool->seqs[seq_id] : it->second;
   e.pages.reserve(want);
-  for (size_t i = 0; i < need; ++i) {
-    e.pages.push_back(pool->stack.back());
-    pool->stack.pop_back();
-  }
+  for (size_t i = 0; i < need; ++i) e.pages.push_back(pop_page(pool));
   e.len = new_len;
   if (n_new_pages) *n_new_pages = (int32_t)need;
   return PF_OK;
@@ -122,35 +143,51 @@ int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new
   std::lock_guard<std::mutex> lk(pool->mu);
   const int64_t B = pool->g.block_size;
   // Validation pass: lengths and page counts as the batch would leave them.
-  std::unordered_map<uint64_t, std::pair<int32_t, size_t>> pending;  // id -> (len, pages)
-  size_t total = 0;
+  // A sequence's last page is shared only if it is still the page it had
+  // before the batch (pages taken in the batch are private).
+  struct Pending {
+    int32_t len;
+    size_t pages;
+    bool last_original;
+  };
+  std::unordered_map<uint64_t, Pending> pending;
   for (int32_t i = 0; i < n; ++i) {
     if (new_lens[i] < 0) return PF_ERR_INVALID;
     auto pit = pending.find(seq_ids[i]);
-    int32_t cur_len;
-    size_t have;
+    int32_t cur_len = 0;
     if (pit != pending.end()) {
-      cur_len = pit->second.first;
-      have = pit->second.second;
+      cur_len = pit->second.len;
     } else {
       auto it = pool->seqs.find(seq_ids[i]);
-      cur_len = it == pool->seqs.end() ? 0 : it->second.len;
-      have = it == pool->seqs.end() ? 0 : it->second.pages.size();
+      if (it != pool->seqs.end()) cur_len = it->second.len;
     }
     if (new_lens[i] < cur_len) return PF_ERR_INVALID;
+    pending[seq_ids[i]] = {new_lens[i], 0, true};
+  }
+  pending.clear();
+  size_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto pit = pending.find(seq_ids[i]);
+    Pending cur{0, 0, false};
+    auto it = pool->seqs.find(seq_ids[i]);
+    if (pit != pending.end()) {
+      cur = pit->second;
+    } else if (it != pool->seqs.end()) {
+      cur = {it->second.len, it->second.pages.size(), true};
+    }
+    if (cur.last_original && it != pool->seqs.end() && writes_shared(pool, it->second, new_lens[i]) &&
+        cur.len == it->second.len)
+      return PF_ERR_SHARED;
     const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
-    total += want - have;
-    pending[seq_ids[i]] = {new_lens[i], want};
+    total += want - cur.pages;
+    pending[seq_ids[i]] = {new_lens[i], want, cur.last_original && want == cur.pages};
   }
   if (total > pool->stack.size()) return PF_ERR_OOM;
   for (int32_t i = 0; i < n; ++i) {
     pf_seq_entry& e = pool->seqs[seq_ids[i]];
     const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
     const size_t need = want - e.pages.size();
-    for (size_t j = 0; j < need; ++j) {
-      e.pages.push_back(pool->stack.back());
-      pool->stack.pop_back();
-    }
+    for (size_t j = 0; j < need; ++j) e.pages.push_back(pop_page(pool));
     e.len = new_lens[i];
     if (n_new_pages) n_new_pages[i] = (int32_t)need;
   }
@@ -163,9 +200,109 @@ int pf_free_seq(pf_pool* pool, uint64_t seq_id) {
   auto it = pool->seqs.find(seq_id);
   if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
   const std::vector<int32_t>& pages = it->second.pages;
-  for (size_t i = pages.size(); i-- > 0;) pool->stack.push_back(pages[i]);
+  for (size_t i = pages.size(); i-- > 0;)
+    if (--pool->refs[(size_t)pages[i]] == 0) pool->stack.push_back(pages[i]);
   pool->seqs.erase(it);
   return PF_OK;
+}
+
+int pf_fork_seq(pf_pool* pool, uint64_t parent, uint64_t child) {
+  if (!pool) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(parent);
+  if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+  if (pool->seqs.count(child)) return PF_ERR_INVALID;
+  pf_seq_entry copy = it->second;
+  for (int32_t p : copy.pages) ++pool->refs[(size_t)p];
+  pool->seqs.emplace(child, std::move(copy));
+  return PF_OK;
+}
+
+int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
+                 int32_t* n_new_pages, int32_t* copies, int32_t* n_copies) {
+  if (n_copies) *n_copies = 0;
+  if (!pool || n < 0 || (n > 0 && (!seq_ids || !new_lens || !copies || !n_copies))) return PF_ERR_INVALID;
+  if (n_new_pages)
+    for (int32_t i = 0; i < n; ++i) n_new_pages[i] = 0;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  const int64_t B = pool->g.block_size;
+  // Dry run over the batch: lengths (INVALID first), then the pages it takes,
+  // copies included, with the reference counts as the batch changes them.
+  struct Pending {
+    int32_t len;
+    size_t pages;
+    int32_t last;  // last page id, or -1 for none / a page taken in this batch
+  };
+  std::unordered_map<uint64_t, int32_t> lens;
+  for (int32_t i = 0; i < n; ++i) {
+    if (new_lens[i] < 0) return PF_ERR_INVALID;
+    auto lit = lens.find(seq_ids[i]);
+    int32_t cur_len = 0;
+    if (lit != lens.end()) {
+      cur_len = lit->second;
+    } else {
+      auto it = pool->seqs.find(seq_ids[i]);
+      if (it != pool->seqs.end()) cur_len = it->second.len;
+    }
+    if (new_lens[i] < cur_len) return PF_ERR_INVALID;
+    lens[seq_ids[i]] = new_lens[i];
+  }
+  std::unordered_map<uint64_t, Pending> pending;
+  std::unordered_map<int32_t, int32_t> dref;  // reference count changes of the batch
+  size_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Pending cur{0, 0, -1};
+    auto pit = pending.find(seq_ids[i]);
+    if (pit != pending.end()) {
+      cur = pit->second;
+    } else {
+      auto it = pool->seqs.find(seq_ids[i]);
+      if (it != pool->seqs.end())
+        cur = {it->second.len, it->second.pages.size(), it->second.pages.empty() ? -1 : it->second.pages.back()};
+    }
+    const bool cow = new_lens[i] > cur.len && cur.len % B != 0 && cur.last >= 0 &&
+                     pool->refs[(size_t)cur.last] + dref[cur.last] > 1;
+    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+    total += want - cur.pages + (cow ? 1 : 0);
+    if (cow) {
+      --dref[cur.last];
+      cur.last = -1;
+    }
+    if (want > cur.pages) cur.last = -1;
+    pending[seq_ids[i]] = {new_lens[i], want, cur.last};
+  }
+  if (total > pool->stack.size()) return PF_ERR_OOM;
+  int32_t nc = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pf_seq_entry& e = pool->seqs[seq_ids[i]];
+    int32_t taken = 0;
+    if (writes_shared(pool, e, new_lens[i])) {
+      const int32_t src = e.pages.back();
+      const int32_t dst = pop_page(pool);
+      --pool->refs[(size_t)src];
+      e.pages.back() = dst;
+      copies[2 * nc] = src;
+      copies[2 * nc + 1] = dst;
+      ++nc;
+      ++taken;
+    }
+    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+    while (e.pages.size() < want) {
+      e.pages.push_back(pop_page(pool));
+      ++taken;
+    }
+    e.len = new_lens[i];
+    if (n_new_pages) n_new_pages[i] = taken;
+  }
+  *n_copies = nc;
+  return PF_OK;
+}
+
+int32_t pf_page_refcount(const pf_pool* pool, int32_t page) {
+  if (!pool) return -1;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  if (page < 0 || page >= pool->g.num_pages) return -1;
+  return pool->refs[(size_t)page];
 }
 
 int32_t pf_free_pages(const pf_pool* pool) {
@@ -292,6 +429,7 @@ const char* pf_status_string(int status) {
     case PF_ERR_WORKSPACE: return "workspace missing or too small";
     case PF_ERR_HIP: return "HIP runtime error";
     case PF_ERR_UNSUPPORTED: return "unsupported block size or head dim";
+    case PF_ERR_SHARED: return "growth would write into a page another sequence shares (use pf_grow_seqs)";
     default: return "unknown status";
   }
 }

@@ -21,6 +21,8 @@ struct pf_pool {
   size_t page_elems = 0;       // L * H * 2 * B * D
   // LIFO free stack of page ids; the top is the back of the vector.
   std::vector<int32_t> stack;
+  // Per page: how many block tables hold it (0 = free).
+  std::vector<int32_t> refs;
   std::unordered_map<uint64_t, pf_seq_entry> seqs;
   mutable std::mutex mu;
   // Caller-owned device memory bound with pf_pool_bind.

@@ -90,6 +90,25 @@ __global__ __launch_bounds__(256) void upload_kernel(const uint4* __restrict__ s
   if (i < tail) tail_dst[i] = tail_src[i];
 }
 
+// Copy-on-write page copies (PagedAttention blog, "Copy-on-Write for Parallel
+// Sampling": the new block receives the shared block's contents): pair j
+// copies page pairs[2j] to page pairs[2j+1], all layers, heads, K and V.  A
+// page is one contiguous run of page_bytes, so the copy is a flat 16-byte
+// stream; consecutive threads take consecutive chunks of one pair (reads and
+// writes both coalesced).  Pairs with an id outside the pool copy nothing.
+__global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* pool, const int32_t* pairs, int64_t chunks,
+                                                         int64_t total, int32_t num_pages) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t j = i / chunks;
+    const int64_t c = i - j * chunks;
+    const int32_t src = pairs[2 * j], dst = pairs[2 * j + 1];
+    if (src < 0 || src >= num_pages || dst < 0 || dst >= num_pages) continue;
+    reinterpret_cast<uint4*>(pool + (int64_t)dst * chunks * 16)[c] =
+        reinterpret_cast<const uint4*>(pool + (int64_t)src * chunks * 16)[c];
+  }
+}
+
 // Table upload (as upload_kernel) and the scatter of each sequence's newest
 // token for a range of layers, in one launch.  Threads [0, up_threads) copy
 // 16-byte words of the staging into the device table; the rest each move one
@@ -289,5 +308,21 @@ extern "C" int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, i
   const int64_t blocks = (a.up_threads + a.sc_threads + 255) / 256;
   if (blocks > 0x7fffffff) return PF_ERR_INVALID;
   hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, a);
+  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}
+
+extern "C" int pf_copy_pages(const pf_pool* pool, const int32_t* pairs, int32_t n, void* hip_stream) {
+  if (!pool || n < 0) return PF_ERR_INVALID;
+  if (!pool->dev) return PF_ERR_UNBOUND;
+  if (n == 0) return PF_OK;
+  if (!pairs || (reinterpret_cast<uintptr_t>(pairs) & 7) != 0) return PF_ERR_INVALID;
+  const size_t page_bytes = pool->page_elems * pool->elem_bytes;
+  if (page_bytes % 16 != 0) return PF_ERR_UNSUPPORTED;
+  const int64_t chunks = (int64_t)(page_bytes / 16);
+  const int64_t total = chunks * n;
+  int blocks = 0;
+  if (pf::launch_grid(total, &blocks) != PF_OK) return PF_ERR_INVALID;
+  hipLaunchKernelGGL(pf::copy_pages_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream,
+                     static_cast<uint8_t*>(pool->dev), pairs, chunks, total, pool->g.num_pages);
   return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
 }

@@ -28,6 +28,7 @@ PF_ERR_UNBOUND = -4
 PF_ERR_WORKSPACE = -5
 PF_ERR_HIP = -6
 PF_ERR_UNSUPPORTED = -7
+PF_ERR_SHARED = -8
 
 PF_OPT_SPLIT_TOKENS = 0
 PF_OPT_GQA_MFMA = 1
@@ -56,6 +57,10 @@ _SIGS = {
     "pf_alloc_for_seq": (_i32, [_vp, _u64, _i32, _pi32]),
     "pf_alloc_for_seqs": (_i32, [_vp, ctypes.POINTER(_u64), _pi32, _i32, _pi32]),
     "pf_free_seq": (_i32, [_vp, _u64]),
+    "pf_fork_seq": (_i32, [_vp, _u64, _u64]),
+    "pf_grow_seqs": (_i32, [_vp, ctypes.POINTER(_u64), _pi32, _i32, _pi32, _pi32, _pi32]),
+    "pf_page_refcount": (_i32, [_vp, _i32]),
+    "pf_copy_pages": (_i32, [_vp, _vp, _i32, _vp]),
     "pf_free_pages": (_i32, [_vp]),
     "pf_num_seqs": (_i32, [_vp]),
     "pf_seq_len": (_i32, [_vp, _u64, _pi32]),
@@ -174,6 +179,32 @@ def pf_alloc_for_seqs(pool, seq_ids, new_lens, n_new_out=None):
 
 def pf_free_seq(pool, seq_id):
     return lib.pf_free_seq(pool, seq_id)
+
+
+def pf_fork_seq(pool, parent, child):
+    return lib.pf_fork_seq(pool, parent, child)
+
+
+def pf_grow_seqs(pool, seq_ids, new_lens):
+    """Copy-on-write batch growth.  Returns (status, n_new_pages array,
+    copies array [n_copies][2] of (source, destination) page ids)."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
+    lens, lens_p = _host_i32(new_lens)
+    nn = np.zeros(len(ids), dtype=np.int32)
+    copies = np.zeros(max(2 * len(ids), 2), dtype=np.int32)
+    nc = ctypes.c_int32(0)
+    st = lib.pf_grow_seqs(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), lens_p, len(ids),
+                          nn.ctypes.data_as(_pi32), copies.ctypes.data_as(_pi32), ctypes.byref(nc))
+    return st, nn, copies[:2 * nc.value].reshape(nc.value, 2)
+
+
+def pf_page_refcount(pool, page):
+    return lib.pf_page_refcount(pool, page)
+
+
+def pf_copy_pages(pool, pairs, n, stream=None):
+    """``pairs``: device tensor / pinned host tensor / address of int32 [n][2]."""
+    return lib.pf_copy_pages(pool, _dev(pairs), n, _stream(stream))
 
 
 def pf_free_pages(pool):

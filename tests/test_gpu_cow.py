@@ -1,0 +1,163 @@
+"""GPU: copy-on-write prefix sharing end to end (PagedAttention blog,
+"Copy-on-Write for Parallel Sampling").  The page-copy kernel against the
+oracle's pool image, bit for bit; then prompts forked into beams that decode
+together: the batch grow's copies run on the GPU before the new tokens are
+scattered, tables and reference counts match the oracle's model at every
+step, attention over the aliased tables matches the oracle on each beam's own
+history, and the read-back of every beam is exactly its history."""
+import numpy as np
+import pytest
+
+import gpu_util as gu
+import oracle.alloc_model as am
+import oracle.attention as oa
+import oracle.layout as ol
+from paged_kv_cache_43_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+BITS = {"f32": torch.int32, "f16": torch.int16, "bf16": torch.int16}
+
+
+def _pool(P, L, H, D, dtype, order=None):
+    from paged_kv_cache_43_amd import pf
+    st, h = pf.pf_pool_create(P, 16, L, H, D, dtype, order)
+    assert st == pf.PF_OK
+    nbytes = pf.pf_pool_bytes(h)
+    pool = torch.empty(nbytes // inputs.DTYPE_BYTES[dtype], dtype=BITS[dtype], device="cuda")
+    pf.check(pf.pf_pool_bind(h, pool, nbytes))
+    return h, pool
+
+
+@pytest.mark.parametrize("pinned", [False, True])
+def test_copy_pages_bit_exact(pinned):
+    """Random pool image, pairs as a batch grow reports them (plus pairs
+    outside the pool, which copy nothing); device or pinned host pairs."""
+    print("copy pages pinned=%s" % pinned, flush=True)
+    from paged_kv_cache_43_amd import pf, runner
+    P, L, H, D = 40, 3, 2, 64
+    g = ol.Geometry(P, 16, L, H, D, 2)
+    rng = np.random.default_rng(31)
+    image = rng.integers(0, 1 << 16, size=g.pool_elems(), dtype=np.uint32).astype(np.uint16)
+    h, pool = _pool(P, L, H, D, "f16")
+    pool.copy_(runner.bits_to_device(image))
+    pairs = np.array([[3, 17], [5, 9], [30, 0], [39, 38], [2, P], [-1, 4]], dtype=np.int32)
+    if pinned:
+        pt = torch.from_numpy(pairs).pin_memory()
+    else:
+        pt = torch.from_numpy(pairs).cuda()
+    pf.check(pf.pf_copy_pages(h, pt, len(pairs)))
+    torch.cuda.synchronize()
+    want = ol.copy_pages(image, g, [tuple(p) for p in pairs[:4]])
+    assert np.array_equal(runner.bits_from_device(pool), want)
+    pf.pf_pool_destroy(h)
+
+
+def _tables(h, ids, max_blocks):
+    from paged_kv_cache_43_amd import pf
+    st, bt, lens = pf.pf_block_tables(h, ids, max_blocks)
+    assert st == pf.PF_OK
+    return torch.from_numpy(bt).cuda(), torch.from_numpy(lens.astype(np.int32)).cuda(), bt, lens
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f16", 4, 4, 64), ("bf16", 14, 2, 64), ("f32", 2, 2, 16)])
+def test_beams_share_prompt_and_decode(dtype, hq, hkv, d):
+    print("beams", dtype, hq, hkv, d, flush=True)
+    from paged_kv_cache_43_amd import pf, runner
+    rng = np.random.default_rng(hq * 10 + d)
+    L, P, W, steps = 2, 200, 4, 18
+    prompts = [20, 32, 45]
+    order = rng.permutation(P).astype(np.int32)
+    h, pool = _pool(P, L, hkv, d, dtype, order)
+    pool.fill_(runner._signed_bits(inputs.NAN_BITS[dtype], dtype))
+    model = am.AllocModel(P, 16, order)
+    nseq = len(prompts) * W
+    hist_k = {}
+    hist_v = {}
+    # prompts: allocate, scatter every token of every layer, fork into beams
+    for p, n in enumerate(prompts):
+        s0 = p * W
+        assert pf.pf_alloc_for_seq(h, s0, n)[0] == pf.PF_OK and model.alloc(s0, n)[0] == am.OK
+        kb = inputs.normal_bits(rng, (L, n, hkv, d), dtype)
+        vb = inputs.normal_bits(rng, (L, n, hkv, d), dtype)
+        bt, _, _, _ = _tables(h, [s0], 4)
+        seq = torch.zeros(n, dtype=torch.int32, device="cuda")
+        pos = torch.arange(n, dtype=torch.int32, device="cuda")
+        for l in range(L):
+            pf.check(pf.pf_scatter_kv(h, l, runner.bits_to_device(kb[l]), runner.bits_to_device(vb[l]),
+                                      seq, pos, n, bt, 1, 4))
+        for b in range(1, W):
+            assert pf.pf_fork_seq(h, s0, s0 + b) == pf.PF_OK and model.fork(s0, s0 + b) == am.OK
+        for b in range(W):
+            hist_k[s0 + b] = [kb[l] for l in range(L)]
+            hist_v[s0 + b] = [vb[l] for l in range(L)]
+    assert pf.pf_free_pages(h) == model.free_pages() == P - sum(am.blocks_for(n, 16) for n in prompts)
+    ids = list(range(nseq))
+    mb = am.blocks_for(max(prompts) + steps, 16)
+    out = torch.empty((nseq, hq, d), dtype=torch.float32, device="cuda")
+    ws = None
+    n_copies_total = 0
+    keep = []       # pinned copy lists stay alive until the kernels that read them have run
+    for t in range(steps):
+        new = [model.lengths[s] + 1 for s in ids]
+        st, nn, copies = pf.pf_grow_seqs(h, ids, new)
+        mst, mnn, mcopies = model.grow_many(list(zip(ids, new)))
+        assert st == pf.PF_OK and mst == am.OK and list(nn) == mnn
+        assert [tuple(c) for c in copies] == mcopies
+        if len(copies):
+            n_copies_total += len(copies)
+            pairs = torch.from_numpy(np.ascontiguousarray(copies)).pin_memory()
+            keep.append(pairs)
+            pf.check(pf.pf_copy_pages(h, pairs, len(copies)))
+        bt, ctx, bt_h, lens_h = _tables(h, ids, mb)
+        rows, mlens = model.block_tables(ids, mb)
+        assert np.array_equal(bt_h, np.array(rows, dtype=np.int32)) and list(lens_h) == mlens
+        assert [pf.pf_page_refcount(h, p) for p in range(P)] == model.refs
+        nk = inputs.normal_bits(rng, (L, nseq, hkv, d), dtype)
+        nv = inputs.normal_bits(rng, (L, nseq, hkv, d), dtype)
+        seq = torch.arange(nseq, dtype=torch.int32, device="cuda")
+        pos = ctx - 1
+        for l in range(L):
+            pf.check(pf.pf_scatter_kv(h, l, runner.bits_to_device(nk[l]), runner.bits_to_device(nv[l]),
+                                      seq, pos, nseq, bt, nseq, mb))
+            for s in ids:
+                hist_k[s][l] = np.concatenate([hist_k[s][l], nk[l, s][None]])
+                hist_v[s][l] = np.concatenate([hist_v[s][l], nv[l, s][None]])
+        if t % 6 == 5 or t == steps - 1:
+            mc = int(max(new))
+            need = pf.pf_attention_workspace_bytes(h, nseq, hq, mc)
+            if ws is None or ws.numel() < need:
+                ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+            q = inputs.normal_bits(rng, (nseq, hq, d), dtype)
+            for l in range(L):
+                pf.check(pf.pf_paged_decode_attention(h, l, runner.bits_to_device(q), hq, bt, mb, ctx, nseq, mc,
+                                                      0.0, out, "f32", ws, ws.numel()))
+                torch.cuda.synchronize()
+                got = out.cpu().numpy().astype(np.float64)
+                qd = oa.decode_bits(q, dtype)
+                grp = hq // hkv
+                ref = np.zeros_like(got)
+                for s in ids:
+                    K = oa.decode_bits(hist_k[s][l], dtype)
+                    V = oa.decode_bits(hist_v[s][l], dtype)
+                    for hh in range(hq):
+                        ref[s, hh] = oa.attention(qd[s, hh], K[:, hh // grp], V[:, hh // grp], oa.default_scale(d))
+                gu.assert_close(got, ref, "f32", "beams step %d layer %d" % (t, l))
+    # three copies per partly filled prompt page (the last holder writes in place)
+    assert n_copies_total == 3 * sum(1 for n in prompts if n % 16)
+    # read-back of every beam equals its own history, bit for bit
+    ml = max(model.lengths.values())
+    for l in range(L):
+        kc = torch.empty((nseq, ml, hkv, d), dtype=BITS[dtype], device="cuda")
+        vc = torch.empty_like(kc)
+        pf.check(pf.pf_gather_kv(h, l, bt, ctx, nseq, mb, ml, kc, vc))
+        torch.cuda.synchronize()
+        kc, vc = runner.bits_from_device(kc), runner.bits_from_device(vc)
+        for s in ids:
+            n = model.lengths[s]
+            assert np.array_equal(kc[s, :n], hist_k[s][l]) and np.array_equal(vc[s, :n], hist_v[s][l])
+    for s in ids:
+        assert pf.pf_free_seq(h, s) == pf.PF_OK
+    assert pf.pf_free_pages(h) == P and all(pf.pf_page_refcount(h, p) == 0 for p in range(P))
+    pf.pf_pool_destroy(h)
