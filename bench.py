@@ -241,6 +241,117 @@ def run_twin(name, frames, reps):
     return res
 
 
+def run_cow(prompts, beam, reps, seed=43):
+    """Copy-on-write prefix sharing (PagedAttention blog, "Copy-on-Write for
+    Parallel Sampling") on the 13B-style head shape: ``prompts`` prompts with
+    lengths U[256, 2048], each forked into ``beam`` sequences that then decode
+    one token each.  Reports pages in use against private copies of every
+    prompt, the page-copy kernel of the first decode step against the HBM
+    roofline, and the attention partition kernel over the aliased tables
+    against the same contents in private pages (cache flushed before each)."""
+    import torch
+    from paged_kv_cache_43_amd import pf
+
+    L, H, D, B = 1, 40, 128, 16
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(256, 2049, size=prompts)
+    n = prompts * beam
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    bits = lambda shape: torch.randn(shape, generator=gen, device="cuda").half().view(torch.int16)
+    fl = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    pages_needed = int(sum(-(-int(x) // B) + 1 for x in lens)) * beam + 64
+    kp = [bits((int(x), H, D)) for x in lens]
+    vp = [bits((int(x), H, D)) for x in lens]
+
+    def make(shared):
+        st, h = pf.pf_pool_create(pages_needed, B, L, H, D, "f16", None)
+        pf.check(st)
+        nbytes = pf.pf_pool_bytes(h)
+        pool = torch.zeros(nbytes // 2, dtype=torch.int16, device="cuda")
+        pf.check(pf.pf_pool_bind(h, pool, nbytes))
+        for p in range(prompts):
+            owners = [p * beam] if shared else [p * beam + b for b in range(beam)]
+            for s in owners:
+                pf.check(pf.pf_alloc_for_seq(h, s, int(lens[p]))[0])
+                st, bt, _ = pf.pf_block_tables(h, [s], 128)
+                btd = torch.from_numpy(bt).cuda()
+                m = int(lens[p])
+                pf.check(pf.pf_scatter_kv(h, 0, kp[p], vp[p], torch.zeros(m, dtype=torch.int32, device="cuda"),
+                                          torch.arange(m, dtype=torch.int32, device="cuda"), m, btd, 1, 128))
+            if shared:
+                for b in range(1, beam):
+                    pf.check(pf.pf_fork_seq(h, p * beam, p * beam + b))
+        torch.cuda.synchronize()
+        return h, pool
+
+    hs, pool_s = make(True)
+    hp, pool_p = make(False)
+    res = {"workload": "%d prompts x beam %d, prompt lengths U[256,2048], 40 heads, d_head 128, fp16, block 16"
+                       % (prompts, beam),
+           "pages_in_use_shared": pages_needed - pf.pf_free_pages(hs),
+           "pages_in_use_private": pages_needed - pf.pf_free_pages(hp)}
+    res["memory_saved_fraction"] = round(1 - res["pages_in_use_shared"] / res["pages_in_use_private"], 4)
+    ids = np.arange(n, dtype=np.uint64)
+    new = np.repeat(lens, beam).astype(np.int32) + 1
+    st, nn, copies = pf.pf_grow_seqs(hs, ids, new)
+    pf.check(st)
+    pf.check(pf.pf_alloc_for_seqs(hp, ids, new)[0])
+    res["first_step_copies"] = int(len(copies))
+    page_bytes = pf.pf_page_bytes(hs)
+    pairs = torch.from_numpy(np.ascontiguousarray(copies)).cuda()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps + 3)]
+    torch.cuda.synchronize()
+    for a, b in ev:       # the copies are idempotent: re-running them times the kernel
+        fl.amax()
+        a.record()
+        pf.check(pf.pf_copy_pages(hs, pairs, len(copies)))
+        b.record()
+    torch.cuda.synchronize()
+    t_copy = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev[3:]]))
+    copy_bytes = 2 * page_bytes * len(copies)
+    res["copy_kernel_us"] = round(t_copy, 2)
+    res["copy_bytes"] = int(copy_bytes)
+    res["copy_GBps"] = round(copy_bytes / t_copy / 1e3, 1)
+    res["copy_frac_of_hbm_peak"] = round(copy_bytes / t_copy / 1e3 / HBM_PEAK_GBS, 4)
+    # attention over aliased vs private tables, same logical K/V
+    mc = int(new.max())
+    mb = -(-mc // B)
+    q = bits((n, H, D))
+    out = torch.empty((n, H, D), dtype=torch.int16, device="cuda")
+    setup = {}
+    for tag, h in (("shared", hs), ("private", hp)):
+        st, bt, ln = pf.pf_block_tables(h, ids, mb)
+        pf.check(st)
+        need = pf.pf_attention_workspace_bytes(h, n, H, mc)
+        setup[tag] = (h, torch.from_numpy(bt).cuda(), torch.from_numpy(ln.astype(np.int32)).cuda(),
+                      torch.empty(max(need, 1), dtype=torch.uint8, device="cuda"), need)
+    order = [t for _ in range(reps + 3) for t in ("shared", "private")]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in order]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for (a, b), tag in zip(ev, order):
+        h, bt, ctx, ws, need = setup[tag]
+        fl.amax()
+        pf.check(pf.pf_pool_set_timing_events(h, a.cuda_event, b.cuda_event))
+        pf.check(pf.pf_paged_decode_attention(h, 0, q, H, bt, mb, ctx, n, mc, 0.0, out, "f16", ws, need))
+        pf.check(pf.pf_pool_set_timing_events(h, None, None))
+    torch.cuda.synchronize()
+    alg = alg_bytes_attention(new, type("W", (), dict(n=n, hq=H, hkv=H, d=D, es=2))(), 2)
+    for tag in ("shared", "private"):
+        t = float(np.median([a.elapsed_time(b) * 1e3 for i, ((a, b), x) in enumerate(zip(ev, order))
+                             if x == tag and i >= 6]))
+        res["attn_%s_us" % tag] = round(t, 2)
+        res["attn_%s_alg_GBps" % tag] = round(alg / t / 1e3, 1)
+    res["attn_private_over_shared"] = round(res["attn_private_us"] / res["attn_shared_us"], 4)
+    res["attn_alg_bytes"] = int(alg)
+    for h in (hs, hp):
+        pf.pf_pool_destroy(h)
+    return res
+
+
 def cpu_baseline(name, budget_s):
     """The CPU fp64 oracle (contiguous two-pass softmax attention on decoded
     K/V) on the same workload, single thread: whole passes over every
@@ -308,6 +419,8 @@ def main():
     ap.add_argument("--twin", default="13b,gqa",
                     help="comma list of configs for the paged vs contiguous-cache comparison (shuffled frames)")
     ap.add_argument("--twin-reps", type=int, default=20)
+    ap.add_argument("--cow", choices=["on", "off"], default="on",
+                    help="copy-on-write prefix sharing leg (16 prompts x beam 4, 13B-style heads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -387,6 +500,8 @@ def main():
         twin[name] = run_twin(name, "shuffled", args.twin_reps)
     if twin:
         line["paged_vs_contiguous"] = twin
+    if args.cow == "on":
+        line["cow_prefix_sharing"] = run_cow(16, 4, 20)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(line), flush=True)
