@@ -16,12 +16,14 @@ Modules, and the passages each one follows:
   "Architecture": allocate a new block only when the last one is full), with
   copy-on-write sharing: reference counts, fork, and a grow that copies a
   shared block before writing into it (PagedAttention blog, "Copy-on-Write
-  for Parallel Sampling").
+  for Parallel Sampling"), and swapping whole sequences to a host backing
+  store and back (PagedAttention blog, "Preemption and Swapping").
 * ``layout``       -- the pool image: element address of a token's K/V inside
   a page, the scatter of new tokens, and the read-back (gather) of a
   sequence's pages into contiguous K/V (PageFault, "The OS analogy": the
   page-table walk; PageForge, "Four layers": K and V combined in one pool),
-  and the whole-page copies of copy-on-write.
+  the whole-page copies of copy-on-write and the page <-> host-slot copies of
+  swapping.
 * ``attention``    -- the plain definition softmax(q.K^T.scale).V on contiguous
   read-back K/V, two-pass, no splitting (PagedAttention blog, "The Attention
   Kernel"; PageFault, "Four stages", stage 1 and 3), plus a pure-Python brute

@@ -46,6 +46,22 @@ where the blog is silent:
   know about sharing can never overwrite another sequence's tokens.
 * The last holder of a page frees it; pages are pushed in the order the
   freeing sequence's table lists them, last first, skipping pages still held.
+
+Swapping (PagedAttention blog, "Preemption and Swapping": a sequence's blocks
+are evicted to CPU memory and copied back when it resumes, block by block).
+Readings where the blog is silent:
+
+* The backing store is a set of page-sized host slots with its own LIFO
+  stack (slot 0 first), like the device pool.
+* A whole sequence is swapped: every page of its table goes to a slot, in
+  table order, and the sequence drops its hold on the device pages (a page
+  another table still holds stays where it is; the swapped copy is private).
+  Its device pages go back to the stack as a free would push them.
+* Swapping in takes pages from the device stack in table order, copies the
+  slots back and returns the slots to their stack last first, as a free does.
+* Both are all or nothing over a batch of sequences (not enough slots, or
+  not enough device pages); a swapped sequence cannot grow, fork or be
+  exported (SWAPPED) until it is swapped in; freeing it releases its slots.
 """
 
 OK = "ok"
@@ -53,6 +69,7 @@ OOM = "oom"
 UNKNOWN_SEQ = "unknown_seq"
 INVALID = "invalid"
 SHARED = "shared"
+SWAPPED = "swapped"
 
 
 def blocks_for(length, block_size):
@@ -76,6 +93,9 @@ class AllocModel:
         self.tables = {}
         self.lengths = {}
         self.refs = [0] * num_pages
+        self.slot_stack = []          # host swap slots, top at the end
+        self.num_slots = 0
+        self.swapped = {}             # seq id -> host slots, in table order
 
     # -- operations -----------------------------------------------------------
     def _writes_shared(self, seq_id, new_len):
@@ -90,6 +110,8 @@ class AllocModel:
         """Grow ``seq_id`` to ``new_len`` tokens.  Returns (status, n_new_pages)."""
         if new_len < 0:
             return INVALID, 0
+        if seq_id in self.swapped:
+            return SWAPPED, 0
         table = self.tables.get(seq_id, [])
         current = self.lengths.get(seq_id, 0)
         if new_len < current:
@@ -109,9 +131,11 @@ class AllocModel:
     def fork(self, parent, child):
         """``child`` starts as a copy of ``parent``'s table and length, sharing
         every page.  Returns a status."""
+        if parent in self.swapped:
+            return SWAPPED
         if parent not in self.tables:
             return UNKNOWN_SEQ
-        if child in self.tables:
+        if child in self.tables or child in self.swapped:
             return INVALID
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
@@ -125,6 +149,8 @@ class AllocModel:
         every page taken from the stack, the copy's destination included."""
         if new_len < 0:
             return INVALID, 0, None
+        if seq_id in self.swapped:
+            return SWAPPED, 0, None
         table = self.tables.get(seq_id, [])
         current = self.lengths.get(seq_id, 0)
         if new_len < current:
@@ -162,6 +188,8 @@ class AllocModel:
             if new_len < 0 or new_len < lens.get(seq_id, 0):
                 return INVALID, [0] * len(entries), []
             lens[seq_id] = new_len
+        if any(seq_id in self.swapped for seq_id, _ in entries):
+            return SWAPPED, [0] * len(entries), []
         saved = (self.stack[:], {k: v[:] for k, v in self.tables.items()}, dict(self.lengths), self.refs[:])
         counts, copies = [], []
         for seq_id, new_len in entries:
@@ -177,15 +205,77 @@ class AllocModel:
     def free(self, seq_id):
         """Drop ``seq_id``'s hold on its pages, returning those no other table
         holds to the pool, and forget the sequence."""
+        if seq_id in self.swapped:
+            for slot in reversed(self.swapped.pop(seq_id)):
+                self.slot_stack.append(slot)
+            del self.lengths[seq_id]
+            return OK
         if seq_id not in self.tables:
             return UNKNOWN_SEQ
-        for page in reversed(self.tables[seq_id]):
-            self.refs[page] -= 1
-            if self.refs[page] == 0:
-                self.stack.append(page)
+        self._release(self.tables[seq_id])
         del self.tables[seq_id]
         del self.lengths[seq_id]
         return OK
+
+    def _release(self, table):
+        for page in reversed(table):
+            self.refs[page] -= 1
+            if self.refs[page] == 0:
+                self.stack.append(page)
+
+    # -- swapping --------------------------------------------------------------
+    def set_swap_space(self, num_slots):
+        """A fresh backing store of ``num_slots`` host slots (slot 0 first)."""
+        self.num_slots = num_slots
+        self.slot_stack = list(reversed(range(num_slots)))
+
+    def swap_out(self, seq_ids):
+        """Evict whole sequences.  Returns (status, [(page, slot), ...]) with
+        the copies to make, device to host, in order."""
+        if len(set(seq_ids)) != len(seq_ids):
+            return INVALID, []
+        for s in seq_ids:
+            if s in self.swapped:
+                return SWAPPED, []
+            if s not in self.tables:
+                return UNKNOWN_SEQ, []
+        if sum(len(self.tables[s]) for s in seq_ids) > len(self.slot_stack):
+            return OOM, []
+        copies = []
+        for s in seq_ids:
+            slots = []
+            for page in self.tables[s]:
+                slot = self.slot_stack.pop()
+                slots.append(slot)
+                copies.append((page, slot))
+            self._release(self.tables[s])
+            del self.tables[s]
+            self.swapped[s] = slots
+        return OK, copies
+
+    def swap_in(self, seq_ids):
+        """Bring whole sequences back.  Returns (status, [(slot, page), ...])
+        with the copies to make, host to device, in order."""
+        if len(set(seq_ids)) != len(seq_ids):
+            return INVALID, []
+        for s in seq_ids:
+            if s not in self.swapped:
+                return (INVALID if s in self.tables else UNKNOWN_SEQ), []
+        if sum(len(self.swapped[s]) for s in seq_ids) > len(self.stack):
+            return OOM, []
+        copies = []
+        for s in seq_ids:
+            slots = self.swapped.pop(s)
+            table = []
+            for slot in slots:
+                page = self.stack.pop()
+                self.refs[page] = 1
+                table.append(page)
+                copies.append((slot, page))
+            for slot in reversed(slots):
+                self.slot_stack.append(slot)
+            self.tables[s] = table
+        return OK, copies
 
     # -- queries --------------------------------------------------------------
     def free_pages(self):
@@ -229,6 +319,12 @@ class AllocModel:
         assert not live & set(self.stack), "a live page is also on the free list"
         assert len(self.stack) + len(live) == self.num_pages, "pages leaked or duplicated"
         assert len(set(self.stack)) == len(self.stack), "page pushed twice"
+        held = [slot for slots in self.swapped.values() for slot in slots]
+        assert len(held) == len(set(held)), "a host slot held twice"
+        assert not set(held) & set(self.slot_stack), "a held slot is also free"
+        assert len(held) + len(self.slot_stack) == self.num_slots, "host slots leaked"
+        for s, slots in self.swapped.items():
+            assert s not in self.tables and len(slots) == blocks_for(self.lengths[s], self.block_size)
 
 
 def replay(num_pages, block_size, initial_free_order, ops):

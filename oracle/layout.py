@@ -101,6 +101,23 @@ def copy_pages(pool, g, pairs):
     return out
 
 
+def swap_copy(pool, host, g, pairs, to_host):
+    """Swap copies (PagedAttention blog, "Preemption and Swapping": blocks go
+    to CPU memory and come back).  ``host`` is the backing store image, one
+    page-sized slot after another, each slot laid out like a page.  With
+    ``to_host`` each (page, slot) pair copies the whole page into the slot;
+    otherwise each (slot, page) pair copies the slot into the page.  Returns
+    new (pool, host) images."""
+    pool, host = pool.copy(), host.copy()
+    n = g.page_elems()
+    for a, b in pairs:
+        if to_host:
+            host[b * n:(b + 1) * n] = pool[a * n:(a + 1) * n]
+        else:
+            pool[b * n:(b + 1) * n] = host[a * n:(a + 1) * n]
+    return pool, host
+
+
 def readback(pool, g, layer, table, length):
     """Gather one sequence's K and V into contiguous ``[length][H][D]`` bit arrays."""
     kc = np.empty((length, g.H, g.D), dtype=pool.dtype)

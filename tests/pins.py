@@ -306,6 +306,142 @@ def pin_cow_random_ops_invariants(o):
     m.check_invariants()
 
 
+def _image_with(o, g, m, seqs, rng, pool=None):
+    """Scatter random K/V for every token of ``seqs`` (all layers); returns the
+    pool image and each sequence's history per layer."""
+    L = o.layout
+    pool = L.empty_pool(g, 0x7E00) if pool is None else pool
+    hist = {}
+    for s in seqs:
+        n = m.seq_len(s)
+        hist[s] = []
+        for layer in range(g.L):
+            k = rng.integers(0, 1 << 15, size=(n, g.H, g.D), dtype=np.uint16)
+            pool = L.scatter(pool, g, layer, k, k ^ 0x2222, [0] * n, list(range(n)), {0: m.table(s)})
+            hist[s].append(k)
+    return pool, hist
+
+
+def _reads_back(o, g, pool, m, s, hist):
+    for layer in range(g.L):
+        kc, vc = o.layout.readback(pool, g, layer, m.table(s), m.seq_len(s))
+        if not (np.array_equal(kc, hist[layer]) and np.array_equal(vc, hist[layer] ^ 0x2222)):
+            return False
+    return True
+
+
+def pin_swap_round_trip(o):
+    """A sequence swapped out, its pages reused and overwritten by another
+    sequence, then swapped back into different pages, reads back exactly."""
+    am, L = o.alloc_model, o.layout
+    rng = _rng(41)
+    g = L.Geometry(10, 16, 2, 2, 4, 2)
+    m = am.AllocModel(10, 16, rng.permutation(10))
+    m.set_swap_space(6)
+    host = np.zeros(6 * g.page_elems(), dtype=np.uint16)
+    m.alloc(0, 37)
+    m.alloc(1, 20)
+    pool, hist = _image_with(o, g, m, [0, 1], rng)
+    pages0 = m.table(0)
+    st, copies = m.swap_out([0])
+    assert st == am.OK and [c[0] for c in copies] == pages0 and [c[1] for c in copies] == [0, 1, 2]
+    pool, host = L.swap_copy(pool, host, g, copies, True)
+    assert m.free_pages() == 10 - 2 and 0 not in m.tables and m.seq_len(0) == 37
+    m.check_invariants()
+    m.alloc(2, 48)                                     # takes seq 0's old pages and overwrites them
+    assert sorted(m.table(2)) == sorted(pages0)
+    pool, hist2 = _image_with(o, g, m, [2], rng, pool)
+    m.free(2)
+    m.alloc(3, 17)                                     # two pages held elsewhere meanwhile
+    st, back = m.swap_in([0])
+    assert st == am.OK and [c[0] for c in back] == [0, 1, 2] and [c[1] for c in back] == m.table(0)
+    assert m.free_pages() == 10 - 2 - 2 - 3 and len(m.slot_stack) == 6
+    pool, host = L.swap_copy(pool, host, g, back, False)
+    assert _reads_back(o, g, pool, m, 0, hist[0]) and _reads_back(o, g, pool, m, 1, hist[1])
+    m.check_invariants()
+
+
+def pin_swap_rules(o):
+    """All or nothing on slots and on device pages; a swapped sequence cannot
+    grow, fork or swap out again; freeing it returns its slots."""
+    am = o.alloc_model
+    m = am.AllocModel(8, 16)
+    m.set_swap_space(4)
+    m.alloc(0, 40)                                     # 3 pages
+    m.alloc(1, 30)                                     # 2 pages
+    assert m.swap_out([0, 1]) == (am.OOM, []) and len(m.slot_stack) == 4 and m.free_pages() == 3
+    assert m.swap_out([0, 0]) == (am.INVALID, [])
+    assert m.swap_out([7]) == (am.UNKNOWN_SEQ, [])
+    assert m.swap_out([0])[0] == am.OK and m.free_pages() == 6
+    assert m.swap_out([0]) == (am.SWAPPED, [])
+    assert m.alloc(0, 41) == (am.SWAPPED, 0) and m.grow(0, 41)[0] == am.SWAPPED
+    assert m.fork(0, 5) == am.SWAPPED and m.grow_many([(1, 31), (0, 50)])[0] == am.SWAPPED
+    assert m.swap_in([1]) == (am.INVALID, [])
+    m.alloc(2, 16 * 5)                                 # 5 of 6 free pages
+    assert m.swap_in([0]) == (am.OOM, []) and 0 in m.swapped and len(m.slot_stack) == 1
+    m.check_invariants()
+    assert m.free(0) == am.OK and len(m.slot_stack) == 4 and 0 not in m.lengths
+    m.check_invariants()
+
+
+def pin_swap_shared_prefix(o):
+    """Swapping out one beam keeps the pages its siblings still hold; the
+    beam comes back into private pages with its own history."""
+    am, L = o.alloc_model, o.layout
+    rng = _rng(42)
+    g = L.Geometry(12, 16, 1, 2, 4, 2)
+    m = am.AllocModel(12, 16, rng.permutation(12))
+    m.set_swap_space(4)
+    host = np.zeros(4 * g.page_elems(), dtype=np.uint16)
+    m.alloc(0, 40)
+    pool, hist = _image_with(o, g, m, [0], rng)
+    m.fork(0, 1)
+    shared = m.table(0)
+    st, copies = m.swap_out([1])
+    assert st == am.OK and [c[0] for c in copies] == shared
+    assert all(m.refcount(p) == 1 for p in shared) and m.free_pages() == 12 - 3
+    pool, host = L.swap_copy(pool, host, g, copies, True)
+    st, back = m.swap_in([1])
+    pool, host = L.swap_copy(pool, host, g, back, False)
+    assert not set(m.table(1)) & set(shared)
+    assert _reads_back(o, g, pool, m, 0, hist[0]) and _reads_back(o, g, pool, m, 1, hist[0])
+    m.check_invariants()
+
+
+def pin_swap_random_ops_invariants(o):
+    """Random alloc / fork / grow / swap out / swap in / free keep every count
+    consistent and lose no page or slot."""
+    am = o.alloc_model
+    rng = _rng(43)
+    m = am.AllocModel(80, 16, rng.permutation(80))
+    m.set_swap_space(40)
+    nxt = 0
+    for step in range(1200):
+        live = sorted(m.tables)
+        out = sorted(m.swapped)
+        r = rng.random()
+        if not live or r < 0.15:
+            m.alloc(nxt, int(rng.integers(1, 50)))
+            nxt += 1
+        elif r < 0.25:
+            m.fork(int(rng.choice(live)), nxt)
+            nxt += 1
+        elif r < 0.5:
+            s = int(rng.choice(live))
+            m.grow(s, m.seq_len(s) + int(rng.integers(0, 20)))
+        elif r < 0.65:
+            m.swap_out([int(x) for x in rng.choice(live, size=min(len(live), int(rng.integers(1, 3))), replace=False)])
+        elif r < 0.8 and out:
+            m.swap_in([int(x) for x in rng.choice(out, size=min(len(out), int(rng.integers(1, 3))), replace=False)])
+        else:
+            m.free(int(rng.choice(live + out)))
+        m.check_invariants()
+    for s in sorted(m.tables) + sorted(m.swapped):
+        m.free(s)
+    assert m.free_pages() == 80 and len(m.slot_stack) == 40
+    m.check_invariants()
+
+
 # ----------------------------------------------------------------------------
 # O2 / O3 layout
 # ----------------------------------------------------------------------------

@@ -85,6 +85,7 @@ def _gqa_interleaved(q_bits, pool, g, layer, tables, lengths, dtype, scale=None)
 
 _orig_attention = oracle.attention.attention
 _orig_readback = oracle.layout.readback
+_orig_swap_copy = oracle.layout.swap_copy
 
 
 class _FifoModel(oracle.alloc_model.AllocModel):
@@ -166,6 +167,33 @@ def _copy_nothing(pool, g, pairs):
     return pool.copy()
 
 
+class _SwapKeepsPagesModel(oracle.alloc_model.AllocModel):
+    def _release(self, table):
+        if getattr(self, "_in_swap", False):
+            return                                              # device pages never released
+        super()._release(table)
+
+    def swap_out(self, seq_ids):
+        self._in_swap = True
+        try:
+            return super().swap_out(seq_ids)
+        finally:
+            self._in_swap = False
+
+
+class _SwapInKeepsSlotsModel(oracle.alloc_model.AllocModel):
+    def swap_in(self, seq_ids):
+        before = list(self.slot_stack)
+        st, copies = super().swap_in(seq_ids)
+        if st == oracle.alloc_model.OK:
+            self.slot_stack = before                            # slots never returned
+        return st, copies
+
+
+def _swap_copy_off_by_one_page(pool, host, g, pairs, to_host):
+    return _orig_swap_copy(pool, host, g, [(a, b + 1 if b + 1 < g.P else b) for a, b in pairs], to_host)
+
+
 MUTANTS = {
     "attention_without_scale": (oracle.attention, "attention", _no_scale),
     "attention_wrong_sign": (oracle.attention, "attention", _wrong_sign),
@@ -185,6 +213,9 @@ MUTANTS = {
     "fork_without_refcounts": (oracle.alloc_model, "AllocModel", _ForkWithoutRefsModel),
     "grow_writes_shared_page": (oracle.alloc_model, "AllocModel", _GrowInPlaceModel),
     "copy_pages_copies_nothing": (oracle.layout, "copy_pages", _copy_nothing),
+    "swap_out_keeps_device_pages": (oracle.alloc_model, "AllocModel", _SwapKeepsPagesModel),
+    "swap_in_keeps_slots": (oracle.alloc_model, "AllocModel", _SwapInKeepsSlotsModel),
+    "swap_copy_wrong_page": (oracle.layout, "swap_copy", _swap_copy_off_by_one_page),
 }
 
 
