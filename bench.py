@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+HOST_LINK_GBS = 64.0   # PCIe 5.0 x16 host link, per direction, nominal
 
 WORKLOADS = {
     "tiny": "Tiny: 4 seqs, 1 layer, 2 heads, d_head 16, fp32, block 16, pool 64 pages, context U[1,64], {frames} frames",
@@ -352,6 +353,75 @@ def run_cow(prompts, beam, reps, seed=43):
     return res
 
 
+def run_swap(n_seqs, reps, seed=44):
+    """Swapping (PagedAttention blog, "Preemption and Swapping") on the
+    13B-style head shape: ``n_seqs`` sequences with lengths U[256, 2048] are
+    swapped out to a pinned host store and back in, ``reps`` times.  Reports
+    the swap kernel's host-link bandwidth each way beside a DMA-engine copy of
+    the same number of contiguous bytes (torch ``copy_`` between pinned and
+    device memory), the achievable ceiling of the link."""
+    import torch
+    from paged_kv_cache_43_amd import pf
+
+    L, H, D, B = 1, 40, 128, 16
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(256, 2049, size=n_seqs)
+    pages = int(sum(-(-int(x) // B) for x in lens))
+    P = 2 * pages + 64
+    st, h = pf.pf_pool_create(P, B, L, H, D, "f16", rng.permutation(P).astype(np.int32))
+    pf.check(st)
+    nb = pf.pf_pool_bytes(h)
+    pool = torch.zeros(nb // 2, dtype=torch.int16, device="cuda")
+    pf.check(pf.pf_pool_bind(h, pool, nb))
+    pb = pf.pf_page_bytes(h)
+    host = torch.zeros(pages * pb // 2, dtype=torch.int16).pin_memory()
+    pf.check(pf.pf_swap_bind(h, host, pages * pb, pages))
+    ids = np.arange(n_seqs, dtype=np.uint64)
+    pf.check(pf.pf_alloc_for_seqs(h, ids, lens.astype(np.int32))[0])
+    staging = torch.zeros(2 * pages, dtype=torch.int32).pin_memory()
+    nbytes = pages * pb
+    t_out, t_in = [], []
+    for r in range(reps + 2):
+        for to_host, acc in ((True, t_out), (False, t_in)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            fn = pf.pf_swap_out if to_host else pf.pf_swap_in
+            pf.check(fn(h, ids, staging, 2 * pages))
+            b.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                acc.append(a.elapsed_time(b) * 1e3)
+    dev = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+    dma_out, dma_in = [], []
+    for r in range(reps + 2):
+        for d2h, acc in ((True, dma_out), (False, dma_in)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            if d2h:
+                host.copy_(dev, non_blocking=True)
+            else:
+                dev.copy_(host, non_blocking=True)
+            b.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                acc.append(a.elapsed_time(b) * 1e3)
+    pf.pf_pool_destroy(h)
+    med = lambda x: float(np.median(x))
+    res = {"workload": "%d sequences, lengths U[256,2048], 40 heads, d_head 128, fp16, block 16: %d pages of %d KiB"
+                       % (n_seqs, pages, pb // 1024),
+           "bytes_each_way": int(nbytes),
+           "swap_out_us": round(med(t_out), 1), "swap_in_us": round(med(t_in), 1),
+           "swap_out_GBps": round(nbytes / med(t_out) / 1e3, 1), "swap_in_GBps": round(nbytes / med(t_in) / 1e3, 1),
+           "dma_copy_d2h_GBps": round(nbytes / med(dma_out) / 1e3, 1),
+           "dma_copy_h2d_GBps": round(nbytes / med(dma_in) / 1e3, 1),
+           "host_link_peak_GBps_each_way": HOST_LINK_GBS, "median_of": reps}
+    res["swap_out_frac_of_link_peak"] = round(res["swap_out_GBps"] / HOST_LINK_GBS, 4)
+    res["swap_in_frac_of_link_peak"] = round(res["swap_in_GBps"] / HOST_LINK_GBS, 4)
+    return res
+
+
 def cpu_baseline(name, budget_s):
     """The CPU fp64 oracle (contiguous two-pass softmax attention on decoded
     K/V) on the same workload, single thread: whole passes over every
@@ -419,6 +489,8 @@ def main():
     ap.add_argument("--twin", default="13b,gqa",
                     help="comma list of configs for the paged vs contiguous-cache comparison (shuffled frames)")
     ap.add_argument("--twin-reps", type=int, default=20)
+    ap.add_argument("--swap", choices=["on", "off"], default="on",
+                    help="swap out/in leg (16 sequences, 13B-style heads)")
     ap.add_argument("--cow", choices=["on", "off"], default="on",
                     help="copy-on-write prefix sharing leg (16 prompts x beam 4, 13B-style heads)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -502,6 +574,8 @@ def main():
         line["paged_vs_contiguous"] = twin
     if args.cow == "on":
         line["cow_prefix_sharing"] = run_cow(16, 4, 20)
+    if args.swap == "on":
+        line["swap"] = run_swap(16, 10)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(line), flush=True)

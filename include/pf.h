@@ -55,7 +55,8 @@ typedef enum {
   PF_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
   PF_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
   PF_ERR_UNSUPPORTED = -7,  /* valid but not built: block size / head dim */
-  PF_ERR_SHARED = -8        /* growth would write into a page another table shares */
+  PF_ERR_SHARED = -8,       /* growth would write into a page another table shares */
+  PF_ERR_SWAPPED = -9       /* the sequence is swapped out (pf_swap_out) */
 } pf_status;
 
 typedef struct {
@@ -146,6 +147,53 @@ int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens
  * or a NULL handle. */
 int32_t pf_page_refcount(const pf_pool* pool, int32_t page);
 
+/* Swapping (PagedAttention blog, "Preemption and Swapping": a sequence's blocks
+ * are evicted to CPU memory and copied back when it resumes).
+ *
+ * Bind a host backing store: host_ptr is caller-owned pinned memory
+ * (hipHostMalloc / pin_memory), 16-byte aligned, of at least
+ * num_slots * pf_page_bytes bytes; slot k is bytes [k, k+1) * pf_page_bytes,
+ * laid out like a page.  Slots are handed out from a LIFO stack, slot 0 first.
+ * Re-binding resets the stack and is refused (PF_ERR_INVALID) while any
+ * sequence is swapped out. */
+int pf_swap_bind(pf_pool* pool, void* host_ptr, size_t bytes, int32_t num_slots);
+
+/* Free host slots (-1 for a NULL handle). */
+int32_t pf_swap_free_slots(const pf_pool* pool);
+
+/* *swapped = 1 if seq_id is swapped out, else 0.  Errors: PF_ERR_UNKNOWN_SEQ. */
+int pf_seq_swapped(const pf_pool* pool, uint64_t seq_id, int32_t* swapped);
+
+/* Swap whole sequences out: each page of each sequence's table, in order, is
+ * assigned a host slot and enqueued on the stream for copying device -> host;
+ * the sequence then drops its hold on those pages (pages no other table holds
+ * return to the free stack, last first, as pf_free_seq would push them; pages
+ * still shared stay with their other holders).  The sequence keeps its length
+ * and is "swapped": growing, forking or exporting it fails with
+ * PF_ERR_SWAPPED until pf_swap_in; pf_free_seq releases its slots.
+ *   staging_host  caller-owned pinned memory, 8-byte aligned, of
+ *                 staging_words int32 >= 2 * (pages of the sequences); receives
+ *                 the (page, slot) pairs that the copy kernel reads when it
+ *                 runs (keep it unchanged until the stream has passed the call).
+ * The copy is enqueued before the call returns, so anything enqueued later on
+ * the same stream (writes into the freed pages included) runs after it.
+ * All or nothing over the batch.  Errors: PF_ERR_INVALID (a repeated id, a
+ * small staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_SWAPPED (already out),
+ * PF_ERR_OOM (not enough free slots), PF_ERR_UNBOUND (no device pool or no
+ * swap space), PF_ERR_HIP. */
+int pf_swap_out(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
+                int64_t staging_words, void* hip_stream);
+
+/* Swap whole sequences back in: each host slot, in table order, gets a fresh
+ * page from the free stack (pop order) and is enqueued for copying host ->
+ * device; the slots return to their stack, last first.  Staging and ordering
+ * as pf_swap_out, with (slot, page) pairs.  All or nothing.  Errors:
+ * PF_ERR_INVALID (a repeated id, a sequence that is not swapped out, a small
+ * staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_OOM (not enough free pages),
+ * PF_ERR_UNBOUND, PF_ERR_HIP. */
+int pf_swap_in(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
+               int64_t staging_words, void* hip_stream);
+
 /* Release seq_id's hold on each of its pages and forget the sequence; pages no
  * other table holds go back on the free stack, last page first (so the
  * sequence's first page ends on top).
@@ -155,7 +203,7 @@ int pf_free_seq(pf_pool* pool, uint64_t seq_id);
 /* Pages currently on the free stack (-1 for a NULL handle). */
 int32_t pf_free_pages(const pf_pool* pool);
 
-/* Number of live sequences (-1 for a NULL handle). */
+/* Number of live sequences, resident or swapped out (-1 for a NULL handle). */
 int32_t pf_num_seqs(const pf_pool* pool);
 
 /* Current length of seq_id.  Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID. */
@@ -164,7 +212,7 @@ int pf_seq_len(const pf_pool* pool, uint64_t seq_id, int32_t* len);
 /* Export dense host tables for n sequences: bt_host is [n][max_blocks] int32,
  * row i = the block table of seq_ids[i] padded with -1; lens_host (nullable)
  * is [n] int32 lengths.  Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID (a table
- * longer than max_blocks, null pointers with n > 0). */
+ * longer than max_blocks, null pointers with n > 0), PF_ERR_SWAPPED. */
 int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
                     int32_t* bt_host, int32_t* lens_host);
 

@@ -19,6 +19,12 @@
 // last page can be written: tokens are appended) either copies it first
 // (pf_grow_seqs, which reports the copy for pf_copy_pages) or is refused
 // (pf_alloc_for_seq / pf_alloc_for_seqs, PF_ERR_SHARED).
+//
+// Swapping (PagedAttention blog, "Preemption and Swapping"): whole sequences
+// move to page-sized slots of a caller-owned pinned host store and back; the
+// state changes here, the copies are enqueued by pf_swap_out / pf_swap_in
+// (pf_kv.hip) in the same call.  A swapped sequence keeps its length and its
+// slots; it cannot grow, fork or be exported until it is swapped in.
 #include <cstring>
 #include <limits>
 #include <new>
@@ -119,6 +125,7 @@ int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n
   if (!pool || new_len < 0) return PF_ERR_INVALID;
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(seq_id);
+  if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
   const int32_t cur_len = it == pool->seqs.end() ? 0 : it->second.len;
   const size_t have = it == pool->seqs.end() ? 0 : it->second.pages.size();
   if (new_len < cur_len) return PF_ERR_INVALID;
@@ -164,6 +171,10 @@ int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new
     if (new_lens[i] < cur_len) return PF_ERR_INVALID;
     pending[seq_ids[i]] = {new_lens[i], 0, true};
   }
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seq_ids[i]);
+    if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
+  }
   pending.clear();
   size_t total = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -199,6 +210,8 @@ int pf_free_seq(pf_pool* pool, uint64_t seq_id) {
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(seq_id);
   if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+  const std::vector<int32_t>& slots = it->second.slots;
+  for (size_t i = slots.size(); i-- > 0;) pool->slot_stack.push_back(slots[i]);
   const std::vector<int32_t>& pages = it->second.pages;
   for (size_t i = pages.size(); i-- > 0;)
     if (--pool->refs[(size_t)pages[i]] == 0) pool->stack.push_back(pages[i]);
@@ -210,6 +223,7 @@ int pf_fork_seq(pf_pool* pool, uint64_t parent, uint64_t child) {
   if (!pool) return PF_ERR_INVALID;
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(parent);
+  if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
   if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
   if (pool->seqs.count(child)) return PF_ERR_INVALID;
   pf_seq_entry copy = it->second;
@@ -246,6 +260,10 @@ int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens
     }
     if (new_lens[i] < cur_len) return PF_ERR_INVALID;
     lens[seq_ids[i]] = new_lens[i];
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seq_ids[i]);
+    if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
   }
   std::unordered_map<uint64_t, Pending> pending;
   std::unordered_map<int32_t, int32_t> dref;  // reference count changes of the batch
@@ -298,6 +316,37 @@ int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens
   return PF_OK;
 }
 
+int pf_swap_bind(pf_pool* pool, void* host_ptr, size_t bytes, int32_t num_slots) {
+  if (!pool || num_slots < 0 || (num_slots > 0 && !host_ptr)) return PF_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(host_ptr) % 16 != 0) return PF_ERR_INVALID;
+  size_t need = 0;
+  if (!mul_ok(pool->page_elems * pool->elem_bytes, (size_t)num_slots, &need) || bytes < need)
+    return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  for (const auto& kv : pool->seqs)
+    if (kv.second.swapped) return PF_ERR_INVALID;  // slots in use
+  pool->host = num_slots > 0 ? host_ptr : nullptr;
+  pool->num_slots = num_slots;
+  pool->slot_stack.resize((size_t)num_slots);
+  for (int32_t i = 0; i < num_slots; ++i) pool->slot_stack[(size_t)(num_slots - 1 - i)] = i;
+  return PF_OK;
+}
+
+int32_t pf_swap_free_slots(const pf_pool* pool) {
+  if (!pool) return -1;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  return (int32_t)pool->slot_stack.size();
+}
+
+int pf_seq_swapped(const pf_pool* pool, uint64_t seq_id, int32_t* swapped) {
+  if (!pool || !swapped) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq_id);
+  if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+  *swapped = it->second.swapped ? 1 : 0;
+  return PF_OK;
+}
+
 int32_t pf_page_refcount(const pf_pool* pool, int32_t page) {
   if (!pool) return -1;
   std::lock_guard<std::mutex> lk(pool->mu);
@@ -334,6 +383,7 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
   for (int32_t i = 0; i < n; ++i) {
     auto it = pool->seqs.find(seq_ids[i]);
     if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+    if (it->second.swapped) return PF_ERR_SWAPPED;
     if (it->second.pages.size() > (size_t)max_blocks) return PF_ERR_INVALID;
   }
   for (int32_t i = 0; i < n; ++i) {
@@ -430,8 +480,72 @@ const char* pf_status_string(int status) {
     case PF_ERR_HIP: return "HIP runtime error";
     case PF_ERR_UNSUPPORTED: return "unsupported block size or head dim";
     case PF_ERR_SHARED: return "growth would write into a page another sequence shares (use pf_grow_seqs)";
+    case PF_ERR_SWAPPED: return "sequence is swapped out";
     default: return "unknown status";
   }
 }
 
 }  // extern "C"
+
+// Host half of swapping, under the pool lock: validate the batch, then move
+// the sequences' blocks between device pages and host slots and write the
+// copy list (pairs of (page, slot) for out, (slot, page) for in) into out.
+// Returns a status; *pairs receives the number of pairs written.
+int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host, int32_t* out,
+                 int64_t out_words, int32_t* pairs) {
+  *pairs = 0;
+  if (!pool || n < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  if (!pool->dev || !pool->host) return PF_ERR_UNBOUND;
+  std::unordered_map<uint64_t, int> seen;
+  size_t total = 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (seen[seq_ids[i]]++) return PF_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seq_ids[i]);
+    if (to_host) {
+      if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+      if (it->second.swapped) return PF_ERR_SWAPPED;
+      total += it->second.pages.size();
+    } else {
+      if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+      if (!it->second.swapped) return PF_ERR_INVALID;
+      total += it->second.slots.size();
+    }
+  }
+  if (total > (to_host ? pool->slot_stack.size() : pool->stack.size())) return PF_ERR_OOM;
+  if ((int64_t)total * 2 > out_words) return PF_ERR_INVALID;
+  int32_t k = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pf_seq_entry& e = pool->seqs.find(seq_ids[i])->second;
+    if (to_host) {
+      e.slots.clear();
+      for (int32_t page : e.pages) {
+        const int32_t slot = pool->slot_stack.back();
+        pool->slot_stack.pop_back();
+        e.slots.push_back(slot);
+        out[2 * k] = page;
+        out[2 * k + 1] = slot;
+        ++k;
+      }
+      for (size_t j = e.pages.size(); j-- > 0;)
+        if (--pool->refs[(size_t)e.pages[j]] == 0) pool->stack.push_back(e.pages[j]);
+      e.pages.clear();
+      e.swapped = true;
+    } else {
+      e.pages.clear();
+      for (int32_t slot : e.slots) {
+        const int32_t page = pop_page(pool);
+        e.pages.push_back(page);
+        out[2 * k] = slot;
+        out[2 * k + 1] = page;
+        ++k;
+      }
+      for (size_t j = e.slots.size(); j-- > 0;) pool->slot_stack.push_back(e.slots[j]);
+      e.slots.clear();
+      e.swapped = false;
+    }
+  }
+  *pairs = k;
+  return PF_OK;
+}

@@ -13,6 +13,8 @@
 struct pf_seq_entry {
   std::vector<int32_t> pages;  // block table: logical block i -> physical page
   int32_t len = 0;             // tokens held
+  bool swapped = false;        // swapped out: pages empty, slots hold the blocks
+  std::vector<int32_t> slots;  // host swap slots of logical blocks 0.. (swapped only)
 };
 
 struct pf_pool {
@@ -28,6 +30,11 @@ struct pf_pool {
   // Caller-owned device memory bound with pf_pool_bind.
   void* dev = nullptr;
   size_t dev_bytes = 0;
+  // Caller-owned pinned host swap space (pf_swap_bind): num_slots page-sized
+  // slots and their LIFO free stack (top at the back).
+  void* host = nullptr;
+  int32_t num_slots = 0;
+  std::vector<int32_t> slot_stack;
   // Tuning options (pf_pool_set_option).
   int32_t split_tokens = 0;
   int32_t gqa_mfma = 1;
@@ -47,3 +54,10 @@ int pf_fill_meta(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_
 // As pf_fill_meta, followed by [n] pages holding each sequence's newest token
 // (-1 for length 0).
 int pf_fill_meta_step(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out);
+
+// Host half of pf_swap_out (to_host) / pf_swap_in: validate, move the
+// sequences between pages and host slots, and write the copy pairs ((page,
+// slot) out, (slot, page) in) into out (out_words int32).  *pairs = pairs
+// written.  Same errors as the entry points.
+int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host, int32_t* out,
+                 int64_t out_words, int32_t* pairs);

@@ -109,6 +109,30 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* pool, const in
   }
 }
 
+// Swap copies (PagedAttention blog, "Preemption and Swapping": blocks move to
+// CPU memory and back): pair j moves one whole page between the device pool
+// and a page-sized slot of the pinned host store -- (page, slot) pairs when
+// to_host, (slot, page) otherwise.  The kernel reads and writes host memory
+// directly over the host link, 16 bytes per thread; the 64 lanes of a wave
+// fall in one pair, so its pair is one shared read.  Out-of-range ids copy
+// nothing.
+__global__ __launch_bounds__(256) void swap_copy_kernel(uint8_t* pool, uint8_t* host, const int32_t* pairs,
+                                                        int64_t chunks, int64_t total, int32_t num_pages,
+                                                        int32_t num_slots, int32_t to_host) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t j = i / chunks;
+    const int64_t c = i - j * chunks;
+    const int32_t a = pairs[2 * j], b = pairs[2 * j + 1];
+    const int32_t page = to_host ? a : b, slot = to_host ? b : a;
+    if (page < 0 || page >= num_pages || slot < 0 || slot >= num_slots) continue;
+    uint4* dp = reinterpret_cast<uint4*>(pool + (int64_t)page * chunks * 16) + c;
+    uint4* hp = reinterpret_cast<uint4*>(host + (int64_t)slot * chunks * 16) + c;
+    if (to_host) *hp = *dp;
+    else *dp = *hp;
+  }
+}
+
 // Table upload (as upload_kernel) and the scatter of each sequence's newest
 // token for a range of layers, in one launch.  Threads [0, up_threads) copy
 // 16-byte words of the staging into the device table; the rest each move one
@@ -325,4 +349,33 @@ extern "C" int pf_copy_pages(const pf_pool* pool, const int32_t* pairs, int32_t 
   hipLaunchKernelGGL(pf::copy_pages_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream,
                      static_cast<uint8_t*>(pool->dev), pairs, chunks, total, pool->g.num_pages);
   return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}
+
+static int swap_call(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
+                     int64_t staging_words, bool to_host, void* hip_stream) {
+  if (!pool) return PF_ERR_INVALID;
+  if (n > 0 && (!staging_host || (reinterpret_cast<uintptr_t>(staging_host) & 7) != 0)) return PF_ERR_INVALID;
+  const size_t page_bytes = pool->page_elems * pool->elem_bytes;
+  if (page_bytes % 16 != 0) return PF_ERR_UNSUPPORTED;
+  int32_t pairs = 0;
+  const int st = pf_swap_plan(pool, seq_ids, n, to_host, staging_host, staging_words, &pairs);
+  if (st != PF_OK || pairs == 0) return st;
+  const int64_t chunks = (int64_t)(page_bytes / 16);
+  const int64_t total = chunks * pairs;
+  int blocks = 0;
+  pf::launch_grid(total, &blocks);
+  hipLaunchKernelGGL(pf::swap_copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream,
+                     static_cast<uint8_t*>(pool->dev), static_cast<uint8_t*>(pool->host), staging_host, chunks,
+                     total, pool->g.num_pages, pool->num_slots, to_host ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}
+
+extern "C" int pf_swap_out(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
+                           int64_t staging_words, void* hip_stream) {
+  return swap_call(pool, seq_ids, n, staging_host, staging_words, true, hip_stream);
+}
+
+extern "C" int pf_swap_in(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
+                          int64_t staging_words, void* hip_stream) {
+  return swap_call(pool, seq_ids, n, staging_host, staging_words, false, hip_stream);
 }

@@ -29,6 +29,7 @@ PF_ERR_WORKSPACE = -5
 PF_ERR_HIP = -6
 PF_ERR_UNSUPPORTED = -7
 PF_ERR_SHARED = -8
+PF_ERR_SWAPPED = -9
 
 PF_OPT_SPLIT_TOKENS = 0
 PF_OPT_GQA_MFMA = 1
@@ -61,6 +62,11 @@ _SIGS = {
     "pf_grow_seqs": (_i32, [_vp, ctypes.POINTER(_u64), _pi32, _i32, _pi32, _pi32, _pi32]),
     "pf_page_refcount": (_i32, [_vp, _i32]),
     "pf_copy_pages": (_i32, [_vp, _vp, _i32, _vp]),
+    "pf_swap_bind": (_i32, [_vp, _vp, _sz, _i32]),
+    "pf_swap_free_slots": (_i32, [_vp]),
+    "pf_seq_swapped": (_i32, [_vp, _u64, _pi32]),
+    "pf_swap_out": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _vp, ctypes.c_int64, _vp]),
+    "pf_swap_in": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _vp, ctypes.c_int64, _vp]),
     "pf_free_pages": (_i32, [_vp]),
     "pf_num_seqs": (_i32, [_vp]),
     "pf_seq_len": (_i32, [_vp, _u64, _pi32]),
@@ -200,6 +206,36 @@ def pf_grow_seqs(pool, seq_ids, new_lens):
 
 def pf_page_refcount(pool, page):
     return lib.pf_page_refcount(pool, page)
+
+
+def pf_swap_bind(pool, host_ptr, nbytes, num_slots):
+    """``host_ptr``: pinned host tensor / address."""
+    return lib.pf_swap_bind(pool, _dev(host_ptr), nbytes, num_slots)
+
+
+def pf_swap_free_slots(pool):
+    return lib.pf_swap_free_slots(pool)
+
+
+def pf_seq_swapped(pool, seq_id):
+    v = ctypes.c_int32(0)
+    st = lib.pf_seq_swapped(pool, seq_id, ctypes.byref(v))
+    return st, v.value
+
+
+def _swap(fn, pool, seq_ids, staging, staging_words, stream):
+    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
+    return fn(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), _dev(staging), staging_words,
+              _stream(stream))
+
+
+def pf_swap_out(pool, seq_ids, staging, staging_words, stream=None):
+    """``staging``: pinned int32 host tensor (or address) of staging_words words."""
+    return _swap(lib.pf_swap_out, pool, seq_ids, staging, staging_words, stream)
+
+
+def pf_swap_in(pool, seq_ids, staging, staging_words, stream=None):
+    return _swap(lib.pf_swap_in, pool, seq_ids, staging, staging_words, stream)
 
 
 def pf_copy_pages(pool, pairs, n, stream=None):
