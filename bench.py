@@ -422,6 +422,58 @@ def run_swap(n_seqs, reps, seed=44):
     return res
 
 
+def run_block_sweep(names, blocks, reps):
+    """Page-size sweep (PageFault, "Stage 2: memory", block-size table: smaller
+    pages waste less memory but mean longer tables and more indirection per
+    token): the same workload, values and lengths at each block size, shuffled
+    frames, cache flushed before every launch.  Reports the attention
+    partition kernel's time and algorithmic bandwidth, the kernel family, table
+    entries per sequence and the unused tail slots of the reserved pages."""
+    import torch
+    from paged_kv_cache_43_amd import inputs, pf, runner
+
+    fl = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    out = {}
+    for name in names:
+        rows = {}
+        values = None
+        for b in blocks:
+            w = inputs.Workload(name, frames="shuffled", block=b)
+            if values is not None:
+                w._values = values
+            kv = runner.PagedKV(w, sentinel=False)
+            q = runner.fill_workload(kv)
+            values = w._values
+            mc = int(w.ctx.max())
+            kv.ensure_workspace(mc)
+            o = torch.empty((w.n, w.hq, w.d), dtype=torch.int32 if w.es == 4 else torch.int16, device="cuda")
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps + 3)]
+            for a, e in ev:
+                a.record()
+                e.record()
+            torch.cuda.synchronize()
+            for a, e in ev:
+                fl.amax()
+                pf.check(pf.pf_pool_set_timing_events(kv.h, a.cuda_event, e.cuda_event))
+                kv.attention(0, q[0], o, mc)
+            pf.check(pf.pf_pool_set_timing_events(kv.h, None, None))
+            torch.cuda.synchronize()
+            t = float(np.median([a.elapsed_time(e) * 1e3 for a, e in ev[3:]]))
+            pages = (w.ctx + b - 1) // b
+            alg = alg_bytes_attention(w.ctx, w, w.es) - int(((w.ctx + 15) // 16).sum()) * 4 + int(pages.sum()) * 4
+            rows[str(b)] = {"partition_us": round(t, 2), "alg_GBps": round(alg / t / 1e3, 1),
+                            "pct_hbm_peak": round(100 * alg / t / 1e3 / HBM_PEAK_GBS, 1),
+                            "kernel": "mfma" if pf.pf_attention_kernel(kv.h, w.hq) == 1 else "valu",
+                            "table_entries_per_seq": round(float(pages.mean()), 1),
+                            "tail_slots_per_seq": round(float((pages * b - w.ctx).mean()), 2),
+                            "reserved_utilization": round(float(w.ctx.sum() / (pages * b).sum()), 4)}
+            kv.close()
+            del kv, q
+            torch.cuda.empty_cache()
+        out[name] = rows
+    return out
+
+
 def cpu_baseline(name, budget_s):
     """The CPU fp64 oracle (contiguous two-pass softmax attention on decoded
     K/V) on the same workload, single thread: whole passes over every
@@ -489,6 +541,8 @@ def main():
     ap.add_argument("--twin", default="13b,gqa",
                     help="comma list of configs for the paged vs contiguous-cache comparison (shuffled frames)")
     ap.add_argument("--twin-reps", type=int, default=20)
+    ap.add_argument("--block-sweep", default="13b,gqa",
+                    help="comma list of configs for the page-size sweep (8, 16, 32, 64 tokens per page)")
     ap.add_argument("--swap", choices=["on", "off"], default="on",
                     help="swap out/in leg (16 sequences, 13B-style heads)")
     ap.add_argument("--cow", choices=["on", "off"], default="on",
@@ -576,6 +630,9 @@ def main():
         line["cow_prefix_sharing"] = run_cow(16, 4, 20)
     if args.swap == "on":
         line["swap"] = run_swap(16, 10)
+    sweep = [x for x in args.block_sweep.split(",") if x]
+    if sweep:
+        line["block_size_sweep"] = run_block_sweep(sweep, (8, 16, 32, 64), 15)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(line), flush=True)

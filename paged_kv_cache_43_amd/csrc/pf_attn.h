@@ -44,17 +44,21 @@ struct BlockAddr {
   bool ok;
 };
 
-template <bool CONTIG, int D, int ES>
+// p is the unit index inside the sequence (units of BlockUnits<BS>::UT
+// tokens); page is the table entry of the page holding it.
+template <bool CONTIG, int D, int ES, int BS = kBlock>
 __device__ inline BlockAddr block_addr(const AttnArgs& a, int page, int s, int p, int hk) {
+  using BU = BlockUnits<BS>;
   if constexpr (CONTIG) {
-    const int64_t off = ((int64_t)s * a.c_seq + (int64_t)p * kBlock * a.c_tok + (int64_t)hk * a.c_head) * ES;
+    const int64_t off = ((int64_t)s * a.c_seq + (int64_t)p * BU::UT * a.c_tok + (int64_t)hk * a.c_head) * ES;
     return {static_cast<const uint8_t*>(a.kc) + off, static_cast<const uint8_t*>(a.vc) + off, a.c_tok * ES, true};
   } else {
     const bool ok = (unsigned)page < (unsigned)a.num_pages;
     const int64_t off =
-        ((int64_t)(ok ? page : 0) * a.page_elems + ((int64_t)a.layer * a.hkv + hk) * 2 * kBlock * D) * ES;
+        ((int64_t)(ok ? page : 0) * a.page_elems + ((int64_t)a.layer * a.hkv + hk) * 2 * BS * D) * ES +
+        (int64_t)(p % BU::R) * BU::UT * D * ES;
     const uint8_t* k = static_cast<const uint8_t*>(a.pool) + off;
-    return {k, k + kBlock * D * ES, (int64_t)D * ES, ok};
+    return {k, k + BS * D * ES, (int64_t)D * ES, ok};
   }
 }
 
@@ -62,6 +66,8 @@ bool mfma_supports(int head_dim);
 // Launch the matrix-core partition kernel (balanced or grid schedule) over
 // the paged pool or, with contig, over a contiguous cache.
 int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, bool contig, hipStream_t st);
+// The same for a pool of block_size 32 or 64 (balanced schedule, paged).
+int launch_mfma_bs(const AttnArgs& a, int dtype, int head_dim, int block_size, hipStream_t st);
 // Resident waves per CU of the balanced matrix-core kernel (0 if unknown).
 int mfma_balanced_waves_per_cu(int dtype, int head_dim);
 

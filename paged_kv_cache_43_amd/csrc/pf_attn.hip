@@ -38,16 +38,17 @@
 
 namespace pf {
 
-template <class T, int D>
+// UT: tokens per unit of the page walk (16, or 8 for 8-token pages).
+template <class T, int D, int UT = kBlock>
 struct ValuShape {
   static constexpr int ES = T::es;
   static constexpr int VEC0 = 16 / ES;
-  static constexpr int VEC = VEC0 < D * kBlock / kWave ? VEC0 : D * kBlock / kWave;  // elements per lane
+  static constexpr int VEC = VEC0 < D * UT / kWave ? VEC0 : D * UT / kWave;  // elements per lane
   static constexpr int LPT = D / VEC;             // lanes per token
   static constexpr int TPI = kWave / LPT;         // tokens per wave instruction
-  static constexpr int ROWS = kBlock / TPI;       // instructions per K (or V) tile
+  static constexpr int ROWS = UT / TPI;           // instructions per K (or V) unit
   static constexpr int NW = VEC * ES / 4;         // 32-bit words per lane per row
-  static_assert(LPT >= 1 && LPT <= kWave && TPI <= kBlock && ROWS * TPI == kBlock, "shape");
+  static_assert(LPT >= 1 && LPT <= kWave && TPI <= UT && ROWS * TPI == UT, "shape");
   static_assert(NW == 1 || NW == 2 || NW == 4, "load width");
 };
 
@@ -82,10 +83,14 @@ __device__ inline void zero_empty_rows(const AttnArgs& a, const SchedLds& L, int
 }
 
 // Per-wave state of the vector kernel: the current piece's online softmax.
-// CONTIG: blocks come from a contiguous cache instead of pool pages.
-template <class T, int D, bool OUT_F32, bool CONTIG>
+// CONTIG: blocks come from a contiguous cache instead of pool pages.  BS: the
+// pool's tokens per page.
+template <class T, int D, bool OUT_F32, bool CONTIG, int BS = kBlock>
 struct ValuWave {
-  using S = ValuShape<T, D>;
+  static constexpr int UT = BlockUnits<BS>::UT;  // tokens per unit of the walk
+  static constexpr int kPPU = 1;                   // pages per unit
+  static constexpr int kUPP = BlockUnits<BS>::R;   // units per page
+  using S = ValuShape<T, D, UT>;
   struct Tile {
     Raw<S::NW> k[S::ROWS], v[S::ROWS];
   };
@@ -120,7 +125,7 @@ struct ValuWave {
   // query head h; false if the table entry is not a valid page (page 0 is
   // read instead, in bounds).
   __device__ inline bool load(int page, int s, int p, int h, Tile& t) const {
-    const BlockAddr b = block_addr<CONTIG, D, S::ES>(a, page, s, p, h / a.group);
+    const BlockAddr b = block_addr<CONTIG, D, S::ES, BS>(a, page, s, p, h / a.group);
     const int64_t lo = (int64_t)tq * b.tok + dc * S::VEC * S::ES;
 #pragma unroll
     for (int r = 0; r < S::ROWS; ++r) t.k[r] = load_raw<S::NW>(b.k + lo + r * S::TPI * b.tok);
@@ -129,7 +134,7 @@ struct ValuWave {
     return b.ok;
   }
 
-  // One page: nvalid of its 16 tokens are below the length.
+  // One unit: nvalid of its UT tokens are below the length.
   __device__ inline void page(const Tile& t, int nvalid) {
     float sc[S::ROWS];
 #pragma unroll
@@ -141,7 +146,7 @@ struct ValuWave {
       for (int e = 0; e < S::VEC; ++e) d = fmaf(qf[e], kf[e], d);
       sc[r] = group_reduce<S::LPT, OpSum>(d);
     }
-    const bool full = nvalid >= kBlock;
+    const bool full = nvalid >= UT;
     if (!full) {
 #pragma unroll
       for (int r = 0; r < S::ROWS; ++r)
@@ -236,15 +241,15 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
 
 // Balanced schedule (pf_sched.h): four waves per workgroup, items are query
 // heads.
-template <class T, int D, int U, bool OUT_F32, bool CONTIG>
+template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock>
 __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) {
-  using Wv = ValuWave<T, D, OUT_F32, CONTIG>;
+  using Wv = ValuWave<T, D, OUT_F32, CONTIG, BS>;
   __shared__ SchedLds L;
-  sched_build(a, L);
+  sched_build<Wv::UT>(a, L);
   zero_empty_rows<T, OUT_F32>(a, L, D);
   const int lane = threadIdx.x % kWave;
   Wv w(a, lane);
-  sched_run<U>(a, L, a.hq, w, lane);
+  sched_run<U, BS>(a, L, a.hq, w, lane);
 }
 
 // Merge the pieces of every output row that was split: M = max m_j,
@@ -310,11 +315,45 @@ __global__ __launch_bounds__(kWave) void attn_merge_kernel(AttnArgs a, int D, in
 // ---------------------------------------------------------------- launchers
 // Pages per prefetch unit: two units are in flight per wave; a unit holds
 // about 32 VGPRs of K/V per lane.
-template <class T, int D>
+template <class T, int D, int UT = kBlock>
 struct ValuUnit {
-  static constexpr int bytes = 2 * kBlock * D * T::es / kWave;  // per lane per page
+  static constexpr int bytes = 2 * UT * D * T::es / kWave;  // per lane per unit
   static constexpr int U = bytes >= 128 ? 1 : (bytes >= 64 ? 2 : 4);
 };
+
+// Pools of 8, 32 or 64 tokens per page: balanced schedule, paged, 16-bit
+// elements, head dim 64 or 128.
+template <class T, int D, bool OUT_F32, int BS>
+static void launch_valu_bs_t(const AttnArgs& a, hipStream_t st) {
+  constexpr int U = ValuUnit<T, D, BlockUnits<BS>::UT>::U;
+  hipLaunchKernelGGL((attn_valu_balanced<T, D, U, OUT_F32, false, BS>), dim3(a.waves / (kSchedThreads / kWave)),
+                     dim3(kSchedThreads), 0, st, a);
+}
+
+template <class T, int D, bool OUT_F32>
+static int launch_valu_bs_d(const AttnArgs& a, int bs, hipStream_t st) {
+  switch (bs) {
+    case 8: launch_valu_bs_t<T, D, OUT_F32, 8>(a, st); return PF_OK;
+    case 32: launch_valu_bs_t<T, D, OUT_F32, 32>(a, st); return PF_OK;
+    case 64: launch_valu_bs_t<T, D, OUT_F32, 64>(a, st); return PF_OK;
+    default: return PF_ERR_UNSUPPORTED;
+  }
+}
+
+template <class T>
+static int launch_valu_bs(const AttnArgs& a, int D, int bs, hipStream_t st) {
+  if (D == 64) return a.out_f32 ? launch_valu_bs_d<T, 64, true>(a, bs, st) : launch_valu_bs_d<T, 64, false>(a, bs, st);
+  if (D == 128)
+    return a.out_f32 ? launch_valu_bs_d<T, 128, true>(a, bs, st) : launch_valu_bs_d<T, 128, false>(a, bs, st);
+  return PF_ERR_UNSUPPORTED;
+}
+
+// Block sizes other than 16 are built for 16-bit elements at head dim 64 or
+// 128, balanced schedule, paged pool.
+static bool block_size_supported(int bs, int dtype, int D) {
+  if (bs == kBlock) return true;
+  return (bs == 8 || bs == 32 || bs == 64) && dtype != PF_F32 && (D == 64 || D == 128);
+}
 
 template <class T, int D, bool OUT_F32>
 static const void* valu_kernel_ptr(bool balanced) {
@@ -443,7 +482,7 @@ bool use_mfma(const pf_pool* pool, int32_t num_q_heads) {
   const pf_geometry& g = pool->g;
   if (!pool->gqa_mfma || g.dtype == PF_F32) return false;
   const int group = num_q_heads / g.num_kv_heads;
-  return group > 1 && group <= 16 && mfma_supports(g.head_dim);
+  return group > 1 && group <= 16 && mfma_supports(g.head_dim) && (g.block_size == 8 || g.block_size % kBlock == 0);
 }
 
 // Grid schedule split: the largest split (64 pages) unless that leaves fewer
@@ -466,8 +505,9 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
   p.items_per_seq = p.mfma ? g.num_kv_heads : num_q_heads;
   p.rows_per_item = p.mfma ? num_q_heads / g.num_kv_heads : 1;
   const int sched = pool->schedule;
-  p.balanced = sched == 2 || (sched == 0 && n <= kMaxSeqsBalanced);
+  p.balanced = sched == 2 || (sched == 0 && n <= kMaxSeqsBalanced) || g.block_size != kBlock;
   if (n > kMaxSeqsBalanced) p.balanced = false;
+  const int ut = g.block_size < kBlock ? g.block_size : kBlock;  // tokens per unit of the walk
   if (p.balanced) {
     // Waves: 8 per CU (two per SIMD), or fewer if the kernel's occupancy is
     // lower, and no more than one wave per 4 pages of the longest possible
@@ -487,7 +527,7 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
       per_cu = occ > 0 && occ < 8 ? occ : 8;
     }
     const int64_t wpg = kSchedThreads / kWave;
-    const int64_t upper = (int64_t)n * p.items_per_seq * ((max_ctx + kBlock - 1) / kBlock);
+    const int64_t upper = (int64_t)n * p.items_per_seq * ((max_ctx + ut - 1) / ut);
     int64_t waves = (int64_t)device_cus() * per_cu;
     const int64_t cap = (upper + 3) / 4;
     if (waves > cap) waves = cap;
@@ -553,7 +593,11 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   if (n < 0 || num_q_heads <= 0 || num_q_heads % g.num_kv_heads != 0 || max_context_len < 0)
     return PF_ERR_INVALID;
   if (out_dtype != PF_F32 && out_dtype != g.dtype) return PF_ERR_INVALID;
-  if (g.block_size != kBlock || !valu_supports(g.dtype, g.head_dim)) return PF_ERR_UNSUPPORTED;
+  // the contiguous twin walks 16-token blocks whatever the pool's page size
+  const int bs = contig ? kBlock : g.block_size;
+  if (!valu_supports(g.dtype, g.head_dim) || !block_size_supported(bs, g.dtype, g.head_dim))
+    return PF_ERR_UNSUPPORTED;
+  if (bs != kBlock && n > kMaxSeqsBalanced) return PF_ERR_UNSUPPORTED;
   if (n == 0) return PF_OK;
   if (n > 65535 || num_q_heads > 65535) return PF_ERR_INVALID;
   if (!q || !ctx_dev || !out) return PF_ERR_INVALID;
@@ -592,7 +636,11 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   hipStream_t st = (hipStream_t)hip_stream;
   if (pool->ev_start) (void)hipEventRecord((hipEvent_t)pool->ev_start, st);
   int rc;
-  if (p.mfma) {
+  if (bs != kBlock) {
+    if (p.mfma) rc = launch_mfma_bs(a, g.dtype, g.head_dim, bs, st);
+    else if (g.dtype == PF_F16) rc = launch_valu_bs<ElF16>(a, g.head_dim, bs, st);
+    else rc = launch_valu_bs<ElBF16>(a, g.head_dim, bs, st);
+  } else if (p.mfma) {
     rc = launch_mfma(a, g.dtype, g.head_dim, p.balanced, contig, st);
   } else {
     switch (g.dtype) {

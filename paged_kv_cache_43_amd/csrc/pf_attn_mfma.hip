@@ -92,9 +92,17 @@ __device__ inline void store_vec4(void* out, int64_t idx, const float* v) {
 
 // Per-wave state of the matrix-core kernel: the current piece's online
 // softmax for the 16 score columns (query heads of one kv head, padded).
-// CONTIG: blocks come from a contiguous cache instead of pool pages.
-template <class T, int D, bool OUT_F32, bool CONTIG>
+// CONTIG: blocks come from a contiguous cache instead of pool pages.  BS: the
+// pool's tokens per page.  The walk is in 16-token tiles: a 32- or 64-token
+// page is two or four tiles, and a tile of 8-token pages spans two pages
+// (rows 0..7 from the first, 8..15 from the second).
+template <class T, int D, bool OUT_F32, bool CONTIG, int BS = kBlock>
 struct MfmaWave {
+  static_assert(BS == 8 || BS % kBlock == 0, "block size");
+  static constexpr int UT = kBlock;                 // tokens per unit of the walk
+  static constexpr int kPPU = BS < kBlock ? kBlock / BS : 1;  // pages per unit
+  static constexpr int kUPP = BS < kBlock ? 1 : BS / kBlock;  // units per page
+  static_assert(kPPU == 1 || kPPU == 2, "pages per tile");
   static constexpr int ES = 2;
   static constexpr int KC = D / 32;                // 32-dim chunks of the score product
   static constexpr int DB = D / 16;                // 16-dim blocks of the value product
@@ -107,6 +115,7 @@ struct MfmaWave {
   struct Tile {
     uint4 k[KC];
     uint4 v[VL];
+    uint32_t okm;  // two pages per tile: bit 0 first page valid, bit 1 second
   };
   const AttnArgs& a;
   uint8_t* vt;  // this wave's V staging tile in LDS
@@ -148,7 +157,7 @@ struct MfmaWave {
   // hk: K as score-product operands, V as 16-byte coalesced chunks.  False if
   // the table entry is not a valid page (page 0 is read instead, in bounds).
   __device__ inline bool load(int page, int s, int p, int hk, Tile& t) const {
-    const BlockAddr b = block_addr<CONTIG, D, ES>(a, page, s, p, hk);
+    const BlockAddr b = block_addr<CONTIG, D, ES, BS>(a, page, s, p, hk);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       t.k[c] = *reinterpret_cast<const uint4*>(b.k + col * b.tok + (32 * c + 8 * grp) * ES);
@@ -160,9 +169,35 @@ struct MfmaWave {
     return b.ok;
   }
 
-  // One page: nvalid of its 16 tokens are below the length.
+  // The same for a tile of two 8-token pages (first, second; an entry that is
+  // not a valid page reads page 0, in bounds, and its rows are masked).
+  __device__ inline bool load2(int page0, int page1, int s, int hk, Tile& t) const {
+    const BlockAddr b0 = block_addr<CONTIG, D, ES, BS>(a, page0, s, 0, hk);
+    const BlockAddr b1 = block_addr<CONTIG, D, ES, BS>(a, page1, s, 0, hk);
+    const uint8_t* kb = (col < BS ? b0.k : b1.k) + (col % BS) * b0.tok;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kb + (32 * c + 8 * grp) * ES);
+#pragma unroll
+    for (int r = 0; r < VL; ++r) {
+      const int f = r * kWave + lane;
+      const int tok = f / VCH;
+      t.v[r] = *reinterpret_cast<const uint4*>((tok < BS ? b0.v : b1.v) + (tok % BS) * b0.tok + (f % VCH) * 16);
+    }
+    t.okm = (b0.ok ? 1u : 0u) | (b1.ok ? 2u : 0u);
+    return b0.ok || b1.ok;
+  }
+
+  // One tile: nvalid of its 16 tokens are below the length (and, for two
+  // pages per tile, in a valid page).
   __device__ inline void page(const Tile& t, int nvalid) {
-    const bool full = nvalid >= kBlock;
+    bool lo_ok = true, hi_ok = true;
+    if constexpr (kPPU == 2) {
+      lo_ok = (t.okm & 1u) != 0;
+      hi_ok = (t.okm & 2u) != 0;
+      if (!((lo_ok && nvalid > 0) || (hi_ok && nvalid > BS))) return;  // nothing valid
+    }
+    const bool full = nvalid >= kBlock && lo_ok && hi_ok;
+    auto tok_ok = [&](int tok) { return tok < nvalid && (tok < BS ? lo_ok : hi_ok); };
     // stage V (row-major, padded rows; tokens past the length as zeros)
 #pragma unroll
     for (int r = 0; r < VL; ++r) {
@@ -170,7 +205,7 @@ struct MfmaWave {
       const int tok = f / VCH;
       const int ch = f % VCH;
       uint4 v = t.v[r];
-      if (!full && tok >= nvalid) v = make_uint4(0, 0, 0, 0);
+      if (!full && !tok_ok(tok)) v = make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(vt + tok * PITCH + ch * 16) = v;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -182,7 +217,7 @@ struct MfmaWave {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       z[r] = sc[r] * a.qscale;
-      if (!full && 4 * grp + r >= nvalid) z[r] = -INFINITY;
+      if (!full && !tok_ok(4 * grp + r)) z[r] = -INFINITY;
     }
     // The reference max m moves only when some score exceeds it by more than
     // 8 (log2 units): probabilities then stay below 2^8, and the cross-group
@@ -297,12 +332,12 @@ __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
 
 // Balanced schedule (pf_sched.h): four waves per workgroup, items are kv
 // heads (each covering its group of query heads).
-template <class T, int D, int U, bool OUT_F32, bool CONTIG>
+template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock>
 __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) {
-  using Wv = MfmaWave<T, D, OUT_F32, CONTIG>;
+  using Wv = MfmaWave<T, D, OUT_F32, CONTIG, BS>;
   __shared__ SchedLds L;
   __shared__ __attribute__((aligned(16))) uint8_t vt[kSchedThreads / kWave][Wv::TILE_BYTES];
-  sched_build(a, L);
+  sched_build<Wv::UT>(a, L);
   if (blockIdx.x == 0) {  // zero rows of empty sequences: one thread per sequence
     const int64_t row_elems = (int64_t)a.hq * D;
     for (int s0 = threadIdx.x; s0 < a.n; s0 += kSchedThreads) {
@@ -316,7 +351,7 @@ __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   Wv w(a, vt[wave], lane);
-  sched_run<U>(a, L, a.hkv, w, lane);
+  sched_run<U, BS>(a, L, a.hkv, w, lane);
 }
 
 bool mfma_supports(int head_dim) { return head_dim == 64 || head_dim == 128; }
@@ -357,6 +392,29 @@ static int launch_t(const AttnArgs& a, int D, bool balanced, bool contig, hipStr
 int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, bool contig, hipStream_t st) {
   return dtype == PF_F16 ? launch_t<ElF16>(a, head_dim, balanced, contig, st)
                          : launch_t<ElBF16>(a, head_dim, balanced, contig, st);
+}
+
+template <class T, int D, bool OUT_F32>
+static int launch_bs_d(const AttnArgs& a, int bs, hipStream_t st) {
+  const dim3 grid(a.waves / (kSchedThreads / kWave));
+  switch (bs) {
+    case 8: hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, OUT_F32, false, 8>), grid, dim3(kSchedThreads), 0, st, a); return PF_OK;
+    case 32: hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, OUT_F32, false, 32>), grid, dim3(kSchedThreads), 0, st, a); return PF_OK;
+    case 64: hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, OUT_F32, false, 64>), grid, dim3(kSchedThreads), 0, st, a); return PF_OK;
+    default: return PF_ERR_UNSUPPORTED;
+  }
+}
+
+template <class T>
+static int launch_bs_t(const AttnArgs& a, int D, int bs, hipStream_t st) {
+  if (D == 64) return a.out_f32 ? launch_bs_d<T, 64, true>(a, bs, st) : launch_bs_d<T, 64, false>(a, bs, st);
+  if (D == 128) return a.out_f32 ? launch_bs_d<T, 128, true>(a, bs, st) : launch_bs_d<T, 128, false>(a, bs, st);
+  return PF_ERR_UNSUPPORTED;
+}
+
+int launch_mfma_bs(const AttnArgs& a, int dtype, int head_dim, int block_size, hipStream_t st) {
+  return dtype == PF_F16 ? launch_bs_t<ElF16>(a, head_dim, block_size, st)
+                         : launch_bs_t<ElBF16>(a, head_dim, block_size, st);
 }
 
 int mfma_balanced_waves_per_cu(int dtype, int head_dim) {

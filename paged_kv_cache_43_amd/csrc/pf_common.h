@@ -9,7 +9,17 @@
 namespace pf {
 
 constexpr int kWave = 64;
-constexpr int kBlock = 16;  // tokens per page the kernels are built for
+constexpr int kBlock = 16;  // tokens per page of the default build (grid schedule, contiguous twin)
+
+// The attention kernels walk a sequence in units of at most 16 tokens: a
+// 16-token page is one unit, a 32- or 64-token page two or four (one table
+// entry, rows offset inside the page), an 8-token page one 8-token unit.
+template <int BS>
+struct BlockUnits {
+  static constexpr int UT = BS < 16 ? BS : 16;  // tokens per unit
+  static constexpr int R = BS / UT;             // units per page
+  static_assert(UT * R == BS && (BS == 8 || BS % 16 == 0), "block size");
+};
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- elements

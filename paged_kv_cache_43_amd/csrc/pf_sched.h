@@ -45,6 +45,7 @@ __device__ inline int clamp_ctx(int c, int max_ctx) { return c < 0 ? 0 : (c > ma
 
 // All threads of the workgroup: clamped lengths and the exclusive page-count
 // prefix into LDS.  Ends with a workgroup barrier.
+template <int UT = kBlock>
 __device__ inline void sched_build(const AttnArgs& a, SchedLds& L) {
   const int t = threadIdx.x;
   const int lane = t % kWave;
@@ -62,7 +63,7 @@ __device__ inline void sched_build(const AttnArgs& a, SchedLds& L) {
         c = clamp_ctx(a.ctx[s], a.max_ctx);
         L.ctx[s] = c;
       }
-      sum += (c + kBlock - 1) / kBlock;
+      sum += (c + UT - 1) / UT;
       incl[k] = sum;
     }
   }
@@ -111,11 +112,16 @@ __device__ inline PagePos sched_locate(const SchedLds& L, int n, int X, int64_t 
 // begin(s, x), load(page, s, p, x, tile) -> bool, page(tile, nvalid),
 // finish_slot(s, x, whole, slot) and kContig (no table).
 // The balanced schedule's driver, shared by both kernels: this wave's slice
-// of the stream, piece by piece.  Wv provides begin(s, x), load(page, s, p, x,
-// tile) -> bool, page(tile, nvalid), finish_slot(s, x, whole, slot) and
-// kContig (blocks addressed without a table).
-template <int U, class Wv>
+// of the stream, piece by piece.  The stream is counted in units of Wv::UT
+// tokens (the prefix in L must be built with the same UT); a unit is part of
+// one page (Wv::kUPP units per page) or, for pages shorter than a unit, spans
+// Wv::kPPU = 2 pages.  Wv provides begin(s, x), load(page, s, p, x, tile) ->
+// bool (load2(page0, page1, s, x, tile) for two pages per unit),
+// page(tile, nvalid), finish_slot(s, x, whole, slot) and kContig (blocks
+// addressed without a table).
+template <int U, int BS, class Wv>
 __device__ inline void sched_run(const AttnArgs& a, const SchedLds& L, int X, Wv& w, int lane) {
+  constexpr int UT = Wv::UT;
   using Tile = typename Wv::Tile;
   const int gw = blockIdx.x * (kSchedThreads / kWave) + threadIdx.x / kWave;
   const int64_t total = (int64_t)X * L.pfx[a.n];
@@ -137,21 +143,33 @@ __device__ inline void sched_run(const AttnArgs& a, const SchedLds& L, int X, Wv
   };
   for (int64_t base = wa; base < wb; base += kWave) {
     const int cnt = (int)min((int64_t)kWave, wb - base);
-    int ls = 0, lx = 0, lp = 0, lP = 1, lpage = -1, lnv = 0;
+    int ls = 0, lx = 0, lp = 0, lP = 1, lpage = -1, lpage2 = -1, lnv = 0;
     if (lane < cnt) {
       const PagePos pp = sched_locate(L, a.n, X, base + lane);
       ls = pp.s;
       lx = pp.x;
       lp = pp.p;
       lP = pp.P;
-      if constexpr (!Wv::kContig) lpage = a.bt[(int64_t)pp.s * a.max_blocks + pp.p];
-      lnv = min(kBlock, L.ctx[pp.s] - pp.p * kBlock);
+      if constexpr (!Wv::kContig) {
+        const int64_t row = (int64_t)pp.s * a.max_blocks;
+        if constexpr (Wv::kPPU == 2) {
+          lpage = a.bt[row + 2 * pp.p];
+          if (2 * pp.p + 1 < (L.ctx[pp.s] + BS - 1) / BS) lpage2 = a.bt[row + 2 * pp.p + 1];
+        } else {
+          lpage = a.bt[row + pp.p / Wv::kUPP];
+        }
+      }
+      lnv = min(UT, L.ctx[pp.s] - pp.p * UT);
     }
     page_pipeline<U, Tile>(
         cnt,
         [&](int i, Tile& t) {
-          return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
-                        __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
+          if constexpr (Wv::kPPU == 2)
+            return w.load2(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(lpage2, i),
+                           __builtin_amdgcn_readlane(ls, i), __builtin_amdgcn_readlane(lx, i), t);
+          else
+            return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
+                          __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
         },
         [&](int i, const Tile& t, bool ok) {
           const int s = __builtin_amdgcn_readlane(ls, i);

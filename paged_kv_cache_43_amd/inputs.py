@@ -138,7 +138,7 @@ class Workload:
     step's allocations).  Sequence ids of the workload are 0..n-1.
     """
 
-    def __init__(self, name, seed=None, frames="shuffled", n=None, lens=None):
+    def __init__(self, name, seed=None, frames="shuffled", n=None, lens=None, block=BLOCK):
         cfg = dict(CONFIGS[name])
         self.name = name
         self.seed = cfg["seed"] if seed is None else seed
@@ -148,7 +148,7 @@ class Workload:
         self.layers, self.hq, self.hkv, self.d = cfg["layers"], cfg["hq"], cfg["hkv"], cfg["d"]
         self.dtype = cfg["dtype"]
         self.es = DTYPE_BYTES[self.dtype]
-        self.block = BLOCK
+        self.block = int(block)
         spec = cfg["lens"]
         if lens is not None:
             self.ctx = np.asarray(lens, dtype=np.int64)
@@ -156,10 +156,11 @@ class Workload:
         else:
             self.ctx = draw_lengths(spec, self.n, g_len)
         if cfg["pool"] == "1.1x":
-            used = int(sum(-(-int(c) // BLOCK) for c in self.ctx))
+            used = int(sum(-(-int(c) // self.block) for c in self.ctx))
             self.num_pages = int(math.ceil(1.1 * used))
         else:
-            self.num_pages = int(cfg["pool"])
+            # the same token capacity in pages of this block size
+            self.num_pages = -(-int(cfg["pool"]) * BLOCK // self.block)
         if frames == "ordered":
             self.free_order = np.arange(self.num_pages, dtype=np.int64)
         elif frames == "shuffled":
@@ -184,7 +185,7 @@ class Workload:
         self._values = None
 
     def max_blocks(self, extra_tokens=0):
-        return int(-(-(int(self.ctx.max()) + extra_tokens) // BLOCK)) if self.n else 1
+        return int(-(-(int(self.ctx.max()) + extra_tokens) // self.block)) if self.n else 1
 
     def values(self):
         """K/V bits per sequence ``[L][ctx_s][Hkv][D]`` and q bits ``[L][n][Hq][D]``."""

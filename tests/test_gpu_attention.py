@@ -222,3 +222,67 @@ def test_scale_argument():
     ref = gu.oracle_attention_contiguous(w, 0, scale=0.9)
     gu.assert_close(got, ref, "f32", "scale 0.9")
     kv.close()
+
+
+@pytest.mark.parametrize("block", [8, 32, 64])
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f16", 4, 4, 128), ("bf16", 14, 2, 64), ("f16", 8, 2, 128)])
+@pytest.mark.parametrize("out_dtype", ["f32", None])
+def test_block_sizes(block, dtype, hq, hkv, d, out_dtype):
+    """Pages of 8, 32 and 64 tokens: lengths on both sides of every unit and
+    page boundary, vector kernel and (for 32 and 64) the matrix-core kernel;
+    ordered and shuffled frames give the same bits."""
+    print("block", block, dtype, hq, hkv, d, out_dtype, flush=True)
+    from paged_kv_cache_43_amd import pf
+    lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 200, 513, 1000]
+    res = {}
+    for frames in ("ordered", "shuffled"):
+        w = inputs.Workload("tiny", seed=block + d, frames=frames, lens=lens, block=block)
+        w.hq, w.hkv, w.d, w.dtype, w.es = hq, hkv, d, dtype, inputs.DTYPE_BYTES[dtype]
+        w.num_pages = sum(-(-int(c) // block) for c in lens) + 8
+        w.free_order = (np.arange(w.num_pages) if frames == "ordered"
+                        else np.random.default_rng(block).permutation(w.num_pages))
+        got, kv, q = _run(w, out_dtype=out_dtype)
+        mfma = pf.pf_attention_kernel(kv.h, hq) == 1
+        assert mfma == (hq > hkv), (block, mfma)
+        od = out_dtype or dtype
+        gu.assert_close(got, gu.oracle_attention_contiguous(w, 0), od, "block %d %s" % (block, frames))
+        res[frames] = got
+        kv.close()
+    assert np.array_equal(res["ordered"], res["shuffled"])
+
+
+@pytest.mark.parametrize("block,drops", [(8, {0: [1], 1: [2], 2: [4]}), (32, {0: [0], 1: [1]}),
+                                         (16, {0: [1], 1: [2], 2: [0]})])
+def test_invalid_entries_grouped_heads(block, drops):
+    """Matrix-core kernel with invalid table entries at every position a page
+    can hold in a tile: with 8-token pages the first or the second page of a
+    16-token tile (the other half still counts), with 32-token pages a page of
+    two tiles.  The result is attention over the remaining tokens."""
+    print("invalid entries mfma block", block, flush=True)
+    from paged_kv_cache_43_amd import pf
+    lens = [40, 45, 80]
+    w = inputs.Workload("tiny", seed=block, frames="shuffled", lens=lens, block=block)
+    w.hq, w.hkv, w.d, w.dtype, w.es = 4, 2, 64, "bf16", 2
+    w.num_pages = sum(-(-c // block) for c in lens) + 8
+    w.free_order = np.random.default_rng(block + 1).permutation(w.num_pages)
+    r = _r()
+    kv = r.PagedKV(w)
+    q = r.fill_workload(kv)
+    assert pf.pf_attention_kernel(kv.h, 4) == 1
+    bt = kv.bt.clone()
+    for s, pages in drops.items():
+        for i, page_idx in enumerate(pages):
+            bt[s, page_idx] = -1 if i % 2 == 0 else w.num_pages
+    kv.bt.copy_(bt)
+    got = _run(w, out_dtype="f32", kv=kv, q=q)
+    ks, vs, qb = w.values()
+    qd = oa.decode_bits(qb[0], "bf16")
+    for s, n in enumerate(lens):
+        drop = {t for p_ in drops.get(s, []) for t in range(p_ * block, (p_ + 1) * block)}
+        keep = [t for t in range(n) if t not in drop]
+        K = oa.decode_bits(ks[s][0], "bf16")[keep]
+        V = oa.decode_bits(vs[s][0], "bf16")[keep]
+        for h in range(4):
+            ref = oa.attention(qd[s, h], K[:, h // 2], V[:, h // 2], oa.default_scale(64))
+            assert np.max(np.abs(got[s, h] - ref)) <= gu.ATOL, (s, h)
+    kv.close()
