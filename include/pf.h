@@ -311,6 +311,26 @@ int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
                               int32_t out_dtype, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
 
+/* pf_scatter_kv of each sequence's newest token fused into
+ * pf_paged_decode_attention, in one launch (PageForge, "Five techniques" and its
+ * roadmap: the per-step scatter launches are the cost to remove).  For every
+ * sequence i with ctx_dev[i] > 0, the token at position ctx_dev[i] - 1 has K
+ * and V k_new[i], v_new[i] ([H][D] each): it is written into its slot of page
+ * bt_dev[i][(ctx-1)/B] for `layer`, and the attention uses it as that token.
+ * The result and the pool afterwards are those of pf_scatter_kv (those tokens,
+ * that layer) followed by pf_paged_decode_attention.  If the newest token's
+ * table entry is not a valid page, nothing is written and that page's tokens
+ * contribute nothing (as for any invalid entry).
+ *   k_new, v_new  device [n][H][D], pool dtype, 16-byte aligned.
+ * Other arguments as pf_paged_decode_attention.  Built for 16-token pages
+ * (PF_ERR_UNSUPPORTED otherwise) and head dims whose rows are a multiple of
+ * 16 bytes.  Errors: as pf_paged_decode_attention. */
+int pf_paged_decode_attention_append(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                                     const void* k_new, const void* v_new, const int32_t* bt_dev,
+                                     int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
+                                     int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                                     void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* The same attention over a contiguous per-sequence cache, with no table walk
  * (PageFault, "Four stages": stage 1's contiguous cache is the baseline that
  * stage 3's paged kernel is checked and timed against).  The kernels,

@@ -29,7 +29,19 @@ struct AttnArgs {
   const void* kc;
   const void* vc;
   int64_t c_seq, c_tok, c_head;
+  // Fused append (pf_paged_decode_attention_append): [n][hkv][D] K/V of each
+  // sequence's newest token, written into its slot and used from registers;
+  // null otherwise.
+  const void* k_new;
+  const void* v_new;
 };
+
+template <int NW>
+__device__ inline void store_raw(void* p, const Raw<NW>& r) {
+  if constexpr (NW == 4) *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+  else if constexpr (NW == 2) *reinterpret_cast<uint2*>(p) = make_uint2(r.w[0], r.w[1]);
+  else *reinterpret_cast<uint32_t*>(p) = r.w[0];
+}
 
 // Where the 16 tokens of block p of sequence s live for kv head hk: byte
 // addresses of the K and V rows of the block's first token and the byte step

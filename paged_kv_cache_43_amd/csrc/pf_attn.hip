@@ -177,6 +177,36 @@ struct ValuWave {
     }
   }
 
+  // Before page() of the sequence's last unit (row nvalid-1 is its newest
+  // token), in pool page `page` (ok: a valid page).  With a fused append the
+  // newest token's K/V come from the input instead of the pool, patched into
+  // the tile, and the first query head of each kv head group writes them into
+  // the page (16-token pages only); other waves that read the slot meanwhile
+  // discard what they read.
+  __device__ inline void patch_last(Tile& u, int nvalid, int s, int h, int page, bool ok) {
+    if (a.k_new == nullptr || !ok) return;
+    const int tn = nvalid - 1;
+    const int hk = h / a.group;
+    if (tq == tn % S::TPI) {
+      const int64_t src = (((int64_t)s * a.hkv + hk) * D + dc * S::VEC) * S::ES;
+      const Raw<S::NW> kk = load_raw<S::NW>(static_cast<const uint8_t*>(a.k_new) + src);
+      const Raw<S::NW> vv = load_raw<S::NW>(static_cast<const uint8_t*>(a.v_new) + src);
+#pragma unroll
+      for (int r = 0; r < S::ROWS; ++r)
+        if (r == tn / S::TPI) {
+          u.k[r] = kk;
+          u.v[r] = vv;
+        }
+      if (h % a.group == 0) {
+        uint8_t* base = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.pool)) +
+                        ((int64_t)page * a.page_elems + ((int64_t)a.layer * a.hkv + hk) * 2 * BS * D +
+                         (int64_t)tn * D + dc * S::VEC) * S::ES;
+        store_raw<S::NW>(base, kk);
+        store_raw<S::NW>(base + (int64_t)BS * D * S::ES, vv);
+      }
+    }
+  }
+
   // Balanced schedule: items are query heads, one record per slot.
   __device__ inline void finish_slot(int s, int h, bool whole, int64_t slot) { finish(s, h, whole, slot); }
 
@@ -233,8 +263,10 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
   w.begin(s, h);
   page_pipeline<U, Tile>(
       npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), s, pg0 + i, h, t); },
-      [&](int i, const Tile& t, bool ok) {
-        if (ok) w.page(t, min(kBlock, tok_end - (pg0 + i) * kBlock));
+      [&](int i, Tile& t, bool ok) {
+        const int nv = min(kBlock, tok_end - (pg0 + i) * kBlock);
+        if (pg0 + i == (ctx - 1) / kBlock) w.patch_last(t, nv, s, h, __builtin_amdgcn_readlane(my_page, i), ok);
+        if (ok) w.page(t, nv);
       });
   w.finish(s, h, nsplit == 1, ((int64_t)s * a.hq + h) * a.max_splits + split);
 }
@@ -665,12 +697,10 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
 
 }  // namespace
 
-extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
-                                         int32_t num_q_heads, const int32_t* bt_dev,
-                                         int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
-                                         int32_t max_context_len, float scale, void* out,
-                                         int32_t out_dtype, void* workspace, size_t workspace_bytes,
-                                         void* hip_stream) {
+static int paged_attention(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                           const void* k_new, const void* v_new, const int32_t* bt_dev, int32_t max_blocks,
+                           const int32_t* ctx_dev, int32_t n, int32_t max_context_len, float scale, void* out,
+                           int32_t out_dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (!pool) return PF_ERR_INVALID;
   if (!pool->dev) return PF_ERR_UNBOUND;
   const pf_geometry& g = pool->g;
@@ -685,8 +715,36 @@ extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, con
   a.layer = layer;
   a.num_pages = g.num_pages;
   a.max_blocks = max_blocks;
+  a.k_new = k_new;
+  a.v_new = v_new;
   return attend(pool, a, false, q, num_q_heads, ctx_dev, n, max_context_len, scale, out, out_dtype, workspace,
                 workspace_bytes, hip_stream);
+}
+
+extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
+                                         int32_t num_q_heads, const int32_t* bt_dev,
+                                         int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
+                                         int32_t max_context_len, float scale, void* out,
+                                         int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                         void* hip_stream) {
+  return paged_attention(pool, layer, q, num_q_heads, nullptr, nullptr, bt_dev, max_blocks, ctx_dev, n,
+                         max_context_len, scale, out, out_dtype, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int pf_paged_decode_attention_append(const pf_pool* pool, int32_t layer, const void* q,
+                                                int32_t num_q_heads, const void* k_new, const void* v_new,
+                                                const int32_t* bt_dev, int32_t max_blocks, const int32_t* ctx_dev,
+                                                int32_t n, int32_t max_context_len, float scale, void* out,
+                                                int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                                void* hip_stream) {
+  if (!pool) return PF_ERR_INVALID;
+  if (pool->g.block_size != kBlock) return PF_ERR_UNSUPPORTED;
+  if (n > 0 && (!k_new || !v_new || reinterpret_cast<uintptr_t>(k_new) % 16 != 0 ||
+                reinterpret_cast<uintptr_t>(v_new) % 16 != 0))
+    return PF_ERR_INVALID;
+  if ((size_t)pool->g.head_dim * pool->elem_bytes % 16 != 0) return PF_ERR_UNSUPPORTED;
+  return paged_attention(pool, layer, q, num_q_heads, k_new, v_new, bt_dev, max_blocks, ctx_dev, n,
+                         max_context_len, scale, out, out_dtype, workspace, workspace_bytes, hip_stream);
 }
 
 extern "C" int pf_contiguous_decode_attention(const pf_pool* pool, const void* q, int32_t num_q_heads,

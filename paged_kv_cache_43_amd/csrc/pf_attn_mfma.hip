@@ -258,6 +258,37 @@ struct MfmaWave {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
 
+  // Before page() of the sequence's last tile (row nvalid-1 is its newest
+  // token), in pool page `page` (ok: a valid page).  With a fused append the
+  // newest token's K/V come from the input instead of the pool, patched into
+  // the tile, and this wave (the only one for this kv head) writes them into
+  // the page (16-token pages only).
+  __device__ inline void patch_last(Tile& u, int nvalid, int s, int hk, int page, bool ok) {
+    if (a.k_new == nullptr || !ok) return;
+    const int tn = nvalid - 1;
+    const int64_t row = ((int64_t)s * a.hkv + hk) * D * ES;
+    uint8_t* pbase = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.pool)) +
+                     ((int64_t)page * a.page_elems + ((int64_t)a.layer * a.hkv + hk) * 2 * BS * D +
+                      (int64_t)tn * D) * ES;
+    if (col == tn) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int64_t off = (32 * c + 8 * grp) * ES;
+        u.k[c] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k_new) + row + off);
+        *reinterpret_cast<uint4*>(pbase + off) = u.k[c];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < VL; ++r) {
+      const int f = r * kWave + lane;
+      if (f / VCH == tn) {
+        const int64_t off = (f % VCH) * 16;
+        u.v[r] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v_new) + row + off);
+        *reinterpret_cast<uint4*>(pbase + (int64_t)BS * D * ES + off) = u.v[r];
+      }
+    }
+  }
+
   // Balanced schedule: items are kv heads; slot k holds the group's records
   // k * group .. k * group + group - 1.
   __device__ inline void finish_slot(int s, int hk, bool whole, int64_t slot) {
@@ -324,8 +355,10 @@ __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
   w.begin(s, hk);
   page_pipeline<U, Tile>(
       npg, [&](int i, Tile& t) { return w.load(__builtin_amdgcn_readlane(my_page, i), s, pg0 + i, hk, t); },
-      [&](int i, const Tile& t, bool ok) {
-        if (ok) w.page(t, min(kBlock, tok_end - (pg0 + i) * kBlock));
+      [&](int i, Tile& t, bool ok) {
+        const int nv = min(kBlock, tok_end - (pg0 + i) * kBlock);
+        if (pg0 + i == (ctx - 1) / kBlock) w.patch_last(t, nv, s, hk, __builtin_amdgcn_readlane(my_page, i), ok);
+        if (ok) w.page(t, nv);
       });
   w.finish(s, hk, nsplit == 1, ((int64_t)s * a.hq + hk * a.group) * a.max_splits + split, a.max_splits);
 }

@@ -144,7 +144,7 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // units are peeled.  load(i, tile) issues the loads of page i and returns
 // whether page i's table entry is a valid page; pages past npg load page
 // npg-1 again and are not used.  proc(i, tile, ok) is called for every page
-// in order.
+// in order and may modify the tile (it is not used afterwards).
 template <int U, class Tile, class LoadF, class ProcF>
 __device__ inline void page_pipeline(int npg, LoadF&& load, ProcF&& proc) {
   Tile ta[U], tb[U];

@@ -171,7 +171,7 @@ __device__ inline void sched_run(const AttnArgs& a, const SchedLds& L, int X, Wv
             return w.load(__builtin_amdgcn_readlane(lpage, i), __builtin_amdgcn_readlane(ls, i),
                           __builtin_amdgcn_readlane(lp, i), __builtin_amdgcn_readlane(lx, i), t);
         },
-        [&](int i, const Tile& t, bool ok) {
+        [&](int i, Tile& t, bool ok) {
           const int s = __builtin_amdgcn_readlane(ls, i);
           const int x = __builtin_amdgcn_readlane(lx, i);
           const int p = __builtin_amdgcn_readlane(lp, i);
@@ -185,6 +185,7 @@ __device__ inline void sched_run(const AttnArgs& a, const SchedLds& L, int X, Wv
             w.begin(s, x);
           }
           cplast = p;
+          if (p == cP - 1) w.patch_last(t, __builtin_amdgcn_readlane(lnv, i), s, x, __builtin_amdgcn_readlane(lpage, i), ok);
           if (ok) w.page(t, __builtin_amdgcn_readlane(lnv, i));
         });
   }

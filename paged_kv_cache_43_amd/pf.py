@@ -78,6 +78,8 @@ _SIGS = {
     "pf_attention_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
     "pf_paged_decode_attention": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
                                          ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
+    "pf_paged_decode_attention_append": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                                ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
     "pf_contiguous_decode_attention": (_i32, [_vp, _vp, _i32, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
                                               ctypes.c_int64, _i32, _vp, _i32, _i32, ctypes.c_float, _vp,
                                               _i32, _vp, _sz, _vp]),
@@ -344,6 +346,15 @@ def pf_paged_decode_attention(pool, layer, q, num_q_heads, bt_dev, max_blocks, c
                                          _dev(ctx_dev), n, max_context_len, float(scale), _dev(out),
                                          DTYPES.get(out_dtype, out_dtype), _dev(workspace),
                                          workspace_bytes, _stream(stream))
+
+
+def pf_paged_decode_attention_append(pool, layer, q, num_q_heads, k_new, v_new, bt_dev, max_blocks, ctx_dev,
+                                     n, max_context_len, scale, out, out_dtype, workspace, workspace_bytes,
+                                     stream=None):
+    return lib.pf_paged_decode_attention_append(pool, layer, _dev(q), num_q_heads, _dev(k_new), _dev(v_new),
+                                                _dev(bt_dev), max_blocks, _dev(ctx_dev), n, max_context_len,
+                                                float(scale), _dev(out), DTYPES.get(out_dtype, out_dtype),
+                                                _dev(workspace), workspace_bytes, _stream(stream))
 
 
 def pf_contiguous_decode_attention(pool, q, num_q_heads, k, v, seq_stride, token_stride, head_stride,

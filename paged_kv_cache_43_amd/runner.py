@@ -134,6 +134,17 @@ class PagedKV:
                                           out_dtype or self.w.dtype, self.ws, self.ws_bytes, stream)
         pf.check(st, "pf_paged_decode_attention")
 
+    def attention_append(self, layer, q, k_new, v_new, out, max_ctx, out_dtype=None, scale=0.0, stream=None,
+                         hq=None):
+        """Fused form: each sequence's newest token (position ctx-1), K/V
+        ``k_new`` / ``v_new`` [n][H][D], written and attended in one launch."""
+        hq = hq or self.w.hq
+        self.ensure_workspace(max_ctx, hq)
+        st = pf.pf_paged_decode_attention_append(self.h, layer, q, hq, k_new, v_new, self.bt, self.max_blocks,
+                                                 self.ctx, self.w.n, max_ctx, scale, out,
+                                                 out_dtype or self.w.dtype, self.ws, self.ws_bytes, stream)
+        pf.check(st, "pf_paged_decode_attention_append")
+
     def contiguous_attention(self, k, v, q, out, max_ctx, out_dtype=None, scale=0.0, stream=None, hq=None):
         """pf_contiguous_decode_attention over k, v viewed as [n][max_len][H][D]
         (any strides with the last dimension dense: the gather output, or a

@@ -16,11 +16,13 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("fused", [False, True, "append"])
 @pytest.mark.parametrize("name,steps", [("tiny", 40), ("gpt2", 12), ("gqa", 3)])
 def test_decode_loop_matches_oracle(name, steps, fused):
     """fused=False: pf_export_tables then pf_scatter_kv per layer;
-    fused=True: pf_decode_prepare (one launch for both)."""
+    fused=True: pf_decode_prepare (one launch for both); fused="append":
+    pf_export_tables, then per layer the newest token is written by the
+    attention launch itself (pf_paged_decode_attention_append)."""
     print("decode loop", name, "fused" if fused else "separate", flush=True)
     from paged_kv_cache_43_amd import pf, runner
     w = inputs.Workload(name, frames="shuffled")
@@ -47,12 +49,12 @@ def test_decode_loop_matches_oracle(name, steps, fused):
         nv = inputs.normal_bits(rng, (w.layers, w.n, w.hkv, w.d), w.dtype)
         q = inputs.normal_bits(rng, (w.layers, w.n, w.hq, w.d), w.dtype)
         qd = runner.bits_to_device(q)
-        if fused:
+        if fused is True:
             kv.decode_prepare(runner.bits_to_device(nk), runner.bits_to_device(nv))
         else:
             kv.export_tables()
         for l in range(w.layers):
-            if not fused:
+            if fused is False:
                 kv.scatter(l, runner.bits_to_device(nk[l]), runner.bits_to_device(nv[l]), tok_seq, kv.last_pos)
             for s in range(w.n):
                 hist_k[s][l] = np.concatenate([hist_k[s][l], nk[l, s][None]])
@@ -62,8 +64,14 @@ def test_decode_loop_matches_oracle(name, steps, fused):
         rows, mlens = model.block_tables(list(range(w.n)), kv.max_blocks)
         assert np.array_equal(kv.bt.cpu().numpy(), np.array(rows, dtype=np.int32))
         assert list(kv.ctx.cpu().numpy()) == mlens
-        for l in check_layers:
-            kv.attention(l, qd[l], out, int(lens.max()), out_dtype="f32")
+        for l in (range(w.layers) if fused == "append" else check_layers):
+            if fused == "append":
+                kv.attention_append(l, qd[l], runner.bits_to_device(nk[l]), runner.bits_to_device(nv[l]), out,
+                                    int(lens.max()), out_dtype="f32")
+                if l not in check_layers:
+                    continue
+            else:
+                kv.attention(l, qd[l], out, int(lens.max()), out_dtype="f32")
             torch.cuda.synchronize()
             got = out.cpu().numpy().astype(np.float64)
             qq = oa.decode_bits(q[l], w.dtype)
