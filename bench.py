@@ -474,6 +474,63 @@ def run_block_sweep(names, blocks, reps):
     return out
 
 
+def run_fused(names, steps):
+    """Fused scatter + attention (PageForge, "Five techniques": a decode step's
+    per-layer scatter launches are the cost to remove).  One decode step as a
+    model runs it, layer by layer with the new token's K/V known only at its
+    layer: table upload, then per layer either pf_scatter_kv + attention
+    ("separate") or the fused pf_paged_decode_attention_append ("fused").
+    Cache flushed before each step (outside the events); mean step time over
+    ``steps`` steps, sequences growing one token per step."""
+    import torch
+    from paged_kv_cache_43_amd import inputs, pf, runner
+
+    fl = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name in names:
+        row = {}
+        for mode in ("separate", "fused"):
+            w = inputs.Workload(name, frames="shuffled")
+            kv = runner.PagedKV(w, sentinel=False, extra_tokens=steps + 4)
+            q = runner.fill_workload(kv)
+            rng = np.random.default_rng(5)
+            nk = runner.bits_to_device(inputs.normal_bits(rng, (w.layers, w.n, w.hkv, w.d), w.dtype))
+            nv = runner.bits_to_device(inputs.normal_bits(rng, (w.layers, w.n, w.hkv, w.d), w.dtype))
+            out = torch.empty((w.n, w.hq, w.d), dtype=torch.int32 if w.es == 4 else torch.int16, device="cuda")
+            ids = np.arange(w.n, dtype=np.uint64)
+            base = w.ctx.astype(np.int64)
+            kv.ensure_workspace(int(base.max()) + steps + 2)
+            seq = torch.arange(w.n, dtype=torch.int32, device="cuda")
+            times = []
+            for t in range(steps + 2):
+                lens = (base + t + 1).astype(np.int32)
+                pf.check(pf.pf_alloc_for_seqs(kv.h, ids, lens)[0])
+                mc = int(lens.max())
+                fl.amax()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                kv.export_tables()
+                for l in range(w.layers):
+                    if mode == "separate":
+                        kv.scatter(l, nk[l], nv[l], seq, kv.last_pos)
+                        kv.attention(l, q[l], out, mc)
+                    else:
+                        kv.attention_append(l, q[l], nk[l], nv[l], out, mc)
+                b.record()
+                torch.cuda.synchronize()
+                if t >= 2:
+                    times.append(a.elapsed_time(b))
+            row[mode + "_ms_per_step"] = round(float(np.mean(times)), 4)
+            kv.close()
+            del kv, q
+            torch.cuda.empty_cache()
+        row["layers"] = w.layers
+        row["saved_us_per_layer"] = round((row["separate_ms_per_step"] - row["fused_ms_per_step"]) * 1e3 / w.layers, 2)
+        row["speedup"] = round(row["separate_ms_per_step"] / row["fused_ms_per_step"], 4)
+        res[name] = row
+    return res
+
+
 def cpu_baseline(name, budget_s):
     """The CPU fp64 oracle (contiguous two-pass softmax attention on decoded
     K/V) on the same workload, single thread: whole passes over every
@@ -541,6 +598,8 @@ def main():
     ap.add_argument("--twin", default="13b,gqa",
                     help="comma list of configs for the paged vs contiguous-cache comparison (shuffled frames)")
     ap.add_argument("--twin-reps", type=int, default=20)
+    ap.add_argument("--fused", default="gpt2,mixed,13b,gqa",
+                    help="comma list of configs for the fused scatter + attention comparison")
     ap.add_argument("--block-sweep", default="13b,gqa",
                     help="comma list of configs for the page-size sweep (8, 16, 32, 64 tokens per page)")
     ap.add_argument("--swap", choices=["on", "off"], default="on",
@@ -630,6 +689,9 @@ def main():
         line["cow_prefix_sharing"] = run_cow(16, 4, 20)
     if args.swap == "on":
         line["swap"] = run_swap(16, 10)
+    fused = [x for x in args.fused.split(",") if x]
+    if fused:
+        line["fused_scatter_attention"] = run_fused(fused, 10)
     sweep = [x for x in args.block_sweep.split(",") if x]
     if sweep:
         line["block_size_sweep"] = run_block_sweep(sweep, (8, 16, 32, 64), 15)
