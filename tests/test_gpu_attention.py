@@ -286,3 +286,21 @@ def test_invalid_entries_grouped_heads(block, drops):
             ref = oa.attention(qd[s, h], K[:, h // 2], V[:, h // 2], oa.default_scale(64))
             assert np.max(np.abs(got[s, h] - ref)) <= gu.ATOL, (s, h)
     kv.close()
+
+
+@pytest.mark.parametrize("n", [2048, 2049, 3000])
+@pytest.mark.parametrize("dtype,hq,hkv", [("f16", 2, 2), ("bf16", 8, 2)])
+def test_many_sequences(n, dtype, hq, hkv):
+    """Up to 2048 sequences the balanced schedule holds every length in LDS;
+    beyond that the automatic plan switches to fixed splits.  Both against the
+    oracle; the plan is as stated."""
+    print("many sequences", n, dtype, hq, hkv, flush=True)
+    from paged_kv_cache_43_amd import pf
+    lens = np.random.default_rng(n).integers(1, 120, size=n).tolist()
+    w = _custom(lens, hq=hq, hkv=hkv, d=64, dtype=dtype, seed=n % 97)
+    got, kv, q = _run(w, out_dtype="f32")
+    waves = pf.pf_attention_waves(kv.h, w.n, hq, int(max(lens)))
+    assert (waves > 0) == (n <= 2048)
+    ref = gu.oracle_attention_contiguous(w, 0)
+    gu.assert_close(got, ref, "f32", "n=%d" % n)
+    kv.close()

@@ -161,3 +161,87 @@ def test_beams_share_prompt_and_decode(dtype, hq, hkv, d):
         assert pf.pf_free_seq(h, s) == pf.PF_OK
     assert pf.pf_free_pages(h) == P and all(pf.pf_page_refcount(h, p) == 0 for p in range(P))
     pf.pf_pool_destroy(h)
+
+
+def _bits16(gen, shape):
+    return torch.randn(shape, generator=gen, device="cuda").half().view(torch.int16)
+
+
+def test_full_size_shared_equals_private_and_swap_round_trip():
+    """The bench's copy-on-write shape (16 prompts x beam 4, lengths
+    U[256,2048], 40 heads, d_head 128, fp16): attention over the aliased
+    tables returns the same bits as over private copies of the prompts, and
+    the same bits again after every sequence is swapped out and back in
+    (other pages, same values); sampled rows against the oracle."""
+    print("full-size shared / private / swap", flush=True)
+    from paged_kv_cache_43_amd import pf
+    L, H, D, B, prompts, beam = 1, 40, 128, 16, 16, 4
+    rng = np.random.default_rng(43)
+    lens = rng.integers(256, 2049, size=prompts)
+    n = prompts * beam
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(43)
+    kp = [_bits16(gen, (int(x), H, D)) for x in lens]
+    vp = [_bits16(gen, (int(x), H, D)) for x in lens]
+    q = _bits16(gen, (n, H, D))
+    P = int(sum(-(-int(x) // B) for x in lens)) * beam + 64
+    pools = {}
+    for shared in (True, False):
+        h, pool = _pool(P, L, H, D, "f16", rng.permutation(P).astype(np.int32))
+        for p in range(prompts):
+            owners = [p * beam] if shared else [p * beam + b for b in range(beam)]
+            for s in owners:
+                pf.check(pf.pf_alloc_for_seq(h, s, int(lens[p]))[0])
+                st, bt, _ = pf.pf_block_tables(h, [s], 128)
+                m = int(lens[p])
+                pf.check(pf.pf_scatter_kv(h, 0, kp[p], vp[p], torch.zeros(m, dtype=torch.int32, device="cuda"),
+                                          torch.arange(m, dtype=torch.int32, device="cuda"), m,
+                                          torch.from_numpy(bt).cuda(), 1, 128))
+            if shared:
+                for b in range(1, beam):
+                    pf.check(pf.pf_fork_seq(h, p * beam, p * beam + b))
+        pools[shared] = (h, pool)
+    ids = np.arange(n, dtype=np.uint64)
+    mc = int(lens.max())
+    mb = -(-mc // B)
+
+    def attend(h):
+        st, bt, ln = pf.pf_block_tables(h, ids, mb)
+        pf.check(st)
+        need = pf.pf_attention_workspace_bytes(h, n, H, mc)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        out = torch.empty((n, H, D), dtype=torch.float32, device="cuda")
+        pf.check(pf.pf_paged_decode_attention(h, 0, q, H, torch.from_numpy(bt).cuda(),
+                                              mb, torch.from_numpy(ln.astype(np.int32)).cuda(), n, mc, 0.0,
+                                              out, "f32", ws, need))
+        torch.cuda.synchronize()
+        return out
+
+    o_shared = attend(pools[True][0])
+    o_private = attend(pools[False][0])
+    assert torch.equal(o_shared, o_private)
+    # swap every sequence of the shared pool out and back in
+    h = pools[True][0]
+    pb = pf.pf_page_bytes(h)
+    slots = int(sum(-(-int(x) // B) for x in lens)) * beam
+    host = torch.zeros(slots * pb // 2, dtype=torch.int16).pin_memory()
+    pf.check(pf.pf_swap_bind(h, host, slots * pb, slots))
+    # one staging buffer per call: a call's pair list is read by its kernel when the kernel runs
+    st_out = torch.zeros(2 * slots, dtype=torch.int32).pin_memory()
+    st_in = torch.zeros(2 * slots, dtype=torch.int32).pin_memory()
+    pf.check(pf.pf_swap_out(h, ids, st_out, 2 * slots))
+    assert pf.pf_free_pages(h) == P
+    pf.check(pf.pf_swap_in(h, ids, st_in, 2 * slots))
+    torch.cuda.synchronize()
+    assert torch.equal(attend(h), o_shared)
+    # sampled rows against the oracle
+    qb = q.cpu().numpy().view(np.uint16)
+    got = o_shared.cpu().numpy().astype(np.float64)
+    for s, hh in ((0, 0), (17, 5), (63, 39)):
+        p = s // beam
+        K = oa.decode_bits(kp[p].cpu().numpy().view(np.uint16), "f16")
+        V = oa.decode_bits(vp[p].cpu().numpy().view(np.uint16), "f16")
+        ref = oa.attention(oa.decode_bits(qb[s, hh], "f16"), K[:, hh], V[:, hh], oa.default_scale(D))
+        assert np.max(np.abs(got[s, hh] - ref)) <= gu.ATOL
+    for shared in (True, False):
+        pf.pf_pool_destroy(pools[shared][0])
