@@ -203,6 +203,15 @@ int pf_free_seq(pf_pool* pool, uint64_t seq_id);
 /* Pages currently on the free stack (-1 for a NULL handle). */
 int32_t pf_free_pages(const pf_pool* pool);
 
+/* Most pages in use at once since the handle was created or the peak was last
+ * reset (PageFault, "Project layout": the host free list records its peak;
+ * PageForge, "Does the pool actually come back to zero?": a batch's paged peak
+ * against the naive reservation).  -1 for a NULL handle. */
+int32_t pf_pool_peak_pages(const pf_pool* pool);
+
+/* Restart the peak from the pages in use now.  Errors: PF_ERR_INVALID. */
+int pf_pool_reset_peak(pf_pool* pool);
+
 /* Number of live sequences, resident or swapped out (-1 for a NULL handle). */
 int32_t pf_num_seqs(const pf_pool* pool);
 

@@ -26,6 +26,10 @@ Readings where the pages are silent:
   holds no random number generator.
 * ``alloc(seq, new_len)`` takes the sequence's new total length; a new id
   creates the entry; a shorter length is invalid; on OOM nothing changes.
+* Peak (PageFault, "Project layout": the host free list records its peak;
+  PageForge, "Does the pool actually come back to zero?": the paged peak of a
+  batch against the naive reservation): the largest number of pages in use
+  at any moment since the pool was made or the peak was last reset.
 
 Copy-on-write sharing (PagedAttention blog, "Copy-on-Write for Parallel
 Sampling"): several tables may hold the same physical page; a reference count
@@ -93,6 +97,7 @@ class AllocModel:
         self.tables = {}
         self.lengths = {}
         self.refs = [0] * num_pages
+        self.peak = 0                 # most pages in use at once (see reset_peak)
         self.slot_stack = []          # host swap slots, top at the end
         self.num_slots = 0
         self.swapped = {}             # seq id -> host slots, in table order
@@ -126,6 +131,7 @@ class AllocModel:
             self.refs[p] = 1
         self.tables[seq_id] = table + new_pages
         self.lengths[seq_id] = new_len
+        self._note_peak()
         return OK, need
 
     def fork(self, parent, child):
@@ -174,6 +180,7 @@ class AllocModel:
             table.append(p)
         self.tables[seq_id] = table
         self.lengths[seq_id] = new_len
+        self._note_peak()
         return OK, need, copy
 
     def grow_many(self, entries):
@@ -190,12 +197,13 @@ class AllocModel:
             lens[seq_id] = new_len
         if any(seq_id in self.swapped for seq_id, _ in entries):
             return SWAPPED, [0] * len(entries), []
-        saved = (self.stack[:], {k: v[:] for k, v in self.tables.items()}, dict(self.lengths), self.refs[:])
+        saved = (self.stack[:], {k: v[:] for k, v in self.tables.items()}, dict(self.lengths), self.refs[:],
+                 self.peak)
         counts, copies = [], []
         for seq_id, new_len in entries:
             st, nn, copy = self.grow(seq_id, new_len)
             if st != OK:
-                self.stack, self.tables, self.lengths, self.refs = saved
+                self.stack, self.tables, self.lengths, self.refs, self.peak = saved
                 return st, [0] * len(entries), []
             counts.append(nn)
             if copy is not None:
@@ -275,6 +283,7 @@ class AllocModel:
             for slot in reversed(slots):
                 self.slot_stack.append(slot)
             self.tables[s] = table
+        self._note_peak()
         return OK, copies
 
     # -- queries --------------------------------------------------------------
@@ -289,6 +298,13 @@ class AllocModel:
 
     def refcount(self, page):
         return self.refs[page]
+
+    def _note_peak(self):
+        self.peak = max(self.peak, self.pages_in_use())
+
+    def reset_peak(self):
+        """Restart the peak from the pages in use now."""
+        self.peak = self.pages_in_use()
 
     def pages_in_use(self):
         return self.num_pages - len(self.stack)

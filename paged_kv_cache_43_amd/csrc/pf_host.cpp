@@ -51,6 +51,8 @@ static int32_t pop_page(pf_pool* pool) {
   const int32_t p = pool->stack.back();
   pool->stack.pop_back();
   pool->refs[(size_t)p] = 1;
+  const int32_t used = pool->g.num_pages - (int32_t)pool->stack.size();
+  if (used > pool->peak) pool->peak = used;
   return p;
 }
 
@@ -358,6 +360,19 @@ int32_t pf_free_pages(const pf_pool* pool) {
   if (!pool) return -1;
   std::lock_guard<std::mutex> lk(pool->mu);
   return (int32_t)pool->stack.size();
+}
+
+int32_t pf_pool_peak_pages(const pf_pool* pool) {
+  if (!pool) return -1;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  return pool->peak;
+}
+
+int pf_pool_reset_peak(pf_pool* pool) {
+  if (!pool) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  pool->peak = pool->g.num_pages - (int32_t)pool->stack.size();
+  return PF_OK;
 }
 
 int32_t pf_num_seqs(const pf_pool* pool) {

@@ -25,6 +25,8 @@ struct pf_pool {
   std::vector<int32_t> stack;
   // Per page: how many block tables hold it (0 = free).
   std::vector<int32_t> refs;
+  // Most pages in use at once since creation or pf_pool_reset_peak.
+  int32_t peak = 0;
   std::unordered_map<uint64_t, pf_seq_entry> seqs;
   mutable std::mutex mu;
   // Caller-owned device memory bound with pf_pool_bind.

@@ -59,6 +59,8 @@ _SIGS = {
     "pf_alloc_for_seqs": (_i32, [_vp, ctypes.POINTER(_u64), _pi32, _i32, _pi32]),
     "pf_free_seq": (_i32, [_vp, _u64]),
     "pf_fork_seq": (_i32, [_vp, _u64, _u64]),
+    "pf_pool_peak_pages": (_i32, [_vp]),
+    "pf_pool_reset_peak": (_i32, [_vp]),
     "pf_grow_seqs": (_i32, [_vp, ctypes.POINTER(_u64), _pi32, _i32, _pi32, _pi32, _pi32]),
     "pf_page_refcount": (_i32, [_vp, _i32]),
     "pf_copy_pages": (_i32, [_vp, _vp, _i32, _vp]),
@@ -187,6 +189,14 @@ def pf_alloc_for_seqs(pool, seq_ids, new_lens, n_new_out=None):
 
 def pf_free_seq(pool, seq_id):
     return lib.pf_free_seq(pool, seq_id)
+
+
+def pf_pool_peak_pages(pool):
+    return lib.pf_pool_peak_pages(pool)
+
+
+def pf_pool_reset_peak(pool):
+    return lib.pf_pool_reset_peak(pool)
 
 
 def pf_fork_seq(pool, parent, child):

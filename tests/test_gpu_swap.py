@@ -80,6 +80,7 @@ class Harness:
         assert [pf.pf_page_refcount(self.h, p) for p in range(self.P)] == m.refs
         assert pf.pf_free_pages(self.h) == m.free_pages()
         assert pf.pf_swap_free_slots(self.h) == len(m.slot_stack)
+        assert pf.pf_pool_peak_pages(self.h) == m.peak
 
     def read_back(self):
         pf, runner, m = self.pf, self.runner, self.model

@@ -35,6 +35,7 @@ def _same_state(h, model):
     assert pf.pf_num_seqs(h) == len(ids)
     assert [pf.pf_page_refcount(h, p) for p in range(model.num_pages)] == model.refs
     assert pf.pf_free_pages(h) == model.free_pages()
+    assert pf.pf_pool_peak_pages(h) == model.peak
 
 
 def test_blog_example_tables_and_counts():
@@ -148,6 +149,9 @@ def test_random_sharing_replays_oracle(seed):
         else:
             s = int(rng.choice(live))
             assert pf.pf_free_seq(h, s) == pf.PF_OK and model.free(s) == am.OK
+        if it % 97 == 96:
+            assert pf.pf_pool_reset_peak(h) == pf.PF_OK
+            model.reset_peak()
         model.check_invariants()
         _same_state(h, model)
     for s in sorted(model.tables):

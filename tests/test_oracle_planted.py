@@ -194,6 +194,11 @@ def _swap_copy_off_by_one_page(pool, host, g, pairs, to_host):
     return _orig_swap_copy(pool, host, g, [(a, b + 1 if b + 1 < g.P else b) for a, b in pairs], to_host)
 
 
+class _PeakIsCurrentModel(oracle.alloc_model.AllocModel):
+    def _note_peak(self):
+        self.peak = self.pages_in_use()                         # the current, not the highest
+
+
 MUTANTS = {
     "attention_without_scale": (oracle.attention, "attention", _no_scale),
     "attention_wrong_sign": (oracle.attention, "attention", _wrong_sign),
@@ -216,6 +221,7 @@ MUTANTS = {
     "swap_out_keeps_device_pages": (oracle.alloc_model, "AllocModel", _SwapKeepsPagesModel),
     "swap_in_keeps_slots": (oracle.alloc_model, "AllocModel", _SwapInKeepsSlotsModel),
     "swap_copy_wrong_page": (oracle.layout, "swap_copy", _swap_copy_off_by_one_page),
+    "peak_is_current_use": (oracle.alloc_model, "AllocModel", _PeakIsCurrentModel),
 }
 
 
