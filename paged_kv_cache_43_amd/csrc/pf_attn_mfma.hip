@@ -160,11 +160,11 @@ struct MfmaWave {
     const BlockAddr b = block_addr<CONTIG, D, ES, BS>(a, page, s, p, hk);
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      t.k[c] = *reinterpret_cast<const uint4*>(b.k + col * b.tok + (32 * c + 8 * grp) * ES);
+      t.k[c] = load16_stream(b.k + col * b.tok + (32 * c + 8 * grp) * ES);
 #pragma unroll
     for (int r = 0; r < VL; ++r) {
       const int f = r * kWave + lane;  // token f / VCH, 16-byte chunk f % VCH
-      t.v[r] = *reinterpret_cast<const uint4*>(b.v + (f / VCH) * b.tok + (f % VCH) * 16);
+      t.v[r] = load16_stream(b.v + (f / VCH) * b.tok + (f % VCH) * 16);
     }
     return b.ok;
   }
@@ -176,12 +176,12 @@ struct MfmaWave {
     const BlockAddr b1 = block_addr<CONTIG, D, ES, BS>(a, page1, s, 0, hk);
     const uint8_t* kb = (col < BS ? b0.k : b1.k) + (col % BS) * b0.tok;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) t.k[c] = *reinterpret_cast<const uint4*>(kb + (32 * c + 8 * grp) * ES);
+    for (int c = 0; c < KC; ++c) t.k[c] = load16_stream(kb + (32 * c + 8 * grp) * ES);
 #pragma unroll
     for (int r = 0; r < VL; ++r) {
       const int f = r * kWave + lane;
       const int tok = f / VCH;
-      t.v[r] = *reinterpret_cast<const uint4*>((tok < BS ? b0.v : b1.v) + (tok % BS) * b0.tok + (f % VCH) * 16);
+      t.v[r] = load16_stream((tok < BS ? b0.v : b1.v) + (tok % BS) * b0.tok + (f % VCH) * 16);
     }
     t.okm = (b0.ok ? 1u : 0u) | (b1.ok ? 2u : 0u);
     return b0.ok || b1.ok;
