@@ -91,7 +91,8 @@ def run_gpu(args, name, frames, steps, warmup, flush):
 
     dev = "cuda"
     w = inputs.Workload(name, frames=frames)
-    kv = runner.PagedKV(w, device=dev, sentinel=False, extra_tokens=2 * steps + warmup + 1)
+    ksteps = min(steps, 20)
+    kv = runner.PagedKV(w, device=dev, sentinel=False, extra_tokens=steps + ksteps + warmup + 1)
     q = runner.fill_workload(kv, device=dev)
     stream = torch.cuda.current_stream()
     rng = np.random.default_rng(123)
@@ -101,21 +102,27 @@ def run_gpu(args, name, frames, steps, warmup, flush):
                         device=dev)
     ids = np.arange(w.n, dtype=np.uint64)
     base = w.ctx.astype(np.int64)
-    total_steps = warmup + 2 * steps   # warmup, K timed steps, K steps with kernel events
+    # warmup, K timed steps (step events only), min(K, 20) steps with events
+    # around every partition kernel; then, at the final lengths, attention calls
+    # alone with events around each (partition + merge)
+    total_steps = warmup + steps + ksteps
+    attn_iters = max(50, steps)
     max_ctx_final = int(base.max()) + total_steps
     kv.ensure_workspace(max_ctx_final)
     flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev) if flush else None
     ev_a = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
     ev_b = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(total_steps)]
+    ev_c = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(attn_iters + 5)]
+    ev_d = [[torch.cuda.Event(enable_timing=True) for _ in range(w.layers)] for _ in range(attn_iters + 5)]
     ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(total_steps)]
-    for row in ev_a + ev_b:
+    for row in ev_a + ev_b + ev_c + ev_d:
         for e in row:
             e.record(stream)   # creates the underlying hipEvent_t
     torch.cuda.synchronize()
     ctx_per_step = []
 
-    def step(t, events):
+    def step(t, events, kernel_events=False):
         new_lens = (base + t + 1).astype(np.int32)
         st, _ = pf.pf_alloc_for_seqs(kv.h, ids, new_lens)
         pf.check(st, "pf_alloc_for_seqs")
@@ -126,33 +133,48 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         kv.decode_prepare(newk, newv)          # tables + every layer's new token, one launch
         mc = int(new_lens.max())
         for layer in range(w.layers):
-            if events:
+            if kernel_events:
                 pf.check(pf.pf_pool_set_timing_events(kv.h, ev_a[t][layer].cuda_event,
                                                       ev_b[t][layer].cuda_event))
             kv.attention(layer, q[layer], out_t[layer], mc)
-        if events:
+        if kernel_events:
             pf.check(pf.pf_pool_set_timing_events(kv.h, None, None))
+        if events:
             ev_step[t][1].record(stream)
         ctx_per_step.append(new_lens.astype(np.int64))
 
     for t in range(warmup):
         step(t, False)
     torch.cuda.synchronize()
-    # the K timed steps: no events in the stream
+    # the K timed steps: only the step's own pair of events in the stream
+    # (and none at all without --flush, where the wall clock times them)
     t0 = time.perf_counter()
     for t in range(warmup, warmup + steps):
         step(t, flush)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # K more steps with HIP events around every partition kernel (roofline)
+    # more steps with HIP events around every partition kernel (roofline)
     for t in range(warmup + steps, total_steps):
-        step(t, True)
+        step(t, True, kernel_events=True)
+    torch.cuda.synchronize()
+    # attention calls alone at the final lengths: 5 untimed, then attn_iters
+    # with events around each layer's call (partition + merge), flushed first
+    mc = int(ctx_per_step[-1].max())
+    for r in range(attn_iters + 5):
+        if flush:
+            flush_buf.amax()
+        for layer in range(w.layers):
+            ev_c[r][layer].record(stream)
+            kv.attention(layer, q[layer], out_t[layer], mc)
+            ev_d[r][layer].record(stream)
     torch.cuda.synchronize()
 
     timed = range(warmup, warmup + steps)
     evsteps = range(warmup + steps, total_steps)
     step_ms = [ev_step[t][0].elapsed_time(ev_step[t][1]) for t in (timed if flush else evsteps)]
     part_ms = [ev_a[t][l].elapsed_time(ev_b[t][l]) for t in evsteps for l in range(w.layers)]
+    attn_ms = [ev_c[r][l].elapsed_time(ev_d[r][l]) for r in range(5, attn_iters + 5) for l in range(w.layers)]
+    attn_call_bytes = [alg_bytes_attention(ctx_per_step[-1], w, w.es)] * len(attn_ms)
     attn_bytes = [alg_bytes_attention(ctx_per_step[t], w, w.es) for t in timed]
     part_bytes = [alg_bytes_attention(ctx_per_step[t], w, w.es) for t in evsteps]
     step_bytes = [b * w.layers + alg_bytes_scatter(w) * w.layers for b in attn_bytes]
@@ -173,6 +195,16 @@ def run_gpu(args, name, frames, steps, warmup, flush):
     avg_attn_bytes = float(np.mean(part_bytes))
     part_avg_ms = float(np.mean(part_ms))
     achieved = avg_attn_bytes / (part_avg_ms * 1e-3) / 1e9
+    attn_med_ms = float(np.median(attn_ms))
+    attention = {
+        "what": "attention calls alone at the final lengths (partition + merge kernels), events around each "
+                "layer's call, cache flushed before each iteration; 5 untimed first",
+        "launches": len(attn_ms), "median_us": round(attn_med_ms * 1e3, 2),
+        "mean_us": round(float(np.mean(attn_ms)) * 1e3, 2), "sd_us": round(float(np.std(attn_ms)) * 1e3, 2),
+        "min_us": round(float(np.min(attn_ms)) * 1e3, 2),
+        "kv_GBps": round(float(np.median(attn_call_bytes)) / (attn_med_ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(float(np.median(attn_call_bytes)) / (attn_med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 1),
+        "seqs_per_ms": round(w.n / (attn_med_ms * w.layers), 2)}
     return dict(
         w=w, name=name, frames=frames, ms_step=ms_step, ms_step_wall=ms_step_wall,
         ms_step_events=ms_step_events, value=avg_step_bytes / (ms_step * 1e-3) / 1e9,
@@ -180,7 +212,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         part_med_us=float(np.median(part_ms)) * 1e3, part_min_us=float(np.min(part_ms)) * 1e3,
         part_sd_us=float(np.std(part_ms)) * 1e3,
         attn_bytes=avg_attn_bytes, achieved=achieved, split=split, waves=waves, mfma=bool(mfma),
-        kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers))
+        kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers), attention=attention)
 
 
 def run_twin(name, frames, reps):
@@ -531,10 +563,56 @@ def run_fused(names, steps):
     return res
 
 
-def cpu_baseline(name, budget_s):
+def _oracle_pass_worker(barrier, results, wid, dtype, hq, hkv, d, qb, ks, vs, budget_s):
+    """One worker of the all-cores oracle leg: whole passes of the fp64 oracle
+    over its share of the sequences (q bits [m][hq][d], K/V bits per sequence
+    [ctx][hkv][d]) until budget_s seconds are spent, one BLAS thread."""
+    sys.path.insert(0, ROOT)
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        pass
+    import oracle.attention as oa
+    qd = oa.decode_bits(qb, dtype)
+    g, sc = hq // hkv, oa.default_scale(d)
+    barrier.wait()
+    t0 = time.perf_counter()
+    done = tokens = 0
+    while True:
+        for s in range(len(ks)):
+            K = oa.decode_bits(ks[s], dtype)
+            V = oa.decode_bits(vs[s], dtype)
+            for h in range(hq):
+                oa.attention(qd[s, h], K[:, h // g, :], V[:, h // g, :], sc)
+            done += 1
+            tokens += len(ks[s])
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    results.put((wid, done, tokens, time.perf_counter() - t0))
+
+
+def host_description():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": aff}
+
+
+def cpu_baseline(name, budget_s, max_workers=16):
     """The CPU fp64 oracle (contiguous two-pass softmax attention on decoded
-    K/V) on the same workload, single thread: whole passes over every
-    sequence of layer 0, repeated until about budget_s seconds are spent."""
+    K/V) on the same workload, layer 0, all query heads.  Headline: the
+    sequences split across worker processes, one per usable core (at most
+    max_workers), each repeating whole passes over its share for a bounded
+    time; also one thread alone, whole passes over every sequence until about
+    budget_s seconds are spent."""
+    import multiprocessing as mp
     from paged_kv_cache_43_amd import inputs
     import oracle.attention as oa
     try:
@@ -547,8 +625,11 @@ def cpu_baseline(name, budget_s):
     qd = oa.decode_bits(qb[0], w.dtype)
     g = w.hq // w.hkv
     sc = oa.default_scale(w.d)
+    wl = type("W", (), dict(hq=w.hq, hkv=w.hkv, d=w.d, es=w.es))
+
+    # one thread, whole passes over all sequences
     t0 = time.perf_counter()
-    done = 0      # sequences attended, over all passes
+    done = 0
     while True:
         for s in range(w.n):
             K = oa.decode_bits(ks[s][0], w.dtype)
@@ -565,13 +646,45 @@ def cpu_baseline(name, budget_s):
     if limiter is not None and hasattr(limiter, "unregister"):
         limiter.unregister()
     full, part = divmod(done, w.n)
-    ctx = np.concatenate([np.tile(w.ctx, full), w.ctx[:part]])
-    b = alg_bytes_attention(ctx, type("W", (), dict(n=done, hq=w.hq, hkv=w.hkv, d=w.d, es=w.es))(), w.es)
-    return {"value": round(b / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seqs_per_ms": round(done / (el * 1e3), 5), "seconds": round(el, 2),
-            "sample": "%d sequence-attentions (%d whole passes over all %d sequences, %d context tokens each "
-                      "pass), layer 0, all %d query heads; decode + fp64 two-pass softmax attention, one thread"
-                      % (done, full, w.n, int(w.ctx.sum()), w.hq)}
+    ctx1 = np.concatenate([np.tile(w.ctx, full), w.ctx[:part]])
+    wl.n = done
+    one = {"value": round(alg_bytes_attention(ctx1, wl, w.es) / el / 1e9, 4), "cores": 1,
+           "seqs_per_ms": round(done / (el * 1e3), 5), "seconds": round(el, 2),
+           "sample": "%d sequence-attentions (%d whole passes over all %d sequences, %d context tokens each "
+                     "pass), one thread" % (done, full, w.n, int(w.ctx.sum()))}
+
+    # all usable cores: sequences dealt round-robin to worker processes
+    # (started fresh, not forked from this process), timed from a common barrier
+    host = host_description()
+    nw = max(1, min(max_workers, host["affinity_cpus"] or 1, w.n))
+    per_worker_s = max(1.0, 24.0 / nw)
+    ctx = mp.get_context("spawn")
+    barrier, results = ctx.Barrier(nw), ctx.Queue()
+    procs = []
+    for k in range(nw):
+        idx = list(range(k, w.n, nw))
+        procs.append(ctx.Process(target=_oracle_pass_worker, args=(
+            barrier, results, k, w.dtype, w.hq, w.hkv, w.d, np.ascontiguousarray(qb[0][idx]),
+            [ks[s][0] for s in idx], [vs[s][0] for s in idx], per_worker_s)))
+    for pr in procs:
+        pr.start()
+    res = [results.get(timeout=600) for _ in procs]
+    for pr in procs:
+        pr.join(timeout=60)
+    secs = max(r[3] for r in res)
+    seqs = sum(r[1] for r in res)
+    bytes_all = 0
+    for wid, dn, toks, _ in res:
+        idx = np.arange(wid, w.n, nw)
+        passes = dn // len(idx)
+        wl.n = dn
+        bytes_all += alg_bytes_attention(np.tile(w.ctx[idx], passes), wl, w.es)
+    return {"value": round(bytes_all / secs / 1e9, 4), "unit": "GB/s", "cores": nw, "kind": "oracle",
+            "seqs_per_ms": round(seqs / (secs * 1e3), 5), "seconds": round(secs, 2),
+            "sample": "%d sequence-attentions in whole passes, the %d sequences dealt round-robin to %d worker "
+                      "processes (one BLAS thread each, %.1f s each, timed from a common barrier), layer 0, all %d "
+                      "query heads; decode + fp64 two-pass softmax attention" % (seqs, w.n, nw, per_worker_s, w.hq),
+            "one_core": one, "host": host}
 
 
 def describe(r):
@@ -587,7 +700,7 @@ def describe(r):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="13b", choices=sorted(WORKLOADS))
     ap.add_argument("--frames", default="shuffled", choices=["shuffled", "ordered"])
@@ -641,16 +754,17 @@ def main():
             "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
             "seqs_per_ms": round(r["seqs_per_ms"], 2), "ms_per_step": round(r["ms_step"], 4),
             "attn_partition_avg_us": round(r["part_avg_us"], 2),
-            "attn_partition_GBps": round(r["achieved"], 1), "config": describe(r)}
-    # PageFault's pending "cost of scattering pages": shuffled / ordered attention time
+            "attn_partition_GBps": round(r["achieved"], 1), "attention": r["attention"], "config": describe(r)}
+    # PageFault's pending "cost of scattering pages": shuffled / ordered median
+    # attention time (partition + merge)
     cost = {}
     for name in dict.fromkeys(n for n, _ in runs):
         sh = head if name == args.config else None
         key_s, key_o = "%s_shuffled" % name, "%s_ordered" % name
-        t_s = sh["part_avg_us"] if sh is not None and args.frames == "shuffled" else others.get(key_s, {}).get("attn_partition_avg_us")
-        t_o = others.get(key_o, {}).get("attn_partition_avg_us")
-        if t_s and t_o:
-            cost[name] = round(t_s / t_o, 3)
+        a_s = sh["attention"] if sh is not None and args.frames == "shuffled" else others.get(key_s, {}).get("attention")
+        a_o = others.get(key_o, {}).get("attention")
+        if a_s and a_o:
+            cost[name] = round(a_s["median_us"] / a_o["median_us"], 3)
     w = head["w"]
     line = {
         "metric": "paged decode attention KV GB/s (% of MI355X HBM peak) + sequences/ms",
@@ -669,6 +783,7 @@ def main():
         "pct_hbm_peak": round(100 * head["value"] / HBM_PEAK_GBS, 1),
         "seqs_per_ms": round(head["seqs_per_ms"], 2),
         "ms_per_step_wall": round(head["ms_step_wall"], 4),
+        "attention": head["attention"],
         "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.config),
