@@ -212,6 +212,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         part_med_us=float(np.median(part_ms)) * 1e3, part_min_us=float(np.min(part_ms)) * 1e3,
         part_sd_us=float(np.std(part_ms)) * 1e3,
         attn_bytes=avg_attn_bytes, achieved=achieved, split=split, waves=waves, mfma=bool(mfma),
+        whole=bool(split) and split >= max_ctx_final,
         kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers), attention=attention)
 
 
@@ -692,7 +693,8 @@ def describe(r):
     return {"workload": WORKLOADS[r["name"]].format(frames=r["frames"]), "n_seqs": w.n,
             "layers": w.layers, "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": w.d,
             "block_size": 16, "pool_pages": w.num_pages, "frames": r["frames"],
-            "schedule": "balanced" if r["waves"] else "fixed splits",
+            "schedule": "balanced" if r["waves"] else (
+                "whole (sequence, head) items, no merge" if r["whole"] else "fixed splits"),
             "waves": r["waves"] or None, "split_tokens": r["split"] or None,
             "kernel": "mfma" if r["mfma"] else "valu"}
 

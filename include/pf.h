@@ -371,7 +371,9 @@ int pf_contiguous_decode_attention(const pf_pool* pool, const void* q, int32_t n
 typedef enum {
   PF_OPT_SPLIT_TOKENS = 0, /* fixed-split schedule: tokens per split (multiple of B, <= 64 B); 0 = automatic */
   PF_OPT_GQA_MFMA = 1,     /* 1 (default): matrix-core kernel for grouped 16-bit heads; 0: vector kernel */
-  PF_OPT_SCHEDULE = 2,     /* 0 (default): balanced if n <= 2048, else fixed splits; 1: fixed splits;
+  PF_OPT_SCHEDULE = 2,     /* 0 (default): one split per (sequence, head) when max_context_len <= 256
+                              (16-token pages, no split-tokens option set: no merge launch), else
+                              balanced if n <= 2048, else fixed splits; 1: fixed splits;
                               2: balanced (n <= 2048) */
   PF_OPT_WAVES_PER_CU = 3  /* balanced schedule: waves launched per compute unit; 0 = resident capacity */
 } pf_option;

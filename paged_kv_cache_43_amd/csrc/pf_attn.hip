@@ -539,6 +539,10 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
   const int sched = pool->schedule;
   p.balanced = sched == 2 || (sched == 0 && n <= kMaxSeqsBalanced) || g.block_size != kBlock;
   if (n > kMaxSeqsBalanced) p.balanced = false;
+  // short contexts: every (sequence, head) whole in one wave, nothing to merge
+  const bool whole = sched == 0 && g.block_size == kBlock && pool->split_tokens == 0 &&
+                     max_ctx <= kWholeItemTokens;
+  if (whole) p.balanced = false;
   const int ut = g.block_size < kBlock ? g.block_size : kBlock;  // tokens per unit of the walk
   if (p.balanced) {
     // Waves: 8 per CU (two per SIMD), or fewer if the kernel's occupancy is
@@ -569,7 +573,8 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
     p.items = (int64_t)n * p.items_per_seq;
     p.records = (p.items + waves) * p.rows_per_item;
   } else {
-    p.split = grid_split(pool, p.mfma, n, num_q_heads, max_ctx);
+    p.split = whole ? (max_ctx <= kBlock ? kBlock : (max_ctx + kBlock - 1) / kBlock * kBlock)
+                    : grid_split(pool, p.mfma, n, num_q_heads, max_ctx);
     p.splits = max_ctx <= 0 ? 1 : (max_ctx + p.split - 1) / p.split;
     p.records = p.splits > 1 ? (int64_t)n * num_q_heads * p.splits : 0;
   }

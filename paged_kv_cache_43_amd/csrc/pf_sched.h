@@ -33,6 +33,12 @@ namespace pf {
 
 constexpr int kSchedThreads = 256;          // four waves per workgroup
 constexpr int kMaxSeqsBalanced = 2048;      // sequences the LDS prefix holds
+// Contexts up to this many tokens are attended one wave per whole (sequence,
+// head) with no split and no merge launch: on MI355X that beat the balanced
+// schedule plus its merge on short contexts (GPT-2 shape, contexts <= 190:
+// 9.7 vs 16.0 us per layer; 4 sequences of <= 64 tokens: 7.2 vs 15.2 us),
+// while from a few hundred tokens on the balanced schedule is faster.
+constexpr int kWholeItemTokens = 256;
 constexpr int kScanPerThread = kMaxSeqsBalanced / kSchedThreads;
 
 struct SchedLds {

@@ -175,6 +175,32 @@ def test_errors_and_all_or_nothing():
     pf.pf_pool_destroy(h)
 
 
+def test_plan_short_contexts_whole_items():
+    """The automatic plan attends contexts of at most 256 tokens one wave per
+    whole (sequence, head): one split of the context rounded up to a page, no
+    partial records, no workspace.  Longer contexts, an explicit schedule or
+    split size, and pages other than 16 tokens keep their own plans."""
+    st, h = pf.pf_pool_create(64, 16, 1, 2, 64, "f16")
+    for mc, split in ((1, 16), (16, 16), (100, 112), (256, 256)):
+        assert pf.pf_attention_waves(h, 4, 2, mc) == 0
+        assert pf.pf_attention_split_tokens(h, 4, 2, mc) == split
+        assert pf.pf_attention_workspace_bytes(h, 4, 2, mc) == 0
+    assert pf.pf_attention_split_tokens(h, 5000, 2, 200) == 208     # beyond 2048 sequences too
+    assert pf.pf_attention_waves(h, 4, 2, 257) > 0                  # longer: balanced
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SCHEDULE, 2) == pf.PF_OK
+    assert pf.pf_attention_waves(h, 4, 2, 100) > 0                  # balanced on request
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SCHEDULE, 0) == pf.PF_OK
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SPLIT_TOKENS, 64) == pf.PF_OK
+    assert pf.pf_attention_waves(h, 4, 2, 200) > 0                  # a split size set: the usual plan
+    assert pf.pf_pool_set_option(h, pf.PF_OPT_SCHEDULE, 1) == pf.PF_OK
+    assert pf.pf_attention_split_tokens(h, 4, 2, 200) == 64
+    assert pf.pf_attention_workspace_bytes(h, 4, 2, 200) > 0
+    pf.pf_pool_destroy(h)
+    st, h = pf.pf_pool_create(64, 8, 1, 2, 64, "f16")
+    assert pf.pf_attention_waves(h, 4, 2, 100) > 0                  # 8-token pages: balanced only
+    pf.pf_pool_destroy(h)
+
+
 def test_contiguous_entry_validates_before_launch():
     """pf_contiguous_decode_attention: the pool (H=1, D=16, f16) gives only the
     geometry and options, so an unbound pool is fine; every bad argument is
