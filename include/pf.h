@@ -234,10 +234,28 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
  * the stream one kernel that copies those n*max_blocks + 2n words to meta_dev
  * (device, 16-byte aligned), reading the pinned memory directly (no DMA
  * engine round trip).  The staging buffer must not be rewritten until the
- * stream has passed this call.  Errors: as pf_block_tables, plus
+ * stream has passed this call.  With PF_OPT_EXPORT_DELTA the table part of
+ * the staging may instead hold (flat index, value) pairs of the entries that
+ * changed since the previous export to meta_dev, and only those entries,
+ * the lengths and the newest positions are written (a decode step changes at
+ * most one entry per sequence).  Errors: as pf_block_tables, plus
  * PF_ERR_INVALID for null or misaligned buffers and PF_ERR_HIP. */
 int pf_export_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
                      int32_t* staging_host, int32_t* meta_dev, void* hip_stream);
+
+/* Host half of pf_export_tables (step = 0) or of pf_decode_prepare's export
+ * (step != 0), with no launch: fill staging_host exactly as that call would
+ * for an export to meta_dev and count the export as made (the next
+ * incremental one builds on it).  meta_dev only names the target for
+ * PF_OPT_EXPORT_DELTA and is not accessed.  *pairs receives -1 when the
+ * staging holds the whole table ([n][max_blocks] at the start), else the
+ * number of (flat index, value) pairs at the start; lengths always at word
+ * n*max_blocks, newest positions at n*max_blocks + n and, with step, the
+ * pages of the newest tokens at n*max_blocks + 2n.  For callers that upload
+ * the staging themselves, and for tests.  Errors: as pf_block_tables, plus
+ * PF_ERR_INVALID for null buffers. */
+int pf_export_staging(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                      const void* meta_dev, int32_t step, int32_t* staging_host, int64_t* pairs);
 
 /* One decode step's host -> device work in one launch: pf_export_tables of
  * seq_ids into meta_dev (same staging layout, followed by [n] destination
@@ -375,7 +393,15 @@ typedef enum {
                               (16-token pages, no split-tokens option set: no merge launch), else
                               balanced if n <= 2048, else fixed splits; 1: fixed splits;
                               2: balanced (n <= 2048) */
-  PF_OPT_WAVES_PER_CU = 3  /* balanced schedule: waves launched per compute unit; 0 = resident capacity */
+  PF_OPT_WAVES_PER_CU = 3, /* balanced schedule: waves launched per compute unit; 0 = resident capacity */
+  PF_OPT_EXPORT_DELTA = 4  /* 0 (default): pf_export_tables / pf_decode_prepare upload the whole table;
+                              1: they upload only the entries that differ from the previous export to
+                              the same meta_dev with the same seq_ids and max_blocks (lengths and
+                              newest positions always).  With 1 the caller promises that meta_dev
+                              is written by nothing else between exports and still holds what the
+                              previous export left there; setting the option (to either value)
+                              forgets the previous export, so set it again after meta_dev is
+                              reallocated or overwritten. */
 } pf_option;
 
 /* Set / read a tuning option of a handle.  Errors: PF_ERR_INVALID. */
@@ -397,6 +423,29 @@ int32_t pf_attention_waves(const pf_pool* pool, int32_t n, int32_t num_q_heads, 
  * stream (hipEvent_t values cast to void*, owned by the caller).  NULL, NULL
  * turns it off.  Errors: PF_ERR_INVALID (NULL handle or only one event). */
 int pf_pool_set_timing_events(pf_pool* pool, void* start_event, void* stop_event);
+
+/* Stream markers: HIP events created without the system-scope cache
+ * writeback and invalidation that default events perform when they are
+ * recorded (hipEventDisableSystemFence).  On MI355X a default event placed
+ * between two kernels adds about 6 us to the stream; these add none of that.
+ * A marker tells the host that the work enqueued before it has run (so, for
+ * instance, pinned staging read by that work may be rewritten) and, if
+ * created with timing, when; it does not make device writes visible to the
+ * host.  The event is returned as a hipEvent_t cast to void* and is owned by
+ * the caller until pf_marker_destroy.
+ *   pf_marker_create: timing != 0 keeps timestamps (for pf_marker_elapsed_ms
+ *                     and pf_pool_set_timing_events).
+ *   pf_marker_record: enqueue on hip_stream (NULL: the null stream).
+ *   pf_marker_wait:   block the host until the marker has been reached.
+ *   pf_marker_elapsed_ms: milliseconds from start to stop, both reached and
+ *                     created with timing.
+ * Errors: PF_ERR_INVALID (NULL event or output), PF_ERR_HIP (the runtime
+ * refused, e.g. a marker never recorded). */
+int pf_marker_create(int32_t timing, void** event);
+int pf_marker_record(void* event, void* hip_stream);
+int pf_marker_wait(void* event);
+int pf_marker_elapsed_ms(void* start, void* stop, float* ms);
+int pf_marker_destroy(void* event);
 
 /* Which attention kernel a call with num_q_heads query heads would use:
  * 1 = matrix-core kernel for grouped heads, 0 = vector kernel, -1 = NULL handle

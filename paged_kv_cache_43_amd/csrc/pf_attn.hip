@@ -284,64 +284,100 @@ __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) 
   sched_run<U, BS>(a, L, a.hq, w, lane);
 }
 
-// Merge the pieces of every output row that was split: M = max m_j,
-// out = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j, summed in piece
-// order (PagedAttention blog, "The Attention Kernel": the final reduction
-// combines partial softmax results with log-sum-exp).  Grid schedule: the
-// row's splits are records row*max_splits + j; balanced schedule: the item's
-// (first record, pieces) pair, records (first + j) * rows_per_item + c.
+// Merge the pieces of output rows that were split (PagedAttention blog, "The
+// Attention Kernel": the final reduction combines partial softmax results
+// with log-sum-exp): with M = max_j m_j and w_j = 2^(m_j - M),
+//   out = sum_j w_j acc_j / sum_j w_j l_j,
+// sums taken in piece order.  Pieces are read in batches of kMergeBatch; a
+// batch that raises M rescales what is summed so far, so with at most
+// kMergeBatch pieces this is the formula above exactly as written.  Record of
+// row c, piece j: rec0 + j * js + c.  Lanes lie across (row, 4-float chunk):
+// D/4 lanes per row, 64/(D/4) rows per pass; this wave does pass `pass`.  All
+// loads of a batch are issued before any is used.
+constexpr int kMergeBatch = 8;
+
+template <class T, bool OUT_F32>
+__device__ inline void store_out4(void* out, int64_t idx, const float* v) {
+  if constexpr (OUT_F32 || T::es == 4) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint2 w;
+    w.x = T::narrow2(v[0], v[1]);
+    w.y = T::narrow2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = w;
+  }
+}
+
+template <class T, bool OUT_F32>
+__device__ inline void merge_rows(const AttnArgs& a, int D, int64_t rec0, int64_t js, int cnt, int rows, int pass,
+                                  int64_t out_row0, int lane) {
+  const int lpr = D / 4;
+  const int c = pass * (kWave / lpr) + lane / lpr;
+  const int q = lane % lpr;
+  if (c >= rows) return;
+  float M = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < cnt; j0 += kMergeBatch) {
+    float2 ml[kMergeBatch];
+    float4 av[kMergeBatch];
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+      if (j0 + b < cnt) {
+        const int64_t rec = rec0 + (int64_t)(j0 + b) * js + c;
+        ml[b] = a.ws_ml[rec];
+        av[b] = *reinterpret_cast<const float4*>(a.ws_acc + rec * D + 4 * q);
+      } else {
+        ml[b] = make_float2(-INFINITY, 0.f);
+        av[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) Mb = fmaxf(Mb, ml[b].x);
+    if (Mb != M) {  // the batch raised the max: rescale the sums so far
+      const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - Mb);
+      den *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] *= alpha;
+      M = Mb;
+    }
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const float wj = ml[b].x == -INFINITY ? 0.f : fast_exp2(ml[b].x - M);
+      den += ml[b].y * wj;
+      num[0] += wj * av[b].x;
+      num[1] += wj * av[b].y;
+      num[2] += wj * av[b].z;
+      num[3] += wj * av[b].w;
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const float o[4] = {num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+  store_out4<T, OUT_F32>(a.out, (out_row0 + c) * D + 4 * q, o);
+}
+
+// One wave per (item or query head, pass, sequence).  Balanced schedule: the
+// item's (first record, pieces) pair, records (first + j) * rows_per_item + c;
+// grid schedule: query head h's splits are records row * max_splits + j.
 template <class T, bool OUT_F32, bool BAL>
 __global__ __launch_bounds__(kWave) void attn_merge_kernel(AttnArgs a, int D, int items_per_seq,
-                                                           int rows_per_item) {
-  const int h = blockIdx.x;
+                                                           int rows_per_item, int passes) {
+  const int x = blockIdx.x / passes;
+  const int pass = blockIdx.x % passes;
   const int s = blockIdx.y;
   const int lane = threadIdx.x;
   const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
   if (ctx == 0) return;
-  int64_t first, stride = 1;
-  int cnt;
-  int c = 0;
   if constexpr (BAL) {
-    const int item = s * items_per_seq + h / rows_per_item;
-    const int2 meta = a.ws_meta[item];
+    const int2 meta = a.ws_meta[(int64_t)s * items_per_seq + x];
     if (meta.y <= 1) return;
-    cnt = meta.y;
-    c = h % rows_per_item;
-    first = (int64_t)meta.x * rows_per_item + c;
-    stride = rows_per_item;
+    merge_rows<T, OUT_F32>(a, D, (int64_t)meta.x * rows_per_item, rows_per_item, meta.y, rows_per_item, pass,
+                           (int64_t)s * a.hq + (int64_t)x * rows_per_item, lane);
   } else {
-    cnt = (ctx + a.split_tokens - 1) / a.split_tokens;
+    const int cnt = (ctx + a.split_tokens - 1) / a.split_tokens;
     if (cnt <= 1) return;
-    first = ((int64_t)s * a.hq + h) * a.max_splits;
+    const int64_t row = (int64_t)s * a.hq + x;
+    merge_rows<T, OUT_F32>(a, D, row * a.max_splits, 1, cnt, 1, 0, row, lane);
   }
-  float M = -INFINITY;
-  for (int j0 = 0; j0 < cnt; j0 += kWave)
-    if (j0 + lane < cnt) M = fmaxf(M, a.ws_ml[first + (j0 + lane) * stride].x);
-  M = group_reduce<kWave, OpMax>(M);
-  float den = 0.f;
-  float num[4] = {0.f, 0.f, 0.f, 0.f};  // dims lane, lane+64, lane+128, lane+192
-  for (int j0 = 0; j0 < cnt; j0 += kWave) {
-    float wj = 0.f;
-    if (j0 + lane < cnt) {
-      const float2 ml = a.ws_ml[first + (j0 + lane) * stride];
-      wj = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - M);
-      den += ml.y * wj;
-    }
-    const int n = min(kWave, cnt - j0);
-    for (int j = 0; j < n; ++j) {
-      const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
-      const float* src = a.ws_acc + (first + (j0 + j) * stride) * D;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (k * kWave + lane < D) num[k] += wgt * src[k * kWave + lane];
-    }
-  }
-  den = group_reduce<kWave, OpSum>(den);
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int64_t out_row = ((int64_t)s * a.hq + h) * D;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    if (k * kWave + lane < D) store_out<T, OUT_F32>(a.out, out_row + k * kWave + lane, num[k] * inv);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -448,13 +484,16 @@ static const void* valu_ptr_dtype(int D) {
 template <class T>
 static void launch_merge(const AttnArgs& a, int D, bool balanced, int items_per_seq, int rows_per_item,
                          hipStream_t st) {
-  const dim3 grid(a.hq, a.n);
+  const int rows = balanced ? rows_per_item : 1;
+  const int rpp = kWave / (D / 4);  // rows per pass of merge_rows
+  const int passes = (rows + rpp - 1) / rpp;
+  const dim3 grid((balanced ? items_per_seq : a.hq) * passes, a.n);
   if (balanced) {
-    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
-    else hipLaunchKernelGGL((attn_merge_kernel<T, false, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
+    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
+    else hipLaunchKernelGGL((attn_merge_kernel<T, false, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
   } else {
-    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
-    else hipLaunchKernelGGL((attn_merge_kernel<T, false, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item);
+    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
+    else hipLaunchKernelGGL((attn_merge_kernel<T, false, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
   }
 }
 
@@ -759,7 +798,6 @@ extern "C" int pf_contiguous_decode_attention(const pf_pool* pool, const void* q
                                               float scale, void* out, int32_t out_dtype, void* workspace,
                                               size_t workspace_bytes, void* hip_stream) {
   if (!pool) return PF_ERR_INVALID;
-  const pf_geometry& g = pool->g;
   if (max_len <= 0 || max_len % kBlock != 0 || max_context_len < 0 || max_context_len > max_len)
     return PF_ERR_INVALID;
   const int64_t es = (int64_t)pool->elem_bytes;

@@ -25,6 +25,7 @@
 // state changes here, the copies are enqueued by pf_swap_out / pf_swap_in
 // (pf_kv.hip) in the same call.  A swapped sequence keeps its length and its
 // slots; it cannot grow, fork or be exported until it is swapped in.
+#include <algorithm>
 #include <cstring>
 #include <limits>
 #include <new>
@@ -139,6 +140,7 @@ int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n
   pf_seq_entry& e = it == pool->seqs.end() ? pool->seqs[seq_id] : it->second;
   e.pages.reserve(want);
   for (size_t i = 0; i < need; ++i) e.pages.push_back(pop_page(pool));
+  if (need) e.ver = ++pool->ver_clock;
   e.len = new_len;
   if (n_new_pages) *n_new_pages = (int32_t)need;
   return PF_OK;
@@ -201,6 +203,7 @@ int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new
     const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
     const size_t need = want - e.pages.size();
     for (size_t j = 0; j < need; ++j) e.pages.push_back(pop_page(pool));
+    if (need) e.ver = ++pool->ver_clock;
     e.len = new_lens[i];
     if (n_new_pages) n_new_pages[i] = (int32_t)need;
   }
@@ -230,6 +233,7 @@ int pf_fork_seq(pf_pool* pool, uint64_t parent, uint64_t child) {
   if (pool->seqs.count(child)) return PF_ERR_INVALID;
   pf_seq_entry copy = it->second;
   for (int32_t p : copy.pages) ++pool->refs[(size_t)p];
+  copy.ver = ++pool->ver_clock;
   pool->seqs.emplace(child, std::move(copy));
   return PF_OK;
 }
@@ -311,6 +315,7 @@ int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens
       e.pages.push_back(pop_page(pool));
       ++taken;
     }
+    if (taken) e.ver = ++pool->ver_clock;
     e.len = new_lens[i];
     if (n_new_pages) n_new_pages[i] = taken;
   }
@@ -414,28 +419,100 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
 
 }  // extern "C"
 
-int pf_fill_meta(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out) {
-  if (!pool || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
-  int32_t* lens = out + (size_t)n * (size_t)max_blocks;
-  const int st = pf_block_tables(pool, seq_ids, n, max_blocks, out, lens);
-  if (st != PF_OK) return st;
-  int32_t* last = lens + n;
-  for (int32_t i = 0; i < n; ++i) last[i] = lens[i] - 1;
-  return PF_OK;
+void pf_export_forget(const pf_pool* pool) {
+  pool->shadow.target = nullptr;
+  pool->shadow.max_blocks = -1;
 }
 
-int pf_fill_meta_step(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out) {
-  const int st = pf_fill_meta(pool, seq_ids, n, max_blocks, out);
-  if (st != PF_OK) return st;
+int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_ids, int32_t n,
+                   int32_t max_blocks, bool step, int32_t* out, int64_t* pairs) {
+  if (!pool || !pairs || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  std::vector<const pf_seq_entry*> rows((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seq_ids[i]);
+    if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+    if (it->second.swapped) return PF_ERR_SWAPPED;
+    if (it->second.pages.size() > (size_t)max_blocks) return PF_ERR_INVALID;
+    rows[(size_t)i] = &it->second;
+  }
+  const size_t nb = (size_t)n * (size_t)max_blocks;
+  int32_t* lens = out + nb;
+  int32_t* newest = lens + n;
   const int32_t B = pool->g.block_size;
-  const int32_t* lens = out + (size_t)n * (size_t)max_blocks;
-  int32_t* dst = out + (size_t)n * (size_t)max_blocks + 2 * (size_t)n;
-  for (int32_t i = 0; i < n; ++i)
-    dst[i] = lens[i] > 0 ? out[(size_t)i * (size_t)max_blocks + (size_t)((lens[i] - 1) / B)] : -1;
+  for (int32_t i = 0; i < n; ++i) {
+    const pf_seq_entry& e = *rows[(size_t)i];
+    lens[i] = e.len;
+    newest[i] = e.len - 1;
+    if (step) newest[n + i] = e.len > 0 ? e.pages[(size_t)((e.len - 1) / B)] : -1;
+  }
+  pf_export_shadow& sh = pool->shadow;
+  bool delta = pool->export_delta && sh.target == target && target != nullptr && sh.max_blocks == max_blocks &&
+               sh.ids.size() == (size_t)n && std::equal(sh.ids.begin(), sh.ids.end(), seq_ids);
+  if (delta) {
+    const int64_t cap = (int64_t)nb / 2;
+    int64_t k = 0;
+    for (int32_t i = 0; i < n && delta; ++i) {
+      const pf_seq_entry& e = *rows[(size_t)i];
+      if (e.ver == sh.ver[(size_t)i]) continue;
+      const int32_t np = (int32_t)e.pages.size();
+      const int32_t hi = np > sh.used[(size_t)i] ? np : sh.used[(size_t)i];
+      int32_t* old = sh.table.data() + (size_t)i * (size_t)max_blocks;
+      for (int32_t j = 0; j < hi; ++j) {
+        const int32_t cur = j < np ? e.pages[(size_t)j] : -1;
+        if (cur == old[j]) continue;
+        if (k == cap) {  // more changes than the staging holds as pairs: export whole
+          delta = false;
+          break;
+        }
+        out[2 * k] = i * max_blocks + j;
+        out[2 * k + 1] = cur;
+        old[j] = cur;
+        ++k;
+      }
+      sh.ver[(size_t)i] = e.ver;
+      sh.used[(size_t)i] = np;
+    }
+    if (delta) {
+      *pairs = k;
+      return PF_OK;
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pf_seq_entry& e = *rows[(size_t)i];
+    int32_t* row = out + (size_t)i * (size_t)max_blocks;
+    const size_t np = e.pages.size();
+    if (np) std::memcpy(row, e.pages.data(), np * sizeof(int32_t));
+    for (size_t j = np; j < (size_t)max_blocks; ++j) row[j] = -1;
+  }
+  *pairs = -1;
+  if (pool->export_delta && target != nullptr) {
+    sh.target = target;
+    sh.max_blocks = max_blocks;
+    sh.ids.assign(seq_ids, seq_ids + n);
+    sh.ver.resize((size_t)n);
+    sh.used.resize((size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+      sh.ver[(size_t)i] = rows[(size_t)i]->ver;
+      sh.used[(size_t)i] = (int32_t)rows[(size_t)i]->pages.size();
+    }
+    sh.table.assign(out, out + nb);
+  } else {
+    pf_export_forget(pool);
+  }
   return PF_OK;
 }
 
 extern "C" {
+
+int pf_export_staging(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                      const void* meta_dev, int32_t step, int32_t* staging_host, int64_t* pairs) {
+  if (!pool || !pairs || n < 0 || max_blocks < 0) return PF_ERR_INVALID;
+  if (n > 0 && (!staging_host || !meta_dev)) return PF_ERR_INVALID;
+  *pairs = -1;
+  if (n == 0) return PF_OK;
+  return pf_fill_export(pool, meta_dev, seq_ids, n, max_blocks, step != 0, staging_host, pairs);
+}
 
 int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {
   if (!pool) return PF_ERR_INVALID;
@@ -459,6 +536,11 @@ int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {
       if (value < 0 || value > 64) return PF_ERR_INVALID;
       pool->waves_per_cu = value;
       return PF_OK;
+    case PF_OPT_EXPORT_DELTA:
+      if (value != 0 && value != 1) return PF_ERR_INVALID;
+      pool->export_delta = value;
+      pf_export_forget(pool);
+      return PF_OK;
     default:
       return PF_ERR_INVALID;
   }
@@ -472,6 +554,7 @@ int pf_pool_get_option(const pf_pool* pool, int32_t option, int32_t* value) {
     case PF_OPT_GQA_MFMA: *value = pool->gqa_mfma; return PF_OK;
     case PF_OPT_SCHEDULE: *value = pool->schedule; return PF_OK;
     case PF_OPT_WAVES_PER_CU: *value = pool->waves_per_cu; return PF_OK;
+    case PF_OPT_EXPORT_DELTA: *value = pool->export_delta; return PF_OK;
     default: return PF_ERR_INVALID;
   }
 }
@@ -546,6 +629,7 @@ int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host
       for (size_t j = e.pages.size(); j-- > 0;)
         if (--pool->refs[(size_t)e.pages[j]] == 0) pool->stack.push_back(e.pages[j]);
       e.pages.clear();
+      e.ver = ++pool->ver_clock;
       e.swapped = true;
     } else {
       e.pages.clear();
@@ -558,6 +642,7 @@ int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host
       }
       for (size_t j = e.slots.size(); j-- > 0;) pool->slot_stack.push_back(e.slots[j]);
       e.slots.clear();
+      e.ver = ++pool->ver_clock;
       e.swapped = false;
     }
   }

@@ -15,6 +15,21 @@ struct pf_seq_entry {
   int32_t len = 0;             // tokens held
   bool swapped = false;        // swapped out: pages empty, slots hold the blocks
   std::vector<int32_t> slots;  // host swap slots of logical blocks 0.. (swapped only)
+  // Version of `pages`: set from the pool's clock whenever the table changes,
+  // so equal versions mean an equal table (0: never held a page).
+  uint64_t ver = 0;
+};
+
+// What the device table of the previous export holds once its upload has
+// run (kept only with PF_OPT_EXPORT_DELTA): the target buffer, its rows'
+// sequences, the version of each row's table and the table image.
+struct pf_export_shadow {
+  const void* target = nullptr;
+  int32_t max_blocks = -1;
+  std::vector<uint64_t> ids;
+  std::vector<uint64_t> ver;
+  std::vector<int32_t> used;   // entries of each row that are not -1
+  std::vector<int32_t> table;  // [rows][max_blocks]
 };
 
 struct pf_pool {
@@ -42,6 +57,11 @@ struct pf_pool {
   int32_t gqa_mfma = 1;
   int32_t schedule = 0;       // 0 automatic, 1 fixed splits, 2 balanced
   int32_t waves_per_cu = 0;   // balanced schedule: 0 = resident capacity
+  // Clock of table versions (pf_seq_entry::ver).
+  uint64_t ver_clock = 0;
+  // Incremental table export (PF_OPT_EXPORT_DELTA) and its shadow.
+  int32_t export_delta = 0;
+  mutable pf_export_shadow shadow;
   // Instrumentation events around the partition kernel (hipEvent_t).
   void* ev_start = nullptr;
   void* ev_stop = nullptr;
@@ -49,13 +69,21 @@ struct pf_pool {
 
 size_t pf_elem_bytes(int32_t dtype);
 
-// Fill [n][max_blocks] tables, [n] lengths and [n] newest positions into
-// out (host memory) under the pool lock.  Same errors as pf_block_tables.
-int pf_fill_meta(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out);
+// Staging of one table export of seq_ids to the device buffer `target`
+// (host memory `out`, under the pool lock).  Lengths go to out[n*max_blocks],
+// newest positions (length - 1) to out[n*max_blocks + n] and, with step, the
+// pages holding the newest tokens (-1 for length 0) to out[n*max_blocks + 2n].
+// The table part: with PF_OPT_EXPORT_DELTA on and the previous export made to
+// the same target with the same seq_ids and max_blocks, the entries that
+// differ from it as (flat index, value) pairs at out[0 .. 2 * *pairs), if at
+// most n*max_blocks/2 of them; otherwise the whole [n][max_blocks] table
+// (padded with -1) at out[0..] and *pairs = -1.  Same errors as
+// pf_block_tables.
+int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_ids, int32_t n,
+                   int32_t max_blocks, bool step, int32_t* out, int64_t* pairs);
 
-// As pf_fill_meta, followed by [n] pages holding each sequence's newest token
-// (-1 for length 0).
-int pf_fill_meta_step(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, int32_t* out);
+// Forget the previous export (the next one is whole).
+void pf_export_forget(const pf_pool* pool);
 
 // Host half of pf_swap_out (to_host) / pf_swap_in: validate, move the
 // sequences between pages and host slots, and write the copy pairs ((page,

@@ -80,15 +80,6 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(KvArgs a) {
   }
 }
 
-// Copy words from pinned host memory to device memory: 16 bytes per thread,
-// read over the bus by the kernel itself.
-__global__ __launch_bounds__(256) void upload_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                     int64_t n16, const int32_t* __restrict__ tail_src,
-                                                     int32_t* __restrict__ tail_dst, int tail) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n16) dst[i] = src[i];
-  if (i < tail) tail_dst[i] = tail_src[i];
-}
 
 // Copy-on-write page copies (PagedAttention blog, "Copy-on-Write for Parallel
 // Sampling": the new block receives the shared block's contents): pair j
@@ -133,19 +124,25 @@ __global__ __launch_bounds__(256) void swap_copy_kernel(uint8_t* pool, uint8_t* 
   }
 }
 
-// Table upload (as upload_kernel) and the scatter of each sequence's newest
-// token for a range of layers, in one launch.  Threads [0, up_threads) copy
-// 16-byte words of the staging into the device table; the rest each move one
-// 16-byte column of one (layer, sequence, head, K|V) row, with the destination
-// page read from the staging (host memory) rather than the device table, so
-// the two halves do not depend on each other.
+// Table upload and the scatter of each sequence's newest token for a range of
+// layers, in one launch.  Threads [0, up_threads) upload: a whole export
+// copies 16-byte words of the staging (host memory, read over the bus, no DMA
+// engine round trip) into the device table, lengths and newest positions; an
+// incremental one writes (flat index, value) pairs into the table and copies
+// the lengths and newest positions.  The rest each move one 16-byte column of
+// one (layer, sequence, head, K|V) row, with the destination page read from
+// the staging rather than the device table, so the two halves do not depend
+// on each other.
 struct PrepArgs {
-  const uint4* src;
+  const uint4* src;          // whole export: n16 16-byte words
   uint4* dst;
   int64_t n16;
-  const int32_t* tail_src;
+  const int2* pairs;         // incremental export: npairs (flat index, value)
+  int32_t* table;
+  int64_t npairs;
+  const int32_t* tail_src;   // words after the n16 (whole) or lengths + newest (incremental)
   int32_t* tail_dst;
-  int tail;
+  int64_t tail;
   int64_t up_threads;
   uint8_t* pool;
   const uint8_t* k;
@@ -161,6 +158,10 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < a.up_threads) {
     if (i < a.n16) a.dst[i] = a.src[i];
+    if (i < a.npairs) {
+      const int2 pr = a.pairs[i];
+      a.table[pr.x] = pr.y;
+    }
     if (i < a.tail) a.tail_dst[i] = a.tail_src[i];
     return;
   }
@@ -272,24 +273,56 @@ extern "C" int pf_gather_kv(const pf_pool* pool, int32_t layer, const int32_t* b
   return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
 }
 
+// Fill the staging for an export of seq_ids to meta_dev and set the upload
+// half of a: whole (16-byte words) or incremental (pairs).
+static int stage_export(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, bool step,
+                        int32_t* staging_host, int32_t* meta_dev, pf::PrepArgs& a) {
+  int64_t pairs = -1;
+  const int st = pf_fill_export(pool, meta_dev, seq_ids, n, max_blocks, step, staging_host, &pairs);
+  if (st != PF_OK) return st;
+  const int64_t nb = (int64_t)n * max_blocks;
+  if (pairs < 0) {
+    const int64_t words = nb + 2 * (int64_t)n;
+    a.n16 = words / 4;
+    a.src = reinterpret_cast<const uint4*>(staging_host);
+    a.dst = reinterpret_cast<uint4*>(meta_dev);
+    a.tail = words - a.n16 * 4;
+    a.tail_src = staging_host + a.n16 * 4;
+    a.tail_dst = meta_dev + a.n16 * 4;
+  } else {
+    a.npairs = pairs;
+    a.pairs = reinterpret_cast<const int2*>(staging_host);
+    a.table = meta_dev;
+    a.tail = 2 * (int64_t)n;
+    a.tail_src = staging_host + nb;
+    a.tail_dst = meta_dev + nb;
+  }
+  int64_t up = a.n16 > a.npairs ? a.n16 : a.npairs;
+  if (a.tail > up) up = a.tail;
+  a.up_threads = up;
+  return PF_OK;
+}
+
 extern "C" int pf_export_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
                                 int32_t* staging_host, int32_t* meta_dev, void* hip_stream) {
   using namespace pf;
   if (!pool || n < 0 || max_blocks < 0) return PF_ERR_INVALID;
   if (n == 0) return PF_OK;
   if (!staging_host || !meta_dev || !aligned16(staging_host) || !aligned16(meta_dev)) return PF_ERR_INVALID;
-  const int st = pf_fill_meta(pool, seq_ids, n, max_blocks, staging_host);
+  PrepArgs a{};
+  const int st = stage_export(pool, seq_ids, n, max_blocks, false, staging_host, meta_dev, a);
   if (st != PF_OK) return st;
-  const int64_t words = (int64_t)n * max_blocks + 2 * (int64_t)n;
-  const int64_t n16 = words / 4;
-  const int tail = (int)(words - n16 * 4);
-  const int64_t threads = n16 > tail ? n16 : tail;
-  const int64_t blocks = (threads + 255) / 256;
-  if (blocks > 0x7fffffff) return PF_ERR_INVALID;
-  hipLaunchKernelGGL(upload_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream,
-                     reinterpret_cast<const uint4*>(staging_host), reinterpret_cast<uint4*>(meta_dev), n16,
-                     staging_host + n16 * 4, meta_dev + n16 * 4, tail);
-  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+  const int64_t blocks = (a.up_threads + 255) / 256;
+  if (blocks > 0x7fffffff) {
+    pf_export_forget(pool);
+    return PF_ERR_INVALID;
+  }
+  hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, a);
+  if (hipGetLastError() != hipSuccess) {
+    pf_export_forget(pool);
+    return PF_ERR_HIP;
+  }
+  return PF_OK;
 }
 
 extern "C" int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
@@ -304,17 +337,9 @@ extern "C" int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, i
   if (n == 0) return PF_OK;
   if (!staging_host || !meta_dev || !aligned16(staging_host) || !aligned16(meta_dev)) return PF_ERR_INVALID;
   if (num_layers > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return PF_ERR_INVALID;
-  const int st = pf_fill_meta_step(pool, seq_ids, n, max_blocks, staging_host);
-  if (st != PF_OK) return st;
   PrepArgs a{};
-  const int64_t words = (int64_t)n * max_blocks + 2 * (int64_t)n;
-  a.n16 = words / 4;
-  a.tail = (int)(words - a.n16 * 4);
-  a.src = reinterpret_cast<const uint4*>(staging_host);
-  a.dst = reinterpret_cast<uint4*>(meta_dev);
-  a.tail_src = staging_host + a.n16 * 4;
-  a.tail_dst = meta_dev + a.n16 * 4;
-  a.up_threads = a.n16 > a.tail ? a.n16 : a.tail;
+  const int st = stage_export(pool, seq_ids, n, max_blocks, true, staging_host, meta_dev, a);
+  if (st != PF_OK) return st;
   a.pool = static_cast<uint8_t*>(pool->dev);
   a.k = static_cast<const uint8_t*>(k);
   a.v = static_cast<const uint8_t*>(v);
@@ -330,9 +355,16 @@ extern "C" int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, i
   a.num_pages = g.num_pages;
   a.sc_threads = (int64_t)num_layers * n * g.num_kv_heads * 2 * (g.head_dim * a.es / 16);
   const int64_t blocks = (a.up_threads + a.sc_threads + 255) / 256;
-  if (blocks > 0x7fffffff) return PF_ERR_INVALID;
+  if (blocks > 0x7fffffff) {
+    pf_export_forget(pool);
+    return PF_ERR_INVALID;
+  }
   hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream, a);
-  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) {
+    pf_export_forget(pool);
+    return PF_ERR_HIP;
+  }
+  return PF_OK;
 }
 
 extern "C" int pf_copy_pages(const pf_pool* pool, const int32_t* pairs, int32_t n, void* hip_stream) {
@@ -378,4 +410,58 @@ extern "C" int pf_swap_out(pf_pool* pool, const uint64_t* seq_ids, int32_t n, in
 extern "C" int pf_swap_in(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
                           int64_t staging_words, void* hip_stream) {
   return swap_call(pool, seq_ids, n, staging_host, staging_words, false, hip_stream);
+}
+
+// ------------------------------------------------------------ stream markers
+// Events without the system-scope fence: recording one adds no cache
+// writeback / invalidation to the stream (a default event did, about 6 us
+// between two kernels on MI355X).
+extern "C" int pf_marker_create(int32_t timing, void** event) {
+  if (!event) return PF_ERR_INVALID;
+  *event = nullptr;
+  unsigned flags = hipEventDisableSystemFence;
+  if (!timing) flags |= hipEventDisableTiming;
+  hipEvent_t e = nullptr;
+  if (hipEventCreateWithFlags(&e, flags) != hipSuccess) {
+    (void)hipGetLastError();
+    return PF_ERR_HIP;
+  }
+  *event = e;
+  return PF_OK;
+}
+
+extern "C" int pf_marker_record(void* event, void* hip_stream) {
+  if (!event) return PF_ERR_INVALID;
+  if (hipEventRecord((hipEvent_t)event, (hipStream_t)hip_stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return PF_ERR_HIP;
+  }
+  return PF_OK;
+}
+
+extern "C" int pf_marker_wait(void* event) {
+  if (!event) return PF_ERR_INVALID;
+  if (hipEventSynchronize((hipEvent_t)event) != hipSuccess) {
+    (void)hipGetLastError();
+    return PF_ERR_HIP;
+  }
+  return PF_OK;
+}
+
+extern "C" int pf_marker_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return PF_ERR_INVALID;
+  if (hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)stop) != hipSuccess) {
+    (void)hipGetLastError();
+    return PF_ERR_HIP;
+  }
+  return PF_OK;
+}
+
+extern "C" int pf_marker_destroy(void* event) {
+  if (!event) return PF_ERR_INVALID;
+  if (hipEventDestroy((hipEvent_t)event) != hipSuccess) {
+    (void)hipGetLastError();
+    return PF_ERR_HIP;
+  }
+  return PF_OK;
 }

@@ -35,6 +35,7 @@ PF_OPT_SPLIT_TOKENS = 0
 PF_OPT_GQA_MFMA = 1
 PF_OPT_SCHEDULE = 2
 PF_OPT_WAVES_PER_CU = 3
+PF_OPT_EXPORT_DELTA = 4
 
 
 class pf_geometry(ctypes.Structure):
@@ -74,6 +75,8 @@ _SIGS = {
     "pf_seq_len": (_i32, [_vp, _u64, _pi32]),
     "pf_block_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _pi32, _pi32]),
     "pf_export_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _vp, _vp]),
+    "pf_export_staging": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _i32, _vp,
+                                 ctypes.POINTER(ctypes.c_int64)]),
     "pf_decode_prepare": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "pf_scatter_kv": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
     "pf_gather_kv": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
@@ -89,6 +92,11 @@ _SIGS = {
     "pf_pool_get_option": (_i32, [_vp, _i32, _pi32]),
     "pf_attention_split_tokens": (_i32, [_vp, _i32, _i32, _i32]),
     "pf_pool_set_timing_events": (_i32, [_vp, _vp, _vp]),
+    "pf_marker_create": (_i32, [_i32, ctypes.POINTER(_vp)]),
+    "pf_marker_record": (_i32, [_vp, _vp]),
+    "pf_marker_wait": (_i32, [_vp]),
+    "pf_marker_elapsed_ms": (_i32, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
+    "pf_marker_destroy": (_i32, [_vp]),
     "pf_attention_kernel": (_i32, [_vp, _i32]),
     "pf_attention_waves": (_i32, [_vp, _i32, _i32, _i32]),
     "pf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -119,6 +127,17 @@ def _dev(x):
         return None
     if isinstance(x, int):
         return x
+    return x.data_ptr()
+
+
+def _host_ptr(x):
+    """Address of a host buffer: a numpy array, a (CPU or pinned) torch tensor
+    or an int address."""
+    if x is None or isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        assert x.dtype == np.int32 and x.flags.c_contiguous
+        return x.ctypes.data
     return x.data_ptr()
 
 
@@ -299,6 +318,63 @@ def pf_pool_set_timing_events(pool, start_event, stop_event):
     return lib.pf_pool_set_timing_events(pool, start_event, stop_event)
 
 
+def pf_marker_create(timing):
+    """A stream marker (hipEvent_t without the system-scope fence); returns
+    (status, handle as int)."""
+    ev = _vp()
+    st = lib.pf_marker_create(1 if timing else 0, ctypes.byref(ev))
+    return st, ev.value
+
+
+def pf_marker_record(event, stream=None):
+    return lib.pf_marker_record(event, _stream(stream))
+
+
+def pf_marker_wait(event):
+    return lib.pf_marker_wait(event)
+
+
+def pf_marker_elapsed_ms(start, stop):
+    ms = ctypes.c_float(0.0)
+    st = lib.pf_marker_elapsed_ms(start, stop, ctypes.byref(ms))
+    return st, ms.value
+
+
+def pf_marker_destroy(event):
+    return lib.pf_marker_destroy(event)
+
+
+class Marker:
+    """Owning wrapper of a stream marker: ``record(stream)``, ``wait()``,
+    ``elapsed_ms(other)``, ``handle`` (for pf_pool_set_timing_events)."""
+
+    def __init__(self, timing=False):
+        st, self.handle = pf_marker_create(timing)
+        check(st, "pf_marker_create")
+
+    def record(self, stream=None):
+        check(pf_marker_record(self.handle, stream), "pf_marker_record")
+
+    def wait(self):
+        check(pf_marker_wait(self.handle), "pf_marker_wait")
+
+    def elapsed_ms(self, stop):
+        st, ms = pf_marker_elapsed_ms(self.handle, stop.handle)
+        check(st, "pf_marker_elapsed_ms")
+        return ms
+
+    def close(self):
+        if self.handle:
+            pf_marker_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def pf_status_string(status):
     return lib.pf_status_string(status).decode()
 
@@ -310,6 +386,17 @@ def pf_export_tables(pool, seq_ids, max_blocks, staging_host, meta_dev, stream=N
     ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
     return lib.pf_export_tables(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
                                 _dev(staging_host), _dev(meta_dev), _stream(stream))
+
+
+def pf_export_staging(pool, seq_ids, max_blocks, meta_dev, step, staging_host):
+    """Host half of an export (no launch).  ``staging_host`` an int32 numpy
+    array (or tensor) of >= n*max_blocks + (3 if step else 2)*n words;
+    ``meta_dev`` an integer naming the target.  Returns (status, pairs)."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
+    pairs = ctypes.c_int64(0)
+    st = lib.pf_export_staging(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
+                               meta_dev, 1 if step else 0, _host_ptr(staging_host), ctypes.byref(pairs))
+    return st, pairs.value
 
 
 def pf_decode_prepare(pool, seq_ids, max_blocks, staging_host, meta_dev, k, v, layer0, num_layers,

@@ -29,10 +29,53 @@ def bits_from_device(t):
     return a.view(np.uint32 if a.dtype == np.int32 else np.uint16)
 
 
+class StagingRing:
+    """Pinned staging buffers for the per-step table upload, so the host can
+    fill step t+1's tables while the device still runs step t.  A buffer is
+    refilled only after the upload that read it has run.  That is learnt from
+    stream markers (pf_marker_*), but not one per upload: on MI355X any marker
+    between two kernels costs ~4.5 us of stream time, so one marker follows
+    every GROUP-th upload, and before slot i is refilled the host waits for the
+    first marker recorded after slot i's previous upload (SLOTS > GROUP keeps
+    that marker in the past)."""
+
+    SLOTS = 16
+    GROUP = 8
+
+    def __init__(self, words, gpu, pin=None):
+        import torch
+        self.gpu = gpu
+        pin = gpu if pin is None else pin
+        self.bufs = []
+        for _ in range(self.SLOTS):
+            t = torch.empty(max(words, 1), dtype=torch.int32)
+            self.bufs.append(t.pin_memory() if pin else t)
+        # marker j covers uploads up to the last of its group; a marker object
+        # is re-recorded only after every wait on its previous group
+        self.markers = [pf.Marker() for _ in range(self.SLOTS // self.GROUP + 1)] if gpu else []
+        self.count = 0   # uploads enqueued so far
+
+    def acquire(self):
+        """The buffer for the next upload, free to overwrite."""
+        k = self.count
+        if self.gpu and k >= self.SLOTS:
+            prev = k - self.SLOTS                   # the upload that last used this slot
+            covering = prev | (self.GROUP - 1)      # the marker recorded after it (< k)
+            self.markers[(covering // self.GROUP) % len(self.markers)].wait()
+        return self.bufs[k % self.SLOTS]
+
+    def enqueued(self, stream=None):
+        """Call right after the upload that read acquire()'s buffer was enqueued."""
+        k = self.count
+        if self.gpu and k % self.GROUP == self.GROUP - 1:
+            self.markers[(k // self.GROUP) % len(self.markers)].record(stream)
+        self.count = k + 1
+
+
 class PagedKV:
     """A pool handle bound to a torch-allocated device pool, plus device tables."""
 
-    def __init__(self, w, device="cuda", sentinel=True, extra_tokens=0, max_blocks=None):
+    def __init__(self, w, device="cuda", sentinel=True, extra_tokens=0, max_blocks=None, delta_export=True):
         self.w = w
         self.device = device
         st, self.h = pf.pf_pool_create(w.num_pages, w.block, w.layers, w.hkv, w.d, w.dtype,
@@ -55,9 +98,9 @@ class PagedKV:
         self.bt = self.meta[:nb].view(w.n, self.max_blocks)
         self.ctx = self.meta[nb:nb + w.n]
         self.last_pos = self.meta[nb + w.n:nb + 2 * w.n]
-        self.ring = [self._host_meta() for _ in range(4)]
-        self.ring_ev = [torch.cuda.Event() if torch.cuda.is_available() else None for _ in range(4)]
-        self.ring_i = 0
+        self.ring = StagingRing(self.stage_elems, torch.cuda.is_available())
+        # self.meta is written only by the exports below: upload only what changed
+        pf.check(pf.pf_pool_set_option(self.h, pf.PF_OPT_EXPORT_DELTA, 1 if delta_export else 0))
         self.ws = None
         self.ws_bytes = 0
 
@@ -81,37 +124,24 @@ class PagedKV:
             else:
                 pf.check(pf.pf_free_seq(self.h, op[1]), "pf_free_seq")
 
-    def _host_meta(self):
-        t = torch.empty(max(self.stage_elems, 1), dtype=torch.int32)
-        return t.pin_memory() if torch.cuda.is_available() else t
-
     def export_tables(self):
         """Block tables, lengths and newest positions of sequences 0..n-1 to the
         device (pf_export_tables: pinned staging, one upload kernel on the
-        current stream).  A ring of four staging buffers lets the host run
-        ahead; a slot is reused only after its upload has run."""
-        slot = self.ring_i
-        self.ring_i = (slot + 1) % len(self.ring)
-        if self.ring_ev[slot] is not None:
-            self.ring_ev[slot].synchronize()
-        st = pf.pf_export_tables(self.h, self.ids, self.max_blocks, self.ring[slot], self.meta)
+        current stream), from the next slot of the staging ring."""
+        buf = self.ring.acquire()
+        st = pf.pf_export_tables(self.h, self.ids, self.max_blocks, buf, self.meta)
         pf.check(st, "pf_export_tables")
-        if self.ring_ev[slot] is not None:
-            self.ring_ev[slot].record()
+        self.ring.enqueued()
 
     def decode_prepare(self, k_new, v_new, layer0=0, num_layers=None):
         """Export the tables and scatter every sequence's newest token for
         layers layer0.. (k_new, v_new: device [layers][n][H][D]) in one launch."""
         num_layers = self.w.layers - layer0 if num_layers is None else num_layers
-        slot = self.ring_i
-        self.ring_i = (slot + 1) % len(self.ring)
-        if self.ring_ev[slot] is not None:
-            self.ring_ev[slot].synchronize()
-        st = pf.pf_decode_prepare(self.h, self.ids, self.max_blocks, self.ring[slot], self.meta, k_new, v_new,
+        buf = self.ring.acquire()
+        st = pf.pf_decode_prepare(self.h, self.ids, self.max_blocks, buf, self.meta, k_new, v_new,
                                   layer0, num_layers)
         pf.check(st, "pf_decode_prepare")
-        if self.ring_ev[slot] is not None:
-            self.ring_ev[slot].record()
+        self.ring.enqueued()
 
     # --------------------------------------------------------------- kernels
     def scatter(self, layer, k, v, tok_seq, tok_pos, stream=None):

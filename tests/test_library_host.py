@@ -364,3 +364,12 @@ def test_batch_alloc_is_all_or_nothing_and_matches_oracle(seed):
             model.free(s)
     _tables_equal(h, model)
     pf.pf_pool_destroy(h)
+
+
+def test_marker_entry_points_refuse_null():
+    """Checked before any HIP call (no GPU needed)."""
+    assert pf.lib.pf_marker_create(0, None) == pf.PF_ERR_INVALID
+    assert pf.lib.pf_marker_record(None, None) == pf.PF_ERR_INVALID
+    assert pf.lib.pf_marker_wait(None) == pf.PF_ERR_INVALID
+    assert pf.lib.pf_marker_destroy(None) == pf.PF_ERR_INVALID
+    assert pf.lib.pf_marker_elapsed_ms(None, None, None) == pf.PF_ERR_INVALID
