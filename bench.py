@@ -57,8 +57,9 @@ def kernel_source_hash():
 
 def measured_traffic(config):
     """HBM bytes per partition launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, copy-kernel calibrated), or None when the
-    kernels changed since the counters were taken."""
+    summary (FETCH_SIZE + WRITE_SIZE, copy-kernel calibrated) and the
+    algorithmic bytes of the same launches (the counter runs' lengths), or None
+    when the kernels changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     try:
         kv = dict(l.split(":", 1) for l in open(path) if ":" in l and not l.startswith("#"))
@@ -66,7 +67,8 @@ def measured_traffic(config):
         return None
     if kv.get("source_hash", "").strip() != kernel_source_hash() or config not in kv:
         return None
-    return int(kv[config])
+    f = kv[config].split()
+    return int(f[0]), (int(f[1]) if len(f) > 1 else None)
 
 
 def alg_bytes_attention(ctx, w, out_bytes):
@@ -788,6 +790,7 @@ def main():
         if a_s and a_o:
             cost[name] = round(a_s["median_us"] / a_o["median_us"], 3)
     w = head["w"]
+    traffic = measured_traffic(args.config)
     line = {
         "metric": "paged decode attention KV GB/s (% of MI355X HBM peak) + sequences/ms",
         "value": round(head["value"], 1),
@@ -808,7 +811,9 @@ def main():
         "attention": head["attention"],
         "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.config),
+                     "traffic": traffic[0] if traffic else None,
+                     "traffic_alg_bytes": traffic[1] if traffic else None,
+                     "traffic_over_alg": round(traffic[0] / traffic[1], 4) if traffic and traffic[1] else None,
                      "kernel": "attention partition", "avg_launch_us": round(head["part_avg_us"], 2),
                      "median_launch_us": round(head["part_med_us"], 2),
                      "min_launch_us": round(head["part_min_us"], 2),
