@@ -750,7 +750,7 @@ def main():
                          "the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); run with --gpus 1",
+        print("bench.py: measures one GPU only (the path has no multi-GPU part); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch
