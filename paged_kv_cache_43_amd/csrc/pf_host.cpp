@@ -419,9 +419,14 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
 
 }  // extern "C"
 
-void pf_export_forget(const pf_pool* pool) {
+static void export_forget_locked(const pf_pool* pool) {
   pool->shadow.target = nullptr;
   pool->shadow.max_blocks = -1;
+}
+
+void pf_export_forget(const pf_pool* pool) {
+  std::lock_guard<std::mutex> lk(pool->mu);
+  export_forget_locked(pool);
 }
 
 int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_ids, int32_t n,
@@ -498,7 +503,7 @@ int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_
     }
     sh.table.assign(out, out + nb);
   } else {
-    pf_export_forget(pool);
+    export_forget_locked(pool);
   }
   return PF_OK;
 }
@@ -539,7 +544,7 @@ int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {
     case PF_OPT_EXPORT_DELTA:
       if (value != 0 && value != 1) return PF_ERR_INVALID;
       pool->export_delta = value;
-      pf_export_forget(pool);
+      export_forget_locked(pool);
       return PF_OK;
     default:
       return PF_ERR_INVALID;

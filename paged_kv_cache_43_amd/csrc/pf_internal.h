@@ -82,7 +82,7 @@ size_t pf_elem_bytes(int32_t dtype);
 int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_ids, int32_t n,
                    int32_t max_blocks, bool step, int32_t* out, int64_t* pairs);
 
-// Forget the previous export (the next one is whole).
+// Forget the previous export (the next one is whole); takes the pool lock.
 void pf_export_forget(const pf_pool* pool);
 
 // Host half of pf_swap_out (to_host) / pf_swap_in: validate, move the

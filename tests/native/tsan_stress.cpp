@@ -2,7 +2,7 @@
 // -fsanitize=thread against pf_host.cpp alone (no device code runs).
 // Eight threads share one pool and work on disjoint sequence ids: grow,
 // batch grow, fork, copy-on-write grow, swap planning out and in, free,
-// table export and option changes.  Exit status 0 if every call returned an
+// table export (whole and incremental) and option changes.  Exit status 0 if every call returned an
 // expected status and the pool came back whole; ThreadSanitizer reports any
 // data race on stderr and makes the exit status non-zero.
 #include <atomic>
@@ -95,6 +95,16 @@ static void worker(pf_pool* pool, int t) {
       int32_t v = 0;
       pf_pool_set_option(pool, PF_OPT_WAVES_PER_CU, (int32_t)(rng() % 9));
       pf_pool_get_option(pool, PF_OPT_WAVES_PER_CU, &v);
+      // incremental export: the shared shadow of the previous export, two
+      // fake targets per thread (never dereferenced), delta switched on and
+      // off by any thread
+      std::vector<int32_t> stage(67 * live.size() + 1);
+      int64_t pairs = 0;
+      const void* target = reinterpret_cast<const void*>((uintptr_t(t) * 2 + 1 + rng() % 2) << 12);
+      const int se = pf_export_staging(pool, live.data(), (int32_t)live.size(), 64, target, (int32_t)(rng() % 2),
+                                       stage.data(), &pairs);
+      expect(se == PF_OK || se == PF_ERR_INVALID, "export staging", se);
+      if (rng() % 16 == 0) pf_pool_set_option(pool, PF_OPT_EXPORT_DELTA, (int32_t)(rng() % 2));
     } else {
       const size_t i = rng() % live.size();
       const int st = pf_free_seq(pool, live[i]);
