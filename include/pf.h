@@ -56,7 +56,10 @@ typedef enum {
   PF_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
   PF_ERR_UNSUPPORTED = -7,  /* valid but not built: block size / head dim */
   PF_ERR_SHARED = -8,       /* growth would write into a page another table shares */
-  PF_ERR_SWAPPED = -9       /* the sequence is swapped out (pf_swap_out) */
+  PF_ERR_SWAPPED = -9,      /* the sequence is swapped out (pf_swap_out) */
+  PF_ERR_HOST_MEMORY = -10  /* host memory for the handle's own state ran out; any entry
+                               point that grows the handle's state may return it (a batch
+                               may then be partly applied: treat the handle as lost) */
 } pf_status;
 
 typedef struct {

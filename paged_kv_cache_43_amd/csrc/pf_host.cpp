@@ -28,6 +28,7 @@
 #include <algorithm>
 #include <cstring>
 #include <limits>
+#include <memory>
 #include <new>
 
 #include "pf_internal.h"
@@ -63,6 +64,20 @@ static bool mul_ok(size_t a, size_t b, size_t* out) {
   return true;
 }
 
+// Host memory for the allocator's own state (vectors and maps) can run out;
+// no C++ exception may cross the C ABI, so the entry points that allocate run
+// their body through guarded().
+template <class F>
+static int guarded(F&& body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return PF_ERR_HOST_MEMORY;
+  } catch (...) {
+    return PF_ERR_INVALID;
+  }
+}
+
 extern "C" {
 
 int pf_pool_create(const pf_geometry* geom, const int32_t* initial_free_order, pf_pool** out) {
@@ -80,8 +95,8 @@ int pf_pool_create(const pf_geometry* geom, const int32_t* initial_free_order, p
   size_t total = 0;
   if (!mul_ok(pe, (size_t)g.num_pages, &total) || !mul_ok(total, pf_elem_bytes(g.dtype), &total))
     return PF_ERR_INVALID;
-  pf_pool* p = new (std::nothrow) pf_pool();
-  if (!p) return PF_ERR_INVALID;
+  return guarded([&]() -> int {
+  std::unique_ptr<pf_pool> p(new pf_pool());
   p->g = g;
   p->elem_bytes = pf_elem_bytes(g.dtype);
   p->page_elems = pe;
@@ -91,18 +106,16 @@ int pf_pool_create(const pf_geometry* geom, const int32_t* initial_free_order, p
     std::vector<uint8_t> seen((size_t)g.num_pages, 0);
     for (int32_t i = 0; i < g.num_pages; ++i) {
       int32_t v = initial_free_order[i];
-      if (v < 0 || v >= g.num_pages || seen[(size_t)v]) {
-        delete p;
-        return PF_ERR_INVALID;
-      }
+      if (v < 0 || v >= g.num_pages || seen[(size_t)v]) return PF_ERR_INVALID;
       seen[(size_t)v] = 1;
     }
   }
   // order[0] must pop first: it goes on top, i.e. at the back.
   for (int32_t i = 0; i < g.num_pages; ++i)
     p->stack[(size_t)(g.num_pages - 1 - i)] = initial_free_order ? initial_free_order[i] : i;
-  *out = p;
+  *out = p.release();
   return PF_OK;
+  });
 }
 
 void pf_pool_destroy(pf_pool* pool) { delete pool; }
@@ -124,90 +137,94 @@ int pf_pool_bind(pf_pool* pool, void* dev_ptr, size_t bytes) {
 }
 
 int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n_new_pages) {
-  if (n_new_pages) *n_new_pages = 0;
-  if (!pool || new_len < 0) return PF_ERR_INVALID;
-  std::lock_guard<std::mutex> lk(pool->mu);
-  auto it = pool->seqs.find(seq_id);
-  if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
-  const int32_t cur_len = it == pool->seqs.end() ? 0 : it->second.len;
-  const size_t have = it == pool->seqs.end() ? 0 : it->second.pages.size();
-  if (new_len < cur_len) return PF_ERR_INVALID;
-  if (it != pool->seqs.end() && writes_shared(pool, it->second, new_len)) return PF_ERR_SHARED;
-  const int64_t B = pool->g.block_size;
-  const size_t want = (size_t)(((int64_t)new_len + B - 1) / B);
-  const size_t need = want - have;
-  if (need > pool->stack.size()) return PF_ERR_OOM;  // all or nothing
-  pf_seq_entry& e = it == pool->seqs.end() ? pool->seqs[seq_id] : it->second;
-  e.pages.reserve(want);
-  for (size_t i = 0; i < need; ++i) e.pages.push_back(pop_page(pool));
-  if (need) e.ver = ++pool->ver_clock;
-  e.len = new_len;
-  if (n_new_pages) *n_new_pages = (int32_t)need;
-  return PF_OK;
+  return guarded([&]() -> int {
+    if (n_new_pages) *n_new_pages = 0;
+    if (!pool || new_len < 0) return PF_ERR_INVALID;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    auto it = pool->seqs.find(seq_id);
+    if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
+    const int32_t cur_len = it == pool->seqs.end() ? 0 : it->second.len;
+    const size_t have = it == pool->seqs.end() ? 0 : it->second.pages.size();
+    if (new_len < cur_len) return PF_ERR_INVALID;
+    if (it != pool->seqs.end() && writes_shared(pool, it->second, new_len)) return PF_ERR_SHARED;
+    const int64_t B = pool->g.block_size;
+    const size_t want = (size_t)(((int64_t)new_len + B - 1) / B);
+    const size_t need = want - have;
+    if (need > pool->stack.size()) return PF_ERR_OOM;  // all or nothing
+    pf_seq_entry& e = it == pool->seqs.end() ? pool->seqs[seq_id] : it->second;
+    e.pages.reserve(want);
+    for (size_t i = 0; i < need; ++i) e.pages.push_back(pop_page(pool));
+    if (need) e.ver = ++pool->ver_clock;
+    e.len = new_len;
+    if (n_new_pages) *n_new_pages = (int32_t)need;
+    return PF_OK;
+  });
 }
 
 int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
                       int32_t* n_new_pages) {
-  if (!pool || n < 0 || (n > 0 && (!seq_ids || !new_lens))) return PF_ERR_INVALID;
-  if (n_new_pages)
-    for (int32_t i = 0; i < n; ++i) n_new_pages[i] = 0;
-  std::lock_guard<std::mutex> lk(pool->mu);
-  const int64_t B = pool->g.block_size;
-  // Validation pass: lengths and page counts as the batch would leave them.
-  // A sequence's last page is shared only if it is still the page it had
-  // before the batch (pages taken in the batch are private).
-  struct Pending {
-    int32_t len;
-    size_t pages;
-    bool last_original;
-  };
-  std::unordered_map<uint64_t, Pending> pending;
-  for (int32_t i = 0; i < n; ++i) {
-    if (new_lens[i] < 0) return PF_ERR_INVALID;
-    auto pit = pending.find(seq_ids[i]);
-    int32_t cur_len = 0;
-    if (pit != pending.end()) {
-      cur_len = pit->second.len;
-    } else {
+  return guarded([&]() -> int {
+    if (!pool || n < 0 || (n > 0 && (!seq_ids || !new_lens))) return PF_ERR_INVALID;
+    if (n_new_pages)
+      for (int32_t i = 0; i < n; ++i) n_new_pages[i] = 0;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    const int64_t B = pool->g.block_size;
+    // Validation pass: lengths and page counts as the batch would leave them.
+    // A sequence's last page is shared only if it is still the page it had
+    // before the batch (pages taken in the batch are private).
+    struct Pending {
+      int32_t len;
+      size_t pages;
+      bool last_original;
+    };
+    std::unordered_map<uint64_t, Pending> pending;
+    for (int32_t i = 0; i < n; ++i) {
+      if (new_lens[i] < 0) return PF_ERR_INVALID;
+      auto pit = pending.find(seq_ids[i]);
+      int32_t cur_len = 0;
+      if (pit != pending.end()) {
+        cur_len = pit->second.len;
+      } else {
+        auto it = pool->seqs.find(seq_ids[i]);
+        if (it != pool->seqs.end()) cur_len = it->second.len;
+      }
+      if (new_lens[i] < cur_len) return PF_ERR_INVALID;
+      pending[seq_ids[i]] = {new_lens[i], 0, true};
+    }
+    for (int32_t i = 0; i < n; ++i) {
       auto it = pool->seqs.find(seq_ids[i]);
-      if (it != pool->seqs.end()) cur_len = it->second.len;
+      if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
     }
-    if (new_lens[i] < cur_len) return PF_ERR_INVALID;
-    pending[seq_ids[i]] = {new_lens[i], 0, true};
-  }
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = pool->seqs.find(seq_ids[i]);
-    if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
-  }
-  pending.clear();
-  size_t total = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    auto pit = pending.find(seq_ids[i]);
-    Pending cur{0, 0, false};
-    auto it = pool->seqs.find(seq_ids[i]);
-    if (pit != pending.end()) {
-      cur = pit->second;
-    } else if (it != pool->seqs.end()) {
-      cur = {it->second.len, it->second.pages.size(), true};
+    pending.clear();
+    size_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      auto pit = pending.find(seq_ids[i]);
+      Pending cur{0, 0, false};
+      auto it = pool->seqs.find(seq_ids[i]);
+      if (pit != pending.end()) {
+        cur = pit->second;
+      } else if (it != pool->seqs.end()) {
+        cur = {it->second.len, it->second.pages.size(), true};
+      }
+      if (cur.last_original && it != pool->seqs.end() && writes_shared(pool, it->second, new_lens[i]) &&
+          cur.len == it->second.len)
+        return PF_ERR_SHARED;
+      const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+      total += want - cur.pages;
+      pending[seq_ids[i]] = {new_lens[i], want, cur.last_original && want == cur.pages};
     }
-    if (cur.last_original && it != pool->seqs.end() && writes_shared(pool, it->second, new_lens[i]) &&
-        cur.len == it->second.len)
-      return PF_ERR_SHARED;
-    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
-    total += want - cur.pages;
-    pending[seq_ids[i]] = {new_lens[i], want, cur.last_original && want == cur.pages};
-  }
-  if (total > pool->stack.size()) return PF_ERR_OOM;
-  for (int32_t i = 0; i < n; ++i) {
-    pf_seq_entry& e = pool->seqs[seq_ids[i]];
-    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
-    const size_t need = want - e.pages.size();
-    for (size_t j = 0; j < need; ++j) e.pages.push_back(pop_page(pool));
-    if (need) e.ver = ++pool->ver_clock;
-    e.len = new_lens[i];
-    if (n_new_pages) n_new_pages[i] = (int32_t)need;
-  }
-  return PF_OK;
+    if (total > pool->stack.size()) return PF_ERR_OOM;
+    for (int32_t i = 0; i < n; ++i) {
+      pf_seq_entry& e = pool->seqs[seq_ids[i]];
+      const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+      const size_t need = want - e.pages.size();
+      for (size_t j = 0; j < need; ++j) e.pages.push_back(pop_page(pool));
+      if (need) e.ver = ++pool->ver_clock;
+      e.len = new_lens[i];
+      if (n_new_pages) n_new_pages[i] = (int32_t)need;
+    }
+    return PF_OK;
+  });
 }
 
 int pf_free_seq(pf_pool* pool, uint64_t seq_id) {
@@ -225,118 +242,124 @@ int pf_free_seq(pf_pool* pool, uint64_t seq_id) {
 }
 
 int pf_fork_seq(pf_pool* pool, uint64_t parent, uint64_t child) {
-  if (!pool) return PF_ERR_INVALID;
-  std::lock_guard<std::mutex> lk(pool->mu);
-  auto it = pool->seqs.find(parent);
-  if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
-  if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
-  if (pool->seqs.count(child)) return PF_ERR_INVALID;
-  pf_seq_entry copy = it->second;
-  for (int32_t p : copy.pages) ++pool->refs[(size_t)p];
-  copy.ver = ++pool->ver_clock;
-  pool->seqs.emplace(child, std::move(copy));
-  return PF_OK;
+  return guarded([&]() -> int {
+    if (!pool) return PF_ERR_INVALID;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    auto it = pool->seqs.find(parent);
+    if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
+    if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+    if (pool->seqs.count(child)) return PF_ERR_INVALID;
+    pf_seq_entry copy = it->second;
+    for (int32_t p : copy.pages) ++pool->refs[(size_t)p];
+    copy.ver = ++pool->ver_clock;
+    pool->seqs.emplace(child, std::move(copy));
+    return PF_OK;
+  });
 }
 
 int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
                  int32_t* n_new_pages, int32_t* copies, int32_t* n_copies) {
-  if (n_copies) *n_copies = 0;
-  if (!pool || n < 0 || (n > 0 && (!seq_ids || !new_lens || !copies || !n_copies))) return PF_ERR_INVALID;
-  if (n_new_pages)
-    for (int32_t i = 0; i < n; ++i) n_new_pages[i] = 0;
-  std::lock_guard<std::mutex> lk(pool->mu);
-  const int64_t B = pool->g.block_size;
-  // Dry run over the batch: lengths (INVALID first), then the pages it takes,
-  // copies included, with the reference counts as the batch changes them.
-  struct Pending {
-    int32_t len;
-    size_t pages;
-    int32_t last;  // last page id, or -1 for none / a page taken in this batch
-  };
-  std::unordered_map<uint64_t, int32_t> lens;
-  for (int32_t i = 0; i < n; ++i) {
-    if (new_lens[i] < 0) return PF_ERR_INVALID;
-    auto lit = lens.find(seq_ids[i]);
-    int32_t cur_len = 0;
-    if (lit != lens.end()) {
-      cur_len = lit->second;
-    } else {
+  return guarded([&]() -> int {
+    if (n_copies) *n_copies = 0;
+    if (!pool || n < 0 || (n > 0 && (!seq_ids || !new_lens || !copies || !n_copies))) return PF_ERR_INVALID;
+    if (n_new_pages)
+      for (int32_t i = 0; i < n; ++i) n_new_pages[i] = 0;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    const int64_t B = pool->g.block_size;
+    // Dry run over the batch: lengths (INVALID first), then the pages it takes,
+    // copies included, with the reference counts as the batch changes them.
+    struct Pending {
+      int32_t len;
+      size_t pages;
+      int32_t last;  // last page id, or -1 for none / a page taken in this batch
+    };
+    std::unordered_map<uint64_t, int32_t> lens;
+    for (int32_t i = 0; i < n; ++i) {
+      if (new_lens[i] < 0) return PF_ERR_INVALID;
+      auto lit = lens.find(seq_ids[i]);
+      int32_t cur_len = 0;
+      if (lit != lens.end()) {
+        cur_len = lit->second;
+      } else {
+        auto it = pool->seqs.find(seq_ids[i]);
+        if (it != pool->seqs.end()) cur_len = it->second.len;
+      }
+      if (new_lens[i] < cur_len) return PF_ERR_INVALID;
+      lens[seq_ids[i]] = new_lens[i];
+    }
+    for (int32_t i = 0; i < n; ++i) {
       auto it = pool->seqs.find(seq_ids[i]);
-      if (it != pool->seqs.end()) cur_len = it->second.len;
+      if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
     }
-    if (new_lens[i] < cur_len) return PF_ERR_INVALID;
-    lens[seq_ids[i]] = new_lens[i];
-  }
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = pool->seqs.find(seq_ids[i]);
-    if (it != pool->seqs.end() && it->second.swapped) return PF_ERR_SWAPPED;
-  }
-  std::unordered_map<uint64_t, Pending> pending;
-  std::unordered_map<int32_t, int32_t> dref;  // reference count changes of the batch
-  size_t total = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    Pending cur{0, 0, -1};
-    auto pit = pending.find(seq_ids[i]);
-    if (pit != pending.end()) {
-      cur = pit->second;
-    } else {
-      auto it = pool->seqs.find(seq_ids[i]);
-      if (it != pool->seqs.end())
-        cur = {it->second.len, it->second.pages.size(), it->second.pages.empty() ? -1 : it->second.pages.back()};
+    std::unordered_map<uint64_t, Pending> pending;
+    std::unordered_map<int32_t, int32_t> dref;  // reference count changes of the batch
+    size_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      Pending cur{0, 0, -1};
+      auto pit = pending.find(seq_ids[i]);
+      if (pit != pending.end()) {
+        cur = pit->second;
+      } else {
+        auto it = pool->seqs.find(seq_ids[i]);
+        if (it != pool->seqs.end())
+          cur = {it->second.len, it->second.pages.size(), it->second.pages.empty() ? -1 : it->second.pages.back()};
+      }
+      const bool cow = new_lens[i] > cur.len && cur.len % B != 0 && cur.last >= 0 &&
+                       pool->refs[(size_t)cur.last] + dref[cur.last] > 1;
+      const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+      total += want - cur.pages + (cow ? 1 : 0);
+      if (cow) {
+        --dref[cur.last];
+        cur.last = -1;
+      }
+      if (want > cur.pages) cur.last = -1;
+      pending[seq_ids[i]] = {new_lens[i], want, cur.last};
     }
-    const bool cow = new_lens[i] > cur.len && cur.len % B != 0 && cur.last >= 0 &&
-                     pool->refs[(size_t)cur.last] + dref[cur.last] > 1;
-    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
-    total += want - cur.pages + (cow ? 1 : 0);
-    if (cow) {
-      --dref[cur.last];
-      cur.last = -1;
+    if (total > pool->stack.size()) return PF_ERR_OOM;
+    int32_t nc = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      pf_seq_entry& e = pool->seqs[seq_ids[i]];
+      int32_t taken = 0;
+      if (writes_shared(pool, e, new_lens[i])) {
+        const int32_t src = e.pages.back();
+        const int32_t dst = pop_page(pool);
+        --pool->refs[(size_t)src];
+        e.pages.back() = dst;
+        copies[2 * nc] = src;
+        copies[2 * nc + 1] = dst;
+        ++nc;
+        ++taken;
+      }
+      const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
+      while (e.pages.size() < want) {
+        e.pages.push_back(pop_page(pool));
+        ++taken;
+      }
+      if (taken) e.ver = ++pool->ver_clock;
+      e.len = new_lens[i];
+      if (n_new_pages) n_new_pages[i] = taken;
     }
-    if (want > cur.pages) cur.last = -1;
-    pending[seq_ids[i]] = {new_lens[i], want, cur.last};
-  }
-  if (total > pool->stack.size()) return PF_ERR_OOM;
-  int32_t nc = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    pf_seq_entry& e = pool->seqs[seq_ids[i]];
-    int32_t taken = 0;
-    if (writes_shared(pool, e, new_lens[i])) {
-      const int32_t src = e.pages.back();
-      const int32_t dst = pop_page(pool);
-      --pool->refs[(size_t)src];
-      e.pages.back() = dst;
-      copies[2 * nc] = src;
-      copies[2 * nc + 1] = dst;
-      ++nc;
-      ++taken;
-    }
-    const size_t want = (size_t)(((int64_t)new_lens[i] + B - 1) / B);
-    while (e.pages.size() < want) {
-      e.pages.push_back(pop_page(pool));
-      ++taken;
-    }
-    if (taken) e.ver = ++pool->ver_clock;
-    e.len = new_lens[i];
-    if (n_new_pages) n_new_pages[i] = taken;
-  }
-  *n_copies = nc;
-  return PF_OK;
+    *n_copies = nc;
+    return PF_OK;
+  });
 }
 
 int pf_swap_bind(pf_pool* pool, void* host_ptr, size_t bytes, int32_t num_slots) {
-  if (!pool || num_slots < 0 || (num_slots > 0 && !host_ptr)) return PF_ERR_INVALID;
-  if (reinterpret_cast<uintptr_t>(host_ptr) % 16 != 0) return PF_ERR_INVALID;
-  size_t need = 0;
-  if (!mul_ok(pool->page_elems * pool->elem_bytes, (size_t)num_slots, &need) || bytes < need)
-    return PF_ERR_INVALID;
-  std::lock_guard<std::mutex> lk(pool->mu);
-  for (const auto& kv : pool->seqs)
-    if (kv.second.swapped) return PF_ERR_INVALID;  // slots in use
-  pool->host = num_slots > 0 ? host_ptr : nullptr;
-  pool->num_slots = num_slots;
-  pool->slot_stack.resize((size_t)num_slots);
-  for (int32_t i = 0; i < num_slots; ++i) pool->slot_stack[(size_t)(num_slots - 1 - i)] = i;
-  return PF_OK;
+  return guarded([&]() -> int {
+    if (!pool || num_slots < 0 || (num_slots > 0 && !host_ptr)) return PF_ERR_INVALID;
+    if (reinterpret_cast<uintptr_t>(host_ptr) % 16 != 0) return PF_ERR_INVALID;
+    size_t need = 0;
+    if (!mul_ok(pool->page_elems * pool->elem_bytes, (size_t)num_slots, &need) || bytes < need)
+      return PF_ERR_INVALID;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    for (const auto& kv : pool->seqs)
+      if (kv.second.swapped) return PF_ERR_INVALID;  // slots in use
+    pool->host = num_slots > 0 ? host_ptr : nullptr;
+    pool->num_slots = num_slots;
+    pool->slot_stack.resize((size_t)num_slots);
+    for (int32_t i = 0; i < num_slots; ++i) pool->slot_stack[(size_t)(num_slots - 1 - i)] = i;
+    return PF_OK;
+  });
 }
 
 int32_t pf_swap_free_slots(const pf_pool* pool) {
@@ -431,81 +454,83 @@ void pf_export_forget(const pf_pool* pool) {
 
 int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_ids, int32_t n,
                    int32_t max_blocks, bool step, int32_t* out, int64_t* pairs) {
-  if (!pool || !pairs || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
-  std::lock_guard<std::mutex> lk(pool->mu);
-  std::vector<const pf_seq_entry*> rows((size_t)n);
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = pool->seqs.find(seq_ids[i]);
-    if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
-    if (it->second.swapped) return PF_ERR_SWAPPED;
-    if (it->second.pages.size() > (size_t)max_blocks) return PF_ERR_INVALID;
-    rows[(size_t)i] = &it->second;
-  }
-  const size_t nb = (size_t)n * (size_t)max_blocks;
-  int32_t* lens = out + nb;
-  int32_t* newest = lens + n;
-  const int32_t B = pool->g.block_size;
-  for (int32_t i = 0; i < n; ++i) {
-    const pf_seq_entry& e = *rows[(size_t)i];
-    lens[i] = e.len;
-    newest[i] = e.len - 1;
-    if (step) newest[n + i] = e.len > 0 ? e.pages[(size_t)((e.len - 1) / B)] : -1;
-  }
-  pf_export_shadow& sh = pool->shadow;
-  bool delta = pool->export_delta && sh.target == target && target != nullptr && sh.max_blocks == max_blocks &&
-               sh.ids.size() == (size_t)n && std::equal(sh.ids.begin(), sh.ids.end(), seq_ids);
-  if (delta) {
-    const int64_t cap = (int64_t)nb / 2;
-    int64_t k = 0;
-    for (int32_t i = 0; i < n && delta; ++i) {
-      const pf_seq_entry& e = *rows[(size_t)i];
-      if (e.ver == sh.ver[(size_t)i]) continue;
-      const int32_t np = (int32_t)e.pages.size();
-      const int32_t hi = np > sh.used[(size_t)i] ? np : sh.used[(size_t)i];
-      int32_t* old = sh.table.data() + (size_t)i * (size_t)max_blocks;
-      for (int32_t j = 0; j < hi; ++j) {
-        const int32_t cur = j < np ? e.pages[(size_t)j] : -1;
-        if (cur == old[j]) continue;
-        if (k == cap) {  // more changes than the staging holds as pairs: export whole
-          delta = false;
-          break;
-        }
-        out[2 * k] = i * max_blocks + j;
-        out[2 * k + 1] = cur;
-        old[j] = cur;
-        ++k;
-      }
-      sh.ver[(size_t)i] = e.ver;
-      sh.used[(size_t)i] = np;
-    }
-    if (delta) {
-      *pairs = k;
-      return PF_OK;
-    }
-  }
-  for (int32_t i = 0; i < n; ++i) {
-    const pf_seq_entry& e = *rows[(size_t)i];
-    int32_t* row = out + (size_t)i * (size_t)max_blocks;
-    const size_t np = e.pages.size();
-    if (np) std::memcpy(row, e.pages.data(), np * sizeof(int32_t));
-    for (size_t j = np; j < (size_t)max_blocks; ++j) row[j] = -1;
-  }
-  *pairs = -1;
-  if (pool->export_delta && target != nullptr) {
-    sh.target = target;
-    sh.max_blocks = max_blocks;
-    sh.ids.assign(seq_ids, seq_ids + n);
-    sh.ver.resize((size_t)n);
-    sh.used.resize((size_t)n);
+  return guarded([&]() -> int {
+    if (!pool || !pairs || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    std::vector<const pf_seq_entry*> rows((size_t)n);
     for (int32_t i = 0; i < n; ++i) {
-      sh.ver[(size_t)i] = rows[(size_t)i]->ver;
-      sh.used[(size_t)i] = (int32_t)rows[(size_t)i]->pages.size();
+      auto it = pool->seqs.find(seq_ids[i]);
+      if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+      if (it->second.swapped) return PF_ERR_SWAPPED;
+      if (it->second.pages.size() > (size_t)max_blocks) return PF_ERR_INVALID;
+      rows[(size_t)i] = &it->second;
     }
-    sh.table.assign(out, out + nb);
-  } else {
-    export_forget_locked(pool);
-  }
-  return PF_OK;
+    const size_t nb = (size_t)n * (size_t)max_blocks;
+    int32_t* lens = out + nb;
+    int32_t* newest = lens + n;
+    const int32_t B = pool->g.block_size;
+    for (int32_t i = 0; i < n; ++i) {
+      const pf_seq_entry& e = *rows[(size_t)i];
+      lens[i] = e.len;
+      newest[i] = e.len - 1;
+      if (step) newest[n + i] = e.len > 0 ? e.pages[(size_t)((e.len - 1) / B)] : -1;
+    }
+    pf_export_shadow& sh = pool->shadow;
+    bool delta = pool->export_delta && sh.target == target && target != nullptr && sh.max_blocks == max_blocks &&
+                 sh.ids.size() == (size_t)n && std::equal(sh.ids.begin(), sh.ids.end(), seq_ids);
+    if (delta) {
+      const int64_t cap = (int64_t)nb / 2;
+      int64_t k = 0;
+      for (int32_t i = 0; i < n && delta; ++i) {
+        const pf_seq_entry& e = *rows[(size_t)i];
+        if (e.ver == sh.ver[(size_t)i]) continue;
+        const int32_t np = (int32_t)e.pages.size();
+        const int32_t hi = np > sh.used[(size_t)i] ? np : sh.used[(size_t)i];
+        int32_t* old = sh.table.data() + (size_t)i * (size_t)max_blocks;
+        for (int32_t j = 0; j < hi; ++j) {
+          const int32_t cur = j < np ? e.pages[(size_t)j] : -1;
+          if (cur == old[j]) continue;
+          if (k == cap) {  // more changes than the staging holds as pairs: export whole
+            delta = false;
+            break;
+          }
+          out[2 * k] = i * max_blocks + j;
+          out[2 * k + 1] = cur;
+          old[j] = cur;
+          ++k;
+        }
+        sh.ver[(size_t)i] = e.ver;
+        sh.used[(size_t)i] = np;
+      }
+      if (delta) {
+        *pairs = k;
+        return PF_OK;
+      }
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      const pf_seq_entry& e = *rows[(size_t)i];
+      int32_t* row = out + (size_t)i * (size_t)max_blocks;
+      const size_t np = e.pages.size();
+      if (np) std::memcpy(row, e.pages.data(), np * sizeof(int32_t));
+      for (size_t j = np; j < (size_t)max_blocks; ++j) row[j] = -1;
+    }
+    *pairs = -1;
+    if (pool->export_delta && target != nullptr) {
+      sh.target = target;
+      sh.max_blocks = max_blocks;
+      sh.ids.assign(seq_ids, seq_ids + n);
+      sh.ver.resize((size_t)n);
+      sh.used.resize((size_t)n);
+      for (int32_t i = 0; i < n; ++i) {
+        sh.ver[(size_t)i] = rows[(size_t)i]->ver;
+        sh.used[(size_t)i] = (int32_t)rows[(size_t)i]->pages.size();
+      }
+      sh.table.assign(out, out + nb);
+    } else {
+      export_forget_locked(pool);
+    }
+    return PF_OK;
+  });
 }
 
 extern "C" {
@@ -584,6 +609,7 @@ const char* pf_status_string(int status) {
     case PF_ERR_UNSUPPORTED: return "unsupported block size or head dim";
     case PF_ERR_SHARED: return "growth would write into a page another sequence shares (use pf_grow_seqs)";
     case PF_ERR_SWAPPED: return "sequence is swapped out";
+    case PF_ERR_HOST_MEMORY: return "host memory for the handle state ran out";
     default: return "unknown status";
   }
 }
@@ -596,61 +622,63 @@ const char* pf_status_string(int status) {
 // Returns a status; *pairs receives the number of pairs written.
 int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host, int32_t* out,
                  int64_t out_words, int32_t* pairs) {
-  *pairs = 0;
-  if (!pool || n < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
-  std::lock_guard<std::mutex> lk(pool->mu);
-  if (!pool->dev || !pool->host) return PF_ERR_UNBOUND;
-  std::unordered_map<uint64_t, int> seen;
-  size_t total = 0;
-  for (int32_t i = 0; i < n; ++i)
-    if (seen[seq_ids[i]]++) return PF_ERR_INVALID;
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = pool->seqs.find(seq_ids[i]);
-    if (to_host) {
-      if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
-      if (it->second.swapped) return PF_ERR_SWAPPED;
-      total += it->second.pages.size();
-    } else {
-      if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
-      if (!it->second.swapped) return PF_ERR_INVALID;
-      total += it->second.slots.size();
-    }
-  }
-  if (total > (to_host ? pool->slot_stack.size() : pool->stack.size())) return PF_ERR_OOM;
-  if ((int64_t)total * 2 > out_words) return PF_ERR_INVALID;
-  int32_t k = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    pf_seq_entry& e = pool->seqs.find(seq_ids[i])->second;
-    if (to_host) {
-      e.slots.clear();
-      for (int32_t page : e.pages) {
-        const int32_t slot = pool->slot_stack.back();
-        pool->slot_stack.pop_back();
-        e.slots.push_back(slot);
-        out[2 * k] = page;
-        out[2 * k + 1] = slot;
-        ++k;
+  return guarded([&]() -> int {
+    *pairs = 0;
+    if (!pool || n < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (!pool->dev || !pool->host) return PF_ERR_UNBOUND;
+    std::unordered_map<uint64_t, int> seen;
+    size_t total = 0;
+    for (int32_t i = 0; i < n; ++i)
+      if (seen[seq_ids[i]]++) return PF_ERR_INVALID;
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = pool->seqs.find(seq_ids[i]);
+      if (to_host) {
+        if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+        if (it->second.swapped) return PF_ERR_SWAPPED;
+        total += it->second.pages.size();
+      } else {
+        if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+        if (!it->second.swapped) return PF_ERR_INVALID;
+        total += it->second.slots.size();
       }
-      for (size_t j = e.pages.size(); j-- > 0;)
-        if (--pool->refs[(size_t)e.pages[j]] == 0) pool->stack.push_back(e.pages[j]);
-      e.pages.clear();
-      e.ver = ++pool->ver_clock;
-      e.swapped = true;
-    } else {
-      e.pages.clear();
-      for (int32_t slot : e.slots) {
-        const int32_t page = pop_page(pool);
-        e.pages.push_back(page);
-        out[2 * k] = slot;
-        out[2 * k + 1] = page;
-        ++k;
-      }
-      for (size_t j = e.slots.size(); j-- > 0;) pool->slot_stack.push_back(e.slots[j]);
-      e.slots.clear();
-      e.ver = ++pool->ver_clock;
-      e.swapped = false;
     }
-  }
-  *pairs = k;
-  return PF_OK;
+    if (total > (to_host ? pool->slot_stack.size() : pool->stack.size())) return PF_ERR_OOM;
+    if ((int64_t)total * 2 > out_words) return PF_ERR_INVALID;
+    int32_t k = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      pf_seq_entry& e = pool->seqs.find(seq_ids[i])->second;
+      if (to_host) {
+        e.slots.clear();
+        for (int32_t page : e.pages) {
+          const int32_t slot = pool->slot_stack.back();
+          pool->slot_stack.pop_back();
+          e.slots.push_back(slot);
+          out[2 * k] = page;
+          out[2 * k + 1] = slot;
+          ++k;
+        }
+        for (size_t j = e.pages.size(); j-- > 0;)
+          if (--pool->refs[(size_t)e.pages[j]] == 0) pool->stack.push_back(e.pages[j]);
+        e.pages.clear();
+        e.ver = ++pool->ver_clock;
+        e.swapped = true;
+      } else {
+        e.pages.clear();
+        for (int32_t slot : e.slots) {
+          const int32_t page = pop_page(pool);
+          e.pages.push_back(page);
+          out[2 * k] = slot;
+          out[2 * k + 1] = page;
+          ++k;
+        }
+        for (size_t j = e.slots.size(); j-- > 0;) pool->slot_stack.push_back(e.slots[j]);
+        e.slots.clear();
+        e.ver = ++pool->ver_clock;
+        e.swapped = false;
+      }
+    }
+    *pairs = k;
+    return PF_OK;
+  });
 }

@@ -30,6 +30,7 @@ PF_ERR_HIP = -6
 PF_ERR_UNSUPPORTED = -7
 PF_ERR_SHARED = -8
 PF_ERR_SWAPPED = -9
+PF_ERR_HOST_MEMORY = -10
 
 PF_OPT_SPLIT_TOKENS = 0
 PF_OPT_GQA_MFMA = 1
