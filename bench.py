@@ -188,6 +188,19 @@ def run_gpu(args, name, frames, steps, warmup, flush):
             kv.attention(layer, q[layer], out_t[layer], mc)
             ev_d[r][layer].record(stream)
     torch.cuda.synchronize()
+    # the scatter alone: one pf_scatter_kv launch writing every sequence's
+    # newest token of layer 0 (the bytes it already holds), flushed first
+    tok_seq = torch.arange(w.n, dtype=torch.int32, device=dev)
+    tok_pos = torch.from_numpy((ctx_per_step[-1] - 1).astype(np.int32)).to(dev)
+    ev_s = [(TimingEvent(), TimingEvent()) for _ in range(attn_iters + 5)]
+    for r in range(attn_iters + 5):
+        if flush:
+            flush_buf.amax()
+        ev_s[r][0].record(stream)
+        kv.scatter(0, newk[0], newv[0], tok_seq, tok_pos)
+        ev_s[r][1].record(stream)
+    torch.cuda.synchronize()
+    sc_ms = [a.elapsed_time(b) for a, b in ev_s[5:]]
 
     timed = range(warmup, warmup + steps)
     evsteps = range(warmup + steps, total_steps)
@@ -225,6 +238,12 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         "kv_GBps": round(float(np.median(attn_call_bytes)) / (attn_med_ms * 1e-3) / 1e9, 1),
         "pct_hbm_peak": round(float(np.median(attn_call_bytes)) / (attn_med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 1),
         "seqs_per_ms": round(w.n / (attn_med_ms * w.layers), 2)}
+    sc_med = float(np.median(sc_ms))
+    scatter = {
+        "what": "one pf_scatter_kv launch (every sequence's newest token, one layer), events around it, "
+                "cache flushed first; 5 untimed first",
+        "launches": len(sc_ms), "median_us": round(sc_med * 1e3, 2), "min_us": round(float(np.min(sc_ms)) * 1e3, 2),
+        "alg_bytes": alg_bytes_scatter(w), "GBps": round(alg_bytes_scatter(w) / (sc_med * 1e-3) / 1e9, 1)}
     return dict(
         w=w, name=name, frames=frames, ms_step=ms_step, ms_step_wall=ms_step_wall,
         ms_step_events=ms_step_events, value=avg_step_bytes / (ms_step * 1e-3) / 1e9,
@@ -233,7 +252,7 @@ def run_gpu(args, name, frames, steps, warmup, flush):
         part_sd_us=float(np.std(part_ms)) * 1e3,
         attn_bytes=avg_attn_bytes, achieved=achieved, split=split, waves=waves, mfma=bool(mfma),
         whole=bool(split) and split >= max_ctx_final,
-        kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers), attention=attention)
+        kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers), attention=attention, scatter=scatter)
 
 
 def run_twin(name, frames, reps):
@@ -778,7 +797,8 @@ def main():
             "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
             "seqs_per_ms": round(r["seqs_per_ms"], 2), "ms_per_step": round(r["ms_step"], 4),
             "attn_partition_avg_us": round(r["part_avg_us"], 2),
-            "attn_partition_GBps": round(r["achieved"], 1), "attention": r["attention"], "config": describe(r)}
+            "attn_partition_GBps": round(r["achieved"], 1), "attention": r["attention"], "scatter": r["scatter"],
+            "config": describe(r)}
     # PageFault's pending "cost of scattering pages": shuffled / ordered median
     # attention time (partition + merge)
     cost = {}
@@ -809,6 +829,7 @@ def main():
         "seqs_per_ms": round(head["seqs_per_ms"], 2),
         "ms_per_step_wall": round(head["ms_step_wall"], 4),
         "attention": head["attention"],
+        "scatter": head["scatter"],
         "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": traffic[0] if traffic else None,
