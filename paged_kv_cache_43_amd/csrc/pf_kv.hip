@@ -138,8 +138,8 @@ struct PrepArgs {
   uint4* dst;
   int64_t n16;
   const int2* pairs;         // incremental export: npairs (flat index, value)
-  int32_t* table;
-  int64_t npairs;
+  int32_t* table;            // n * max_blocks entries
+  int64_t npairs, table_words;
   const int32_t* tail_src;   // words after the n16 (whole) or lengths + newest (incremental)
   int32_t* tail_dst;
   int64_t tail;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
     if (i < a.n16) a.dst[i] = a.src[i];
     if (i < a.npairs) {
       const int2 pr = a.pairs[i];
-      a.table[pr.x] = pr.y;
+      if (pr.x >= 0 && pr.x < a.table_words) a.table[pr.x] = pr.y;  // staging rewritten too early: no stray write
     }
     if (i < a.tail) a.tail_dst[i] = a.tail_src[i];
     return;
@@ -293,6 +293,7 @@ static int stage_export(const pf_pool* pool, const uint64_t* seq_ids, int32_t n,
     a.npairs = pairs;
     a.pairs = reinterpret_cast<const int2*>(staging_host);
     a.table = meta_dev;
+    a.table_words = nb;
     a.tail = 2 * (int64_t)n;
     a.tail_src = staging_host + nb;
     a.tail_dst = meta_dev + nb;
