@@ -97,16 +97,31 @@ struct ValuWave {
   const AttnArgs& a;
   const int lane, dc, tq;
   float qf[S::VEC];
+  Raw<S::NW> qnx;  // the next item's q bits, loaded ahead (prefetch)
+  int64_t qn_key = -1;
   float m, l, acc[S::VEC];
 
   static constexpr bool kContig = CONTIG;
 
   __device__ ValuWave(const AttnArgs& args, int ln) : a(args), lane(ln), dc(ln % S::LPT), tq(ln / S::LPT) {}
 
-  // Start a piece of (sequence s, query head h): q in log2 units, empty state.
-  __device__ inline void begin(int s, int h) {
+  __device__ inline Raw<S::NW> load_q(int s, int h) const {
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) + ((((int64_t)s * a.hq + h) * D) + dc * S::VEC) * S::ES;
-    Raw<S::NW> r = load_raw<S::NW>(qp);
+    return load_raw<S::NW>(qp);
+  }
+
+  // Issue the q load of the item that follows in this wave's stream, so that
+  // its begin() does not wait behind the page loads in flight (see the
+  // matrix-core kernel).  key = s * items + h.
+  __device__ inline void prefetch(int s, int h, int64_t key) {
+    qnx = load_q(s, h);
+    qn_key = key;
+  }
+
+  // Start a piece of (sequence s, query head h), item key (or -1): q in log2
+  // units, empty state.
+  __device__ inline void begin(int s, int h, int64_t key = -1) {
+    const Raw<S::NW> r = key >= 0 && key == qn_key ? qnx : load_q(s, h);
     widen_words<T, S::NW>(r, qf);
 #pragma unroll
     for (int i = 0; i < S::VEC; ++i) qf[i] *= a.qscale;

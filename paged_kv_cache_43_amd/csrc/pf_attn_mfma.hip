@@ -122,6 +122,8 @@ struct MfmaWave {
   const int lane, col, grp;
   const bool head_ok;
   uint4 qop[KC];
+  uint4 qnx[KC];  // the next item's Q^T operand, loaded ahead (prefetch)
+  int64_t qn_key = -1;
   float m, l;  // running max (log2 units) of head col; this lane's share of the sum
   f4 acc[DB];
 
@@ -130,15 +132,35 @@ struct MfmaWave {
 
   static constexpr bool kContig = CONTIG;
 
-  // Start a piece of (sequence s, kv head hk): the Q^T operand (head col, dims
-  // 32c + 8*grp .. +8; zero rows past the group) and an empty state.
-  __device__ inline void begin(int s, int hk) {
+  // The Q^T operand of (sequence s, kv head hk): head col, dims 32c + 8*grp
+  // .. +8; zero rows past the group.
+  __device__ inline void load_q(int s, int hk, uint4* dst) const {
     const int head = hk * a.group + col;
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) + (((int64_t)s * a.hq + (head_ok ? head : 0)) * D) * ES;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       uint4 v = *reinterpret_cast<const uint4*>(qp + (32 * c + 8 * grp) * ES);
-      qop[c] = head_ok ? v : make_uint4(0, 0, 0, 0);
+      dst[c] = head_ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Issue the loads of the item that follows in this wave's stream, so that
+  // its begin() finds q in registers: a begin() that loads q waits behind
+  // every page load in flight and drains the page pipeline (measured: waves
+  // that switch item mid-slice finished 2.3 us later).  key = s * items + hk.
+  __device__ inline void prefetch(int s, int hk, int64_t key) {
+    load_q(s, hk, qnx);
+    qn_key = key;
+  }
+
+  // Start a piece of (sequence s, kv head hk), item key (or -1): q and an
+  // empty state.
+  __device__ inline void begin(int s, int hk, int64_t key = -1) {
+    if (key >= 0 && key == qn_key) {
+#pragma unroll
+      for (int c = 0; c < KC; ++c) qop[c] = qnx[c];
+    } else {
+      load_q(s, hk, qop);
     }
     // Pin q in registers, complete, here: begin() runs on a rarely taken
     // branch inside the page loop.  Left alone, the compiler re-loads q at

@@ -188,7 +188,15 @@ __device__ inline void sched_run(const AttnArgs& a, const SchedLds& L, int X, Wv
             cx = x;
             cP = __builtin_amdgcn_readlane(lP, i);
             cp0 = p;
-            w.begin(s, x);
+            w.begin(s, x, cur);
+            // the next item of this batch, if any: load its q now
+            const uint64_t nxt =
+                __builtin_amdgcn_ballot_w64(lane > i && lane < cnt && ls * X + lx != cur);
+            if (nxt) {
+              const int j = __builtin_ctzll(nxt);
+              const int s2 = __builtin_amdgcn_readlane(ls, j), x2 = __builtin_amdgcn_readlane(lx, j);
+              w.prefetch(s2, x2, s2 * X + x2);
+            }
           }
           cplast = p;
           if (p == cP - 1) w.patch_last(t, __builtin_amdgcn_readlane(lnv, i), s, x, __builtin_amdgcn_readlane(lpage, i), ok);
