@@ -77,7 +77,7 @@ def alg_bytes_attention(ctx, w, out_bytes):
     ctx = np.asarray(ctx, dtype=np.int64)
     kv = int(ctx.sum()) * w.hkv * w.d * 2 * w.es
     qo = w.n * w.hq * w.d * (w.es + out_bytes)
-    tables = int(((ctx + 15) // 16).sum()) * 4
+    tables = int(((ctx + w.block - 1) // w.block).sum()) * 4
     return kv + qo + tables + 4 * w.n
 
 
