@@ -412,7 +412,7 @@ def run_cow(prompts, beam, reps, seed=43):
         pf.check(pf.pf_paged_decode_attention(h, 0, q, H, bt, mb, ctx, n, mc, 0.0, out, "f16", ws, need))
         pf.check(pf.pf_pool_set_timing_events(h, None, None))
     torch.cuda.synchronize()
-    alg = alg_bytes_attention(new, type("W", (), dict(n=n, hq=H, hkv=H, d=D, es=2))(), 2)
+    alg = alg_bytes_attention(new, type("W", (), dict(n=n, hq=H, hkv=H, d=D, es=2, block=B))(), 2)
     for tag in ("shared", "private"):
         t = float(np.median([a.elapsed_time(b) * 1e3 for i, ((a, b), x) in enumerate(zip(ev, order))
                              if x == tag and i >= 6]))
@@ -534,7 +534,7 @@ def run_block_sweep(names, blocks, reps):
             torch.cuda.synchronize()
             t = float(np.median([a.elapsed_time(e) * 1e3 for a, e in ev[3:]]))
             pages = (w.ctx + b - 1) // b
-            alg = alg_bytes_attention(w.ctx, w, w.es) - int(((w.ctx + 15) // 16).sum()) * 4 + int(pages.sum()) * 4
+            alg = alg_bytes_attention(w.ctx, w, w.es)   # table entries at this page size
             rows[str(b)] = {"partition_us": round(t, 2), "alg_GBps": round(alg / t / 1e3, 1),
                             "pct_hbm_peak": round(100 * alg / t / 1e3 / HBM_PEAK_GBS, 1),
                             "kernel": "mfma" if pf.pf_attention_kernel(kv.h, w.hq) == 1 else "valu",
@@ -667,7 +667,7 @@ def cpu_baseline(name, budget_s, max_workers=16):
     qd = oa.decode_bits(qb[0], w.dtype)
     g = w.hq // w.hkv
     sc = oa.default_scale(w.d)
-    wl = type("W", (), dict(hq=w.hq, hkv=w.hkv, d=w.d, es=w.es))
+    wl = type("W", (), dict(hq=w.hq, hkv=w.hkv, d=w.d, es=w.es, block=w.block))
 
     # one thread, whole passes over all sequences
     t0 = time.perf_counter()

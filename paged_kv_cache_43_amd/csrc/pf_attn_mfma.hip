@@ -248,8 +248,8 @@ struct MfmaWave {
     const bool over = (z[0] > lim) | (z[1] > lim) | (z[2] > lim) | (z[3] > lim);
     if (__builtin_amdgcn_ballot_w64(over)) {
       float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      pm = fmaxf(pm, shfl_xor(pm, 16));
-      pm = fmaxf(pm, shfl_xor(pm, 32));
+      pm = xor16<OpMax>(pm);
+      pm = xor32<OpMax>(pm);
       const float mn = fmaxf(m, pm);
       const float alpha = fast_exp2(m - mn);
       m = mn;
@@ -322,8 +322,8 @@ struct MfmaWave {
   // col * rec_mul of each query head.
   __device__ inline void finish(int s, int hk, bool whole, int64_t rec_base, int64_t rec_mul) {
     // the four k-groups hold disjoint tokens of the same heads: add their sums
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
+    l = xor16<OpSum>(l);
+    l = xor32<OpSum>(l);
     if (!head_ok) return;
     const int64_t row = (int64_t)s * a.hq + hk * a.group + col;
     if (whole) {

@@ -114,7 +114,22 @@ __device__ inline float dpp(float v) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ inline float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+// v op v[lane ^ 16] and v op v[lane ^ 32] with gfx950's lane swaps:
+// v_permlane16_swap / v_permlane32_swap of v with itself leave the pair
+// {v[lane & ~16], v[lane | 16]} (resp. 32) in every lane, a VALU operation,
+// where a shuffle across 16-lane rows is a ds_bpermute round trip through the
+// LDS crossbar.  + and max are commutative, so the result is the shuffle's
+// bit for bit (checked on the hardware: lane layout as stated).
+template <class Op>
+__device__ inline float xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <class Op>
+__device__ inline float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 struct OpSum {
   __device__ static inline float f(float a, float b) { return a + b; }
@@ -130,8 +145,8 @@ __device__ inline float group_reduce(float v) {
   if constexpr (G >= 4) v = Op::f(v, dpp<kDppXor2>(v));
   if constexpr (G >= 8) v = Op::f(v, dpp<kDppRowHalfMirror>(v));
   if constexpr (G >= 16) v = Op::f(v, dpp<kDppRowMirror>(v));
-  if constexpr (G >= 32) v = Op::f(v, shfl_xor(v, 16));
-  if constexpr (G >= 64) v = Op::f(v, shfl_xor(v, 32));
+  if constexpr (G >= 32) v = xor16<Op>(v);
+  if constexpr (G >= 64) v = xor32<Op>(v);
   return v;
 }
 
@@ -142,8 +157,8 @@ __device__ inline float strided_reduce(float v) {
   if constexpr (G <= 2) v = Op::f(v, dpp<kDppRowRor + 2>(v));
   if constexpr (G <= 4) v = Op::f(v, dpp<kDppRowRor + 4>(v));
   if constexpr (G <= 8) v = Op::f(v, dpp<kDppRowRor + 8>(v));
-  if constexpr (G <= 16) v = Op::f(v, shfl_xor(v, 16));
-  if constexpr (G <= 32) v = Op::f(v, shfl_xor(v, 32));
+  if constexpr (G <= 16) v = xor16<Op>(v);
+  if constexpr (G <= 32) v = xor32<Op>(v);
   return v;
 }
 
