@@ -80,7 +80,8 @@ bool mfma_supports(int head_dim);
 int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, bool contig, hipStream_t st);
 // The same for a pool of block_size 32 or 64 (balanced schedule, paged).
 int launch_mfma_bs(const AttnArgs& a, int dtype, int head_dim, int block_size, hipStream_t st);
-// Resident waves per CU of the balanced matrix-core kernel (0 if unknown).
-int mfma_balanced_waves_per_cu(int dtype, int head_dim);
+// The balanced matrix-core kernel of the default page size (for occupancy
+// queries), or null.
+const void* mfma_balanced_kernel(int dtype, int head_dim);
 
 }  // namespace pf

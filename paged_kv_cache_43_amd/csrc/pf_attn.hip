@@ -29,7 +29,10 @@
 //    exponentials are exp2.
 // Work is assigned by the balanced schedule (pf_sched.h) or by fixed context
 // splits; both end with the same merge.
+#include <atomic>
 #include <cmath>
+#include <mutex>
+#include <vector>
 
 #include "pf_attn.h"
 #include "pf_common.h"
@@ -520,31 +523,54 @@ static bool valu_supports(int dtype, int D) {
   }
 }
 
-// Compute units of the current device (256 on MI355X if the query fails).
+// Compute units of the current device (256 on MI355X if the query fails),
+// asked once per device; the cache may be filled by several threads at once.
 static int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
       (void)hipGetLastError();
       return 256;
     }
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
-// Resident waves per CU of a balanced kernel (16 if the query fails).
+// Resident waves per CU of a balanced kernel (16 if the query fails), asked
+// of the runtime once per kernel and device: the answer depends only on the
+// kernel's resources, and the query would otherwise run on every call.
 static int occupancy_waves(const void* kernel, size_t lds) {
+  struct Entry {
+    const void* kernel;
+    int dev, waves;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    dev = -1;
+  }
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry& e : cache)
+      if (e.kernel == kernel && e.dev == dev) return e.waves;
+  }
   int blocks = 0;
+  int waves = 16;
   if (!kernel || hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kSchedThreads, lds) != hipSuccess ||
       blocks <= 0) {
     (void)hipGetLastError();
-    return 16;
+  } else {
+    waves = blocks * (kSchedThreads / kWave);
   }
-  return blocks * (kSchedThreads / kWave);
+  std::lock_guard<std::mutex> lk(mu);
+  cache.push_back({kernel, dev, waves});
+  return waves;
 }
 
 }  // namespace pf
@@ -606,14 +632,10 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
     // clearly faster for the second (fewer pieces, fewer partial records).
     int per_cu = pool->waves_per_cu;
     if (per_cu <= 0) {
-      int occ;
-      if (p.mfma) {
-        occ = mfma_balanced_waves_per_cu(g.dtype, g.head_dim);
-      } else {
-        const void* k = g.dtype == PF_F32 ? valu_ptr_dtype<ElF32>(g.head_dim)
-                        : (g.dtype == PF_F16 ? valu_ptr_dtype<ElF16>(g.head_dim) : valu_ptr_dtype<ElBF16>(g.head_dim));
-        occ = occupancy_waves(k, 0);
-      }
+      const void* k = p.mfma ? mfma_balanced_kernel(g.dtype, g.head_dim)
+                      : g.dtype == PF_F32 ? valu_ptr_dtype<ElF32>(g.head_dim)
+                      : (g.dtype == PF_F16 ? valu_ptr_dtype<ElF16>(g.head_dim) : valu_ptr_dtype<ElBF16>(g.head_dim));
+      const int occ = occupancy_waves(k, 0);
       per_cu = occ > 0 && occ < 8 ? occ : 8;
     }
     const int64_t wpg = kSchedThreads / kWave;

@@ -472,21 +472,14 @@ int launch_mfma_bs(const AttnArgs& a, int dtype, int head_dim, int block_size, h
                          : launch_bs_t<ElBF16>(a, head_dim, block_size, st);
 }
 
-int mfma_balanced_waves_per_cu(int dtype, int head_dim) {
-  const void* k = nullptr;
+const void* mfma_balanced_kernel(int dtype, int head_dim) {
   if (head_dim == 64)
-    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 64, 1, false, false>)
-                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 64, 1, false, false>);
-  else if (head_dim == 128)
-    k = dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 128, 1, false, false>)
-                        : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 128, 1, false, false>);
-  int blocks = 0;
-  if (!k || hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, kSchedThreads, 0) != hipSuccess ||
-      blocks <= 0) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  return blocks * (kSchedThreads / kWave);
+    return dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 64, 1, false, false>)
+                           : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 64, 1, false, false>);
+  if (head_dim == 128)
+    return dtype == PF_F16 ? reinterpret_cast<const void*>(&attn_mfma_balanced<ElF16, 128, 1, false, false>)
+                           : reinterpret_cast<const void*>(&attn_mfma_balanced<ElBF16, 128, 1, false, false>);
+  return nullptr;
 }
 
 }  // namespace pf
