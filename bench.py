@@ -37,6 +37,8 @@ WORKLOADS = {
     "mixed": "Mixed-length: 32 seqs, 50% U[32,128] / 30% U[256,512] / 20% U[1024,2048], 12 heads, d_head 64, fp16, block 16, pool 4096, {frames} frames",
     "13b": "13B-style: 40 heads, d_head 128, fp16, one layer's decode, 64 seqs, context U[256,2048], block 16, pool 1.1x blocks used, {frames} frames",
     "gqa": "GQA large batch: 14 q heads / 2 kv heads, d_head 64, bf16, 256 seqs, context U[1024,4096], block 16, pool 70k pages after 500x16 alloc/free churn, {frames} frames",
+    "13b_32k": "13B-style at 32k-token contexts: 40 heads, d_head 128, fp16, one layer's decode, 2 seqs, context U[30720,32768], block 16, pool 1.1x blocks used, {frames} frames",
+    "gqa_32k": "GQA at 32k-token contexts: 14 q heads / 2 kv heads, d_head 64, bf16, 32 seqs, context U[30720,32768], block 16, pool 1.1x blocks used, {frames} frames",
 }
 
 
@@ -105,12 +107,14 @@ class TimingEvent:
         return self.m.elapsed_ms(stop.m)
 
 
-def run_gpu(args, name, frames, steps, warmup, flush):
+def run_gpu(args, name, frames, steps, warmup, flush, share=None):
     import torch
     from paged_kv_cache_43_amd import inputs, pf, runner
 
     dev = "cuda"
     w = inputs.Workload(name, frames=frames)
+    if share is not None:
+        w.share_values(share)   # the other frame order's draws (identical values)
     ksteps = min(steps, 20)
     kv = runner.PagedKV(w, device=dev, sentinel=False, extra_tokens=steps + ksteps + warmup + 1)
     q = runner.fill_workload(kv, device=dev)
@@ -747,7 +751,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="13b", choices=sorted(WORKLOADS))
     ap.add_argument("--frames", default="shuffled", choices=["shuffled", "ordered"])
-    ap.add_argument("--also", default="gqa,mixed,gpt2,tiny",
+    ap.add_argument("--also", default="gqa,13b_32k,gqa_32k,mixed,gpt2,tiny",
                     help="comma list of extra configs reported beside the headline (both frame orders)")
     ap.add_argument("--flush", choices=["on", "off"], default="on",
                     help="read a 1 GiB buffer before every step, outside the step's events (default on)")
@@ -787,11 +791,18 @@ def main():
     head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, args.flush == "on")
     others = {}
     head_ordered = run_gpu(args, args.config, "ordered" if args.frames == "shuffled" else "shuffled",
-                           args.steps, args.warmup, args.flush == "on")
+                           args.steps, args.warmup, args.flush == "on", share=head["w"])
+    head["w"]._values = head_ordered["w"]._values = None   # the drawn values are no longer needed
     runs = [(args.config, head_ordered)]
     for extra in [x for x in args.also.split(",") if x and x != args.config]:
+        first = None
         for fr in ("shuffled", "ordered"):
-            runs.append((extra, run_gpu(args, extra, fr, args.steps, args.warmup, args.flush == "on")))
+            r = run_gpu(args, extra, fr, args.steps, args.warmup, args.flush == "on",
+                        share=first["w"] if first else None)
+            if first is not None:
+                first["w"]._values = r["w"]._values = None   # the drawn values are no longer needed
+            first = first or r
+            runs.append((extra, r))
     for name, r in runs:
         others["%s_%s" % (name, r["frames"])] = {
             "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),

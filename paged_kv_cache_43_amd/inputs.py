@@ -23,6 +23,10 @@ Shapes follow the workloads on the pages and the ones derived from them:
   256 sequences with context U[1024,4096], 70 000-page pool that went through
   500 alloc/free cycles of 16 sequences first (PageForge, "Allocator stress
   test").
+* ``13b_32k`` -- the 13B-style layer at 32k-token contexts: 2 sequences with
+  context U[30720,32768], fp16, pool sized to 1.1x the blocks in use.
+* ``gqa_32k`` -- the grouped-query shape at 32k-token contexts: 32 sequences
+  with context U[30720,32768], bf16, pool sized to 1.1x the blocks in use.
 
 Randomness: ``numpy.random.SeedSequence(seed).spawn(4)`` gives independent
 PCG64 streams for lengths, frame order, churn and values.  Values are drawn in
@@ -53,6 +57,10 @@ CONFIGS = {
                 lens=("uniform", 256, 2048), seed=3, churn=None),
     "gqa": dict(n=256, layers=1, hq=14, hkv=2, d=64, dtype="bf16", pool=70000,
                 lens=("uniform", 1024, 4096), seed=4, churn=(500, 16, 4096)),
+    "13b_32k": dict(n=2, layers=1, hq=40, hkv=40, d=128, dtype="f16", pool="1.1x",
+                    lens=("uniform", 30720, 32768), seed=5, churn=None),
+    "gqa_32k": dict(n=32, layers=1, hq=14, hkv=2, d=64, dtype="bf16", pool="1.1x",
+                    lens=("uniform", 30720, 32768), seed=6, churn=None),
 }
 
 CHURN_SEQ_BASE = 1 << 40
@@ -97,8 +105,23 @@ def to_bits(x, dtype):
     raise ValueError(dtype)
 
 
+# Values drawn per chunk by normal_bits (float64 scratch of this many).
+NORMAL_CHUNK = 1 << 22
+
+
 def normal_bits(gen, shape, dtype):
-    return to_bits(gen.standard_normal(size=shape), dtype)
+    """N(0,1) draws of ``shape`` as ``dtype`` bit patterns.  The draws go in
+    chunks through one reused float64 buffer: the generator produces the same
+    sequence as a single call of the full size, without a full-size float64
+    array (long contexts hold billions of values)."""
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint32 if dtype == "f32" else np.uint16)
+    buf = np.empty(max(min(n, NORMAL_CHUNK), 0))
+    for a in range(0, n, NORMAL_CHUNK):
+        x = buf[: min(n - a, NORMAL_CHUNK)]
+        gen.standard_normal(out=x)
+        out[a:a + len(x)] = to_bits(x, dtype)
+    return out.reshape(shape)
 
 
 def churn_ops(gen, cycles, seqs_per_cycle, max_len):
@@ -186,6 +209,19 @@ class Workload:
 
     def max_blocks(self, extra_tokens=0):
         return int(-(-(int(self.ctx.max()) + extra_tokens) // self.block)) if self.n else 1
+
+    def share_values(self, other):
+        """Take ``other``'s drawn K/V/q instead of drawing them again.  Values
+        come from their own generator stream, so two workloads of the same
+        configuration and seed that differ only in frame order (or page size)
+        draw identical values; this checks that the shapes and lengths agree."""
+        same = (self.seed == other.seed and self.n == other.n and self.layers == other.layers and
+                self.hq == other.hq and self.hkv == other.hkv and self.d == other.d and
+                self.dtype == other.dtype and np.array_equal(self.ctx, other.ctx))
+        if not same:
+            raise ValueError("share_values: workloads differ in seed, geometry or lengths")
+        self._values = other.values()
+        return self
 
     def values(self):
         """K/V bits per sequence ``[L][ctx_s][Hkv][D]`` and q bits ``[L][n][Hq][D]``."""

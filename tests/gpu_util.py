@@ -37,11 +37,15 @@ def oracle_attention_contiguous(w, layer, seqs=None, scale=None):
     qd = oa.decode_bits(q[layer], w.dtype)
     g = w.hq // w.hkv
     sc = oa.default_scale(w.d) if scale is None else scale
+    ks, vs, _ = w.values()
     out = np.zeros((len(seqs), w.hq, w.d))
     for i, s in enumerate(seqs):
-        K, V = decoded(w, s, layer)
-        for h in range(w.hq):
-            out[i, h] = oa.attention(qd[s, h], K[:, h // g, :], V[:, h // g, :], sc)
+        # one kv head at a time: contiguous [len][D] slices, no whole-sequence float64 copy
+        for hk in range(w.hkv):
+            K = oa.decode_bits(np.ascontiguousarray(ks[s][layer][:, hk, :]), w.dtype)
+            V = oa.decode_bits(np.ascontiguousarray(vs[s][layer][:, hk, :]), w.dtype)
+            for h in range(hk * g, (hk + 1) * g):
+                out[i, h] = oa.attention(qd[s, h], K, V, sc)
     return out
 
 

@@ -64,17 +64,18 @@ def test_attention_parity_small_configs(name, out_dtype, sched):
     kv.close()
 
 
-@pytest.mark.parametrize("name", ["tiny", "gpt2", "mixed", "13b", "gqa"])
+@pytest.mark.parametrize("name", ["tiny", "gpt2", "mixed", "13b", "gqa", "13b_32k", "gqa_32k"])
 def test_ordered_equals_shuffled_bitwise(name):
     print("ordered vs shuffled", name, flush=True)
-    a, kva, _ = _run(inputs.Workload(name, frames="ordered"))
+    wa = inputs.Workload(name, frames="ordered")
+    a, kva, _ = _run(wa)
     kva.close()
-    b, kvb, _ = _run(inputs.Workload(name, frames="shuffled"))
+    b, kvb, _ = _run(inputs.Workload(name, frames="shuffled").share_values(wa))
     kvb.close()
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["mixed", "gqa"])
+@pytest.mark.parametrize("name", ["mixed", "gqa", "gqa_32k"])
 def test_schedules_agree(name):
     """Fixed splits and the balanced schedule (several wave counts, so the
     slices fall differently) give the same results to fp32 rounding."""
@@ -90,7 +91,7 @@ def test_schedules_agree(name):
     kv.close()
 
 
-@pytest.mark.parametrize("name", ["13b", "gqa"])
+@pytest.mark.parametrize("name", ["13b", "gqa", "13b_32k", "gqa_32k"])
 def test_attention_parity_full_size(name):
     """The bench's configurations at full size, in the launch configuration it
     times; every output against the oracle on the generated K/V, and sampled
@@ -107,11 +108,24 @@ def test_attention_parity_full_size(name):
     model = gu.oracle_tables(w)
     g = gu.geometry(w)
     rng = np.random.default_rng(1)
-    sample = sorted(rng.choice(w.n, size=3, replace=False).tolist())
-    _, _, qb = w.values()
-    paged = oa.paged_decode_attention(qb[0][sample], pool, g, 0, [model.table(s) for s in sample],
-                                      [int(w.ctx[s]) for s in sample], w.dtype)
-    assert np.array_equal(paged, ref[sample])
+    ks, vs, qb = w.values()
+    if int(w.ctx.max()) <= 4096:
+        sample = sorted(rng.choice(w.n, size=3, replace=False).tolist())
+        paged = oa.paged_decode_attention(qb[0][sample], pool, g, 0, [model.table(s) for s in sample],
+                                          [int(w.ctx[s]) for s in sample], w.dtype)
+        assert np.array_equal(paged, ref[sample])
+    else:
+        # 32k-token contexts: one sequence read back through its table (bit-exact
+        # against the drawn K/V) and a few heads attended from the read-back bits
+        s = int(rng.integers(w.n))
+        kc, vc = ol.readback(pool, g, 0, model.table(s), int(w.ctx[s]))
+        assert np.array_equal(kc, ks[s][0]) and np.array_equal(vc, vs[s][0])
+        qd = oa.decode_bits(qb[0][s], w.dtype)
+        grp = w.hq // w.hkv
+        for h in sorted(rng.choice(w.hq, size=4, replace=False).tolist()):
+            K = oa.decode_bits(np.ascontiguousarray(kc[:, h // grp, :]), w.dtype)
+            V = oa.decode_bits(np.ascontiguousarray(vc[:, h // grp, :]), w.dtype)
+            assert np.array_equal(oa.attention(qd[h], K, V, oa.default_scale(w.d)), ref[s, h])
     kv.close()
 
 
