@@ -514,14 +514,14 @@ def run_block_sweep(names, blocks, reps):
     out = {}
     for name in names:
         rows = {}
-        values = None
+        first = None
         for b in blocks:
             w = inputs.Workload(name, frames="shuffled", block=b)
-            if values is not None:
-                w._values = values
+            if first is not None:
+                w.share_values(first)   # values do not depend on the page size
+            first = first or w
             kv = runner.PagedKV(w, sentinel=False)
             q = runner.fill_workload(kv)
-            values = w._values
             mc = int(w.ctx.max())
             kv.ensure_workspace(mc)
             o = torch.empty((w.n, w.hq, w.d), dtype=torch.int32 if w.es == 4 else torch.int16, device="cuda")
@@ -792,15 +792,17 @@ def main():
     others = {}
     head_ordered = run_gpu(args, args.config, "ordered" if args.frames == "shuffled" else "shuffled",
                            args.steps, args.warmup, args.flush == "on", share=head["w"])
-    head["w"]._values = head_ordered["w"]._values = None   # the drawn values are no longer needed
+    head["w"].drop_values()
+    head_ordered["w"].drop_values()
     runs = [(args.config, head_ordered)]
     for extra in [x for x in args.also.split(",") if x and x != args.config]:
         first = None
         for fr in ("shuffled", "ordered"):
             r = run_gpu(args, extra, fr, args.steps, args.warmup, args.flush == "on",
                         share=first["w"] if first else None)
-            if first is not None:
-                first["w"]._values = r["w"]._values = None   # the drawn values are no longer needed
+            if first is not None:   # both frame orders done: the drawn values are no longer needed
+                first["w"].drop_values()
+                r["w"].drop_values()
             first = first or r
             runs.append((extra, r))
     for name, r in runs:

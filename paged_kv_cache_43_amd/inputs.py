@@ -166,7 +166,7 @@ class Workload:
         self.name = name
         self.seed = cfg["seed"] if seed is None else seed
         self.frames = frames
-        g_len, g_frame, g_churn, g_val = streams(self.seed)
+        g_len, g_frame, g_churn, _ = streams(self.seed)
         self.n = cfg["n"] if n is None else n
         self.layers, self.hq, self.hkv, self.d = cfg["layers"], cfg["hq"], cfg["hkv"], cfg["d"]
         self.dtype = cfg["dtype"]
@@ -204,7 +204,6 @@ class Workload:
             ops += [("alloc", s, max(int(self.ctx[s]) - 1, 0)) for s in range(self.n)]
         self.history_ops = ops
         self.step_ops = [("alloc", s, int(self.ctx[s])) for s in range(self.n)]
-        self._g_val = g_val
         self._values = None
 
     def max_blocks(self, extra_tokens=0):
@@ -223,10 +222,14 @@ class Workload:
         self._values = other.values()
         return self
 
+    def drop_values(self):
+        """Forget the drawn values (they are drawn again on the next use)."""
+        self._values = None
+
     def values(self):
         """K/V bits per sequence ``[L][ctx_s][Hkv][D]`` and q bits ``[L][n][Hq][D]``."""
         if self._values is None:
-            g = self._g_val
+            g = streams(self.seed)[3]   # a fresh values stream: a redraw gives the same values
             ks, vs = [], []
             for s in range(self.n):
                 shape = (self.layers, int(self.ctx[s]), self.hkv, self.d)

@@ -42,3 +42,12 @@ def test_32k_context_workloads(name, n):
     assert w.num_pages == int(np.ceil(1.1 * used))
     assert sorted(w.free_order.tolist()) == list(range(w.num_pages))
     assert len(w.step_ops) == n and w.max_blocks() <= 2048
+
+
+def test_dropped_values_redraw_identically():
+    w = inputs.Workload("tiny")
+    ks, vs, q = w.values()
+    ks, vs, q = [a.copy() for a in ks], [a.copy() for a in vs], q.copy()
+    w.drop_values()
+    ks2, vs2, q2 = w.values()
+    assert all(np.array_equal(a, b) for a, b in zip(ks + vs + [q], ks2 + vs2 + [q2]))
