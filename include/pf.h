@@ -396,7 +396,8 @@ typedef enum {
                               (16-token pages, no split-tokens option set: no merge launch), else
                               balanced if n <= 2048, else fixed splits; 1: fixed splits;
                               2: balanced (n <= 2048) */
-  PF_OPT_WAVES_PER_CU = 3, /* balanced schedule: waves launched per compute unit; 0 = resident capacity */
+  PF_OPT_WAVES_PER_CU = 3, /* balanced schedule: waves launched per compute unit; 0 (default) = 8,
+                              or the kernel's resident capacity per CU if that is lower */
   PF_OPT_EXPORT_DELTA = 4  /* 0 (default): pf_export_tables / pf_decode_prepare upload the whole table;
                               1: they upload only the entries that differ from the previous export to
                               the same meta_dev with the same seq_ids and max_blocks (lengths and
