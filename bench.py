@@ -35,6 +35,7 @@ WORKLOADS = {
     "tiny": "Tiny: 4 seqs, 1 layer, 2 heads, d_head 16, fp32, block 16, pool 64 pages, context U[1,64], {frames} frames",
     "gpt2": "GPT-2-124M shape: 12 layers x 12 heads, d_head 64, fp16, 32 seqs, prompts U[8,64] + 50 decode steps, block 16, pool 1024 pages, {frames} frames",
     "mixed": "Mixed-length: 32 seqs, 50% U[32,128] / 30% U[256,512] / 20% U[1024,2048], 12 heads, d_head 64, fp16, block 16, pool 4096, {frames} frames",
+    "mixed_s7": "Mixed-length, seed 7: 32 seqs, 50% U[32,128] / 30% U[256,512] / 20% U[1024,2048], 12 heads, d_head 64, fp16, block 16, pool 4096, {frames} frames",
     "13b": "13B-style: 40 heads, d_head 128, fp16, one layer's decode, 64 seqs, context U[256,2048], block 16, pool 1.1x blocks used, {frames} frames",
     "gqa": "GQA large batch: 14 q heads / 2 kv heads, d_head 64, bf16, 256 seqs, context U[1024,4096], block 16, pool 70k pages after 500x16 alloc/free churn, {frames} frames",
     "13b_32k": "13B-style at 32k-token contexts: 40 heads, d_head 128, fp16, one layer's decode, 2 seqs, context U[30720,32768], block 16, pool 1.1x blocks used, {frames} frames",
@@ -751,7 +752,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="13b", choices=sorted(WORKLOADS))
     ap.add_argument("--frames", default="shuffled", choices=["shuffled", "ordered"])
-    ap.add_argument("--also", default="gqa,13b_32k,gqa_32k,mixed,gpt2,tiny",
+    ap.add_argument("--also", default="gqa,13b_32k,gqa_32k,mixed,mixed_s7,gpt2,tiny",
                     help="comma list of extra configs reported beside the headline (both frame orders)")
     ap.add_argument("--flush", choices=["on", "off"], default="on",
                     help="read a 1 GiB buffer before every step, outside the step's events (default on)")

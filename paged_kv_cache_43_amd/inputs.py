@@ -15,7 +15,9 @@ Shapes follow the workloads on the pages and the ones derived from them:
   1024-page pool.
 * ``mixed``  -- PageFault's "Stage 2: memory" traffic mix: 50 % U[32,128],
   30 % U[256,512], 20 % U[1024,2048]; 12 heads, head dim 64, fp16,
-  4096-page pool.
+  4096-page pool.  ``mixed_s7`` is the same mix drawn from seed 7 (PageFault
+  reports the mix under seeds 42 and 7; its lengths come from another
+  generator, so only the recipe is shared).
 * ``13b``    -- a 13B-style layer (PagedAttention blog, opening section:
   40 heads of dimension 128): 64 sequences with context U[256,2048], fp16,
   pool sized to 1.1x the blocks in use.
@@ -53,6 +55,8 @@ CONFIGS = {
                  lens=("prompt_decode", 8, 64, 50), seed=1, churn=None),
     "mixed": dict(n=32, layers=1, hq=12, hkv=12, d=64, dtype="f16", pool=4096,
                   lens=("mix",), seed=42, churn=None),
+    "mixed_s7": dict(n=32, layers=1, hq=12, hkv=12, d=64, dtype="f16", pool=4096,
+                     lens=("mix",), seed=7, churn=None),
     "13b": dict(n=64, layers=1, hq=40, hkv=40, d=128, dtype="f16", pool="1.1x",
                 lens=("uniform", 256, 2048), seed=3, churn=None),
     "gqa": dict(n=256, layers=1, hq=14, hkv=2, d=64, dtype="bf16", pool=70000,

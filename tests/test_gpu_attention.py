@@ -49,7 +49,7 @@ def _run(w, layer=0, out_dtype=None, split=None, mfma=None, kv=None, q=None, sch
 
 
 @pytest.mark.parametrize("sched", [SCHED_GRID, SCHED_BALANCED])
-@pytest.mark.parametrize("name", ["tiny", "gpt2", "mixed"])
+@pytest.mark.parametrize("name", ["tiny", "gpt2", "mixed", "mixed_s7"])
 @pytest.mark.parametrize("out_dtype", ["f32", None])
 def test_attention_parity_small_configs(name, out_dtype, sched):
     print("parity", name, out_dtype, sched, flush=True)
@@ -64,7 +64,7 @@ def test_attention_parity_small_configs(name, out_dtype, sched):
     kv.close()
 
 
-@pytest.mark.parametrize("name", ["tiny", "gpt2", "mixed", "13b", "gqa", "13b_32k", "gqa_32k"])
+@pytest.mark.parametrize("name", ["tiny", "gpt2", "mixed", "mixed_s7", "13b", "gqa", "13b_32k", "gqa_32k"])
 def test_ordered_equals_shuffled_bitwise(name):
     print("ordered vs shuffled", name, flush=True)
     wa = inputs.Workload(name, frames="ordered")
