@@ -71,7 +71,7 @@ def test_twin_small_configs(name, sched):
     kv.close()
 
 
-@pytest.mark.parametrize("name", ["13b", "gqa"])
+@pytest.mark.parametrize("name", ["13b", "gqa", "13b_32k", "gqa_32k"])
 def test_twin_full_size(name):
     """The bench's configurations at full size and default options (the
     launch configuration it times)."""
