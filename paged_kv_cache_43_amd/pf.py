@@ -122,12 +122,39 @@ def check(status, what="libpf"):
     return status
 
 
-def _dev(x):
-    """Device address of a torch tensor, an int address, or None."""
-    if x is None:
-        return None
-    if isinstance(x, int):
+def _kind(x):
+    if isinstance(x, np.ndarray):
+        return "a numpy array"
+    return "a %s tensor" % ("device" if getattr(x, "is_cuda", False) else "host")
+
+
+def _dev(x, strided=False):
+    """Device address of a GPU torch tensor (contiguous unless ``strided``), an
+    int address (taken as is), or None.  Host tensors and numpy arrays are
+    refused here: a kernel given their address would fault."""
+    if x is None or isinstance(x, int):
         return x
+    if isinstance(x, np.ndarray) or not getattr(x, "is_cuda", False):
+        raise ValueError("expected a device tensor or an int address, got " + _kind(x))
+    if not strided and not x.is_contiguous():
+        raise ValueError("expected a contiguous device tensor")
+    return x.data_ptr()
+
+
+def _pinned(x, device_ok=False):
+    """Address of pinned host memory that a kernel reads or writes over the
+    host link: a contiguous pinned CPU tensor (``pin_memory``), or with
+    ``device_ok`` also a contiguous device tensor; an int address is taken as
+    is.  Pageable host memory is refused (a kernel cannot reach it)."""
+    if x is None or isinstance(x, int):
+        return x
+    if device_ok and getattr(x, "is_cuda", False):
+        return _dev(x)
+    if isinstance(x, np.ndarray) or getattr(x, "is_cuda", False) or not x.is_pinned():
+        got = _kind(x) if isinstance(x, np.ndarray) or x.is_cuda else "a pageable host tensor"
+        raise ValueError("expected pinned host memory (pin_memory) or an int address, got " + got)
+    if not x.is_contiguous():
+        raise ValueError("expected a contiguous pinned host tensor")
     return x.data_ptr()
 
 
@@ -242,7 +269,7 @@ def pf_page_refcount(pool, page):
 
 def pf_swap_bind(pool, host_ptr, nbytes, num_slots):
     """``host_ptr``: pinned host tensor / address."""
-    return lib.pf_swap_bind(pool, _dev(host_ptr), nbytes, num_slots)
+    return lib.pf_swap_bind(pool, _pinned(host_ptr), nbytes, num_slots)
 
 
 def pf_swap_free_slots(pool):
@@ -257,7 +284,7 @@ def pf_seq_swapped(pool, seq_id):
 
 def _swap(fn, pool, seq_ids, staging, staging_words, stream):
     ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
-    return fn(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), _dev(staging), staging_words,
+    return fn(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), _pinned(staging), staging_words,
               _stream(stream))
 
 
@@ -272,7 +299,7 @@ def pf_swap_in(pool, seq_ids, staging, staging_words, stream=None):
 
 def pf_copy_pages(pool, pairs, n, stream=None):
     """``pairs``: device tensor / pinned host tensor / address of int32 [n][2]."""
-    return lib.pf_copy_pages(pool, _dev(pairs), n, _stream(stream))
+    return lib.pf_copy_pages(pool, _pinned(pairs, device_ok=True), n, _stream(stream))
 
 
 def pf_free_pages(pool):
@@ -386,7 +413,7 @@ def pf_export_tables(pool, seq_ids, max_blocks, staging_host, meta_dev, stream=N
     tensor of at least n*max_blocks + 2n words; ``meta_dev`` a device tensor."""
     ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
     return lib.pf_export_tables(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
-                                _dev(staging_host), _dev(meta_dev), _stream(stream))
+                                _pinned(staging_host), _dev(meta_dev), _stream(stream))
 
 
 def pf_export_staging(pool, seq_ids, max_blocks, meta_dev, step, staging_host):
@@ -406,7 +433,7 @@ def pf_decode_prepare(pool, seq_ids, max_blocks, staging_host, meta_dev, k, v, l
     device [num_layers][n][H][D]."""
     ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
     return lib.pf_decode_prepare(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
-                                 _dev(staging_host), _dev(meta_dev), _dev(k), _dev(v), layer0, num_layers,
+                                 _pinned(staging_host), _dev(meta_dev), _dev(k), _dev(v), layer0, num_layers,
                                  _stream(stream))
 
 
@@ -458,7 +485,8 @@ def pf_paged_decode_attention_append(pool, layer, q, num_q_heads, k_new, v_new, 
 def pf_contiguous_decode_attention(pool, q, num_q_heads, k, v, seq_stride, token_stride, head_stride,
                                    max_len, ctx_dev, n, max_context_len, scale, out, out_dtype, workspace,
                                    workspace_bytes, stream=None):
-    return lib.pf_contiguous_decode_attention(pool, _dev(q), num_q_heads, _dev(k), _dev(v), seq_stride,
+    return lib.pf_contiguous_decode_attention(pool, _dev(q), num_q_heads, _dev(k, strided=True),
+                                              _dev(v, strided=True), seq_stride,
                                               token_stride, head_stride, max_len, _dev(ctx_dev), n,
                                               max_context_len, float(scale), _dev(out),
                                               DTYPES.get(out_dtype, out_dtype), _dev(workspace),

@@ -373,3 +373,27 @@ def test_marker_entry_points_refuse_null():
     assert pf.lib.pf_marker_wait(None) == pf.PF_ERR_INVALID
     assert pf.lib.pf_marker_destroy(None) == pf.PF_ERR_INVALID
     assert pf.lib.pf_marker_elapsed_ms(None, None, None) == pf.PF_ERR_INVALID
+
+
+def test_binding_refuses_memory_a_kernel_cannot_reach():
+    """Marshalling guards of the binding: device arguments must be GPU tensors
+    (contiguous unless the entry point takes strides), memory a kernel reaches
+    over the host link must be pinned; int addresses pass through unchanged."""
+    import torch
+    assert pf._dev(None) is None and pf._dev(1 << 20) == 1 << 20
+    assert pf._pinned(None) is None and pf._pinned(4096) == 4096
+    with pytest.raises(ValueError, match="numpy"):
+        pf._dev(np.zeros(4, dtype=np.int32))
+    with pytest.raises(ValueError, match="host tensor"):
+        pf._dev(torch.zeros(4))
+    with pytest.raises(ValueError, match="pageable"):
+        pf._pinned(torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="numpy"):
+        pf._pinned(np.zeros(4, dtype=np.int32))
+    st, h = pf.pf_pool_create(4, 16, 1, 1, 16, "f16")
+    assert st == pf.PF_OK
+    with pytest.raises(ValueError):
+        pf.pf_scatter_kv(h, 0, torch.zeros(4), torch.zeros(4), None, None, 0, None, 0, 1, stream=0)
+    with pytest.raises(ValueError):
+        pf.pf_copy_pages(h, torch.zeros(2, dtype=torch.int32), 1, stream=0)
+    pf.pf_pool_destroy(h)
