@@ -161,6 +161,45 @@ int pf_alloc_for_seq(pf_pool* pool, uint64_t seq_id, int32_t new_len, int32_t* n
   });
 }
 
+// The common decode-step batch: every id names a distinct live resident
+// sequence.  Resolves each entry once (no per-batch map) and applies the same
+// checks, in the same order, as the general path below.  Returns -1 when the
+// batch does not qualify (an unknown or repeated id): the general path then
+// decides.  Caller holds the lock.
+static int alloc_batch_fast(pf_pool* pool, const uint64_t* ids, const int32_t* lens, int32_t n,
+                            int32_t* n_new_pages) {
+  std::vector<pf_seq_entry*>& ents = pool->batch_entries;
+  ents.resize((size_t)n);
+  const uint64_t epoch = ++pool->batch_epoch;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(ids[i]);
+    if (it == pool->seqs.end() || it->second.batch_mark == epoch) return -1;
+    it->second.batch_mark = epoch;
+    ents[(size_t)i] = &it->second;
+  }
+  const int64_t B = pool->g.block_size;
+  for (int32_t i = 0; i < n; ++i)   // negative lengths included: every length is >= 0
+    if (lens[i] < ents[(size_t)i]->len) return PF_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i)
+    if (ents[(size_t)i]->swapped) return PF_ERR_SWAPPED;
+  size_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const pf_seq_entry& e = *ents[(size_t)i];
+    if (writes_shared(pool, e, lens[i])) return PF_ERR_SHARED;
+    total += (size_t)(((int64_t)lens[i] + B - 1) / B) - e.pages.size();
+  }
+  if (total > pool->stack.size()) return PF_ERR_OOM;
+  for (int32_t i = 0; i < n; ++i) {
+    pf_seq_entry& e = *ents[(size_t)i];
+    const size_t need = (size_t)(((int64_t)lens[i] + B - 1) / B) - e.pages.size();
+    for (size_t j = 0; j < need; ++j) e.pages.push_back(pop_page(pool));
+    if (need) e.ver = ++pool->ver_clock;
+    e.len = lens[i];
+    if (n_new_pages) n_new_pages[i] = (int32_t)need;
+  }
+  return PF_OK;
+}
+
 int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens, int32_t n,
                       int32_t* n_new_pages) {
   return guarded([&]() -> int {
@@ -168,6 +207,8 @@ int pf_alloc_for_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new
     if (n_new_pages)
       for (int32_t i = 0; i < n; ++i) n_new_pages[i] = 0;
     std::lock_guard<std::mutex> lk(pool->mu);
+    const int fast = alloc_batch_fast(pool, seq_ids, new_lens, n, n_new_pages);
+    if (fast != -1) return fast;
     const int64_t B = pool->g.block_size;
     // Validation pass: lengths and page counts as the batch would leave them.
     // A sequence's last page is shared only if it is still the page it had

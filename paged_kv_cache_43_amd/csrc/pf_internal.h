@@ -18,6 +18,7 @@ struct pf_seq_entry {
   // Version of `pages`: set from the pool's clock whenever the table changes,
   // so equal versions mean an equal table (0: never held a page).
   uint64_t ver = 0;
+  uint64_t batch_mark = 0;     // last batch (pool batch_epoch) that named this sequence
 };
 
 // What the device table of the previous export holds once its upload has
@@ -59,6 +60,10 @@ struct pf_pool {
   int32_t waves_per_cu = 0;   // balanced schedule: 0 = resident capacity
   // Clock of table versions (pf_seq_entry::ver).
   uint64_t ver_clock = 0;
+  // Batched growth: epoch stamped into the entries a batch names (finds
+  // repeated ids without a map) and the entries it resolved.
+  uint64_t batch_epoch = 0;
+  std::vector<pf_seq_entry*> batch_entries;
   // Incremental table export (PF_OPT_EXPORT_DELTA) and its shadow.
   int32_t export_delta = 0;
   mutable pf_export_shadow shadow;

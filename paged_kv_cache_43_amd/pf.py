@@ -58,7 +58,7 @@ _SIGS = {
     "pf_page_bytes": (_sz, [_vp]),
     "pf_pool_bind": (_i32, [_vp, _vp, _sz]),
     "pf_alloc_for_seq": (_i32, [_vp, _u64, _i32, _pi32]),
-    "pf_alloc_for_seqs": (_i32, [_vp, ctypes.POINTER(_u64), _pi32, _i32, _pi32]),
+    "pf_alloc_for_seqs": (_i32, [_vp, _vp, _vp, _i32, _vp]),
     "pf_free_seq": (_i32, [_vp, _u64]),
     "pf_fork_seq": (_i32, [_vp, _u64, _u64]),
     "pf_pool_peak_pages": (_i32, [_vp]),
@@ -75,10 +75,10 @@ _SIGS = {
     "pf_num_seqs": (_i32, [_vp]),
     "pf_seq_len": (_i32, [_vp, _u64, _pi32]),
     "pf_block_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _pi32, _pi32]),
-    "pf_export_tables": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _vp, _vp]),
+    "pf_export_tables": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "pf_export_staging": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _i32, _vp,
                                  ctypes.POINTER(ctypes.c_int64)]),
-    "pf_decode_prepare": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+    "pf_decode_prepare": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "pf_scatter_kv": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
     "pf_gather_kv": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pf_attention_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
@@ -169,15 +169,31 @@ def _host_ptr(x):
     return x.data_ptr()
 
 
+def _current_stream_fn():
+    """A function returning the raw handle of torch's current stream, or None
+    without a GPU.  torch's own raw getter costs ~0.2 us per call against
+    ~3 us for torch.cuda.current_stream().cuda_stream (the same value)."""
+    try:
+        import torch
+    except ImportError:
+        return lambda: None
+    if not torch.cuda.is_available():
+        return lambda: None
+    raw, dev = getattr(torch._C, "_cuda_getCurrentRawStream", None), getattr(torch._C, "_cuda_getDevice", None)
+    if raw is not None and dev is not None:
+        return lambda: raw(dev())
+    return lambda: torch.cuda.current_stream().cuda_stream
+
+
+_current_stream = None
+
+
 def _stream(stream):
+    global _current_stream
     if stream is None:
-        try:
-            import torch
-            if torch.cuda.is_available():
-                return torch.cuda.current_stream().cuda_stream
-        except ImportError:
-            pass
-        return None
+        if _current_stream is None:
+            _current_stream = _current_stream_fn()
+        return _current_stream()
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -186,6 +202,17 @@ def _stream(stream):
 def _host_i32(a):
     a = np.ascontiguousarray(a, dtype=np.int32)
     return a, a.ctypes.data_as(_pi32)
+
+
+def _np(a, dtype):
+    """``a`` as a C-contiguous numpy array of ``dtype`` (no copy when it is one)."""
+    if type(a) is np.ndarray and a.dtype == dtype and a.flags.c_contiguous:
+        return a
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _np_ptr(a):
+    return a.__array_interface__["data"][0]
 
 
 # ---------------------------------------------------------------- allocator
@@ -226,11 +253,14 @@ def pf_alloc_for_seq(pool, seq_id, new_len):
 def pf_alloc_for_seqs(pool, seq_ids, new_lens, n_new_out=None):
     """Batch growth; ``seq_ids`` uint64 and ``new_lens`` int32 host arrays.
     Returns (status, n_new_pages array)."""
-    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
-    lens, lens_p = _host_i32(new_lens)
-    nn = np.zeros(len(ids), dtype=np.int32) if n_new_out is None else n_new_out
-    st = lib.pf_alloc_for_seqs(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), lens_p, len(ids),
-                               nn.ctypes.data_as(_pi32))
+    ids = _np(seq_ids, np.uint64)
+    lens = _np(new_lens, np.int32)
+    if len(lens) != len(ids):
+        raise ValueError("seq_ids and new_lens differ in length")
+    nn = np.zeros(len(ids), dtype=np.int32) if n_new_out is None else _np(n_new_out, np.int32)
+    if len(nn) < len(ids):
+        raise ValueError("n_new_out is shorter than seq_ids")
+    st = lib.pf_alloc_for_seqs(pool, _np_ptr(ids), _np_ptr(lens), len(ids), _np_ptr(nn))
     return st, nn
 
 
@@ -411,8 +441,8 @@ def pf_status_string(status):
 def pf_export_tables(pool, seq_ids, max_blocks, staging_host, meta_dev, stream=None):
     """``seq_ids`` a uint64 numpy array; ``staging_host`` a pinned int32 torch
     tensor of at least n*max_blocks + 2n words; ``meta_dev`` a device tensor."""
-    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
-    return lib.pf_export_tables(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
+    ids = _np(seq_ids, np.uint64)
+    return lib.pf_export_tables(pool, _np_ptr(ids), len(ids), max_blocks,
                                 _pinned(staging_host), _dev(meta_dev), _stream(stream))
 
 
@@ -431,8 +461,8 @@ def pf_decode_prepare(pool, seq_ids, max_blocks, staging_host, meta_dev, k, v, l
                       stream=None):
     """``staging_host`` pinned int32 with >= n*max_blocks + 3n words; ``k``, ``v``
     device [num_layers][n][H][D]."""
-    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
-    return lib.pf_decode_prepare(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
+    ids = _np(seq_ids, np.uint64)
+    return lib.pf_decode_prepare(pool, _np_ptr(ids), len(ids), max_blocks,
                                  _pinned(staging_host), _dev(meta_dev), _dev(k), _dev(v), layer0, num_layers,
                                  _stream(stream))
 

@@ -223,3 +223,51 @@ def test_swap_state_without_copies():
     model.check_invariants()
     _same_state(h, model)
     pf.pf_pool_destroy(h)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_distinct_live_batches_replay_oracle(seed):
+    """Batches naming distinct live sequences only (the decode-step batch, which
+    the library resolves on a fast path without a per-batch map): statuses --
+    INVALID first, then SHARED, then OOM -- pages taken, tables and counts
+    agree with the model after every op, across forks, shrink attempts and
+    growth beyond the free pages."""
+    rng = np.random.default_rng(100 + seed)
+    P = 120
+    order = rng.permutation(P).astype(np.int32)
+    h = _make(P, order)
+    model = am.AllocModel(P, 16, order)
+    for s in range(6):
+        ln = int(rng.integers(1, 60))
+        assert STATUS[pf.pf_alloc_for_seq(h, s, ln)[0]] == model.alloc(s, ln)[0]
+    nxt = 6
+    for it in range(500):
+        live = sorted(model.tables)
+        r = rng.random()
+        if r < 0.04 and live:
+            parent = int(rng.choice(live))
+            assert STATUS[pf.pf_fork_seq(h, parent, nxt)] == model.fork(parent, nxt)
+            nxt += 1
+        elif r < 0.2 and len(live) > 2:
+            s = int(rng.choice(live))
+            assert pf.pf_free_seq(h, s) == pf.PF_OK and model.free(s) == am.OK
+        elif r < 0.25:
+            ln = int(rng.integers(0, 40))
+            assert STATUS[pf.pf_alloc_for_seq(h, nxt, ln)[0]] == model.alloc(nxt, ln)[0]
+            nxt += 1
+        elif live:
+            k = int(rng.integers(1, len(live) + 1))
+            ids = [int(x) for x in rng.choice(live, size=k, replace=False)]
+            big = rng.random() < 0.15
+            step = [-1 if rng.random() < 0.01 else int(rng.integers(0, 600 if big else 3)) for _ in ids]
+            new = [model.lengths[s] + d for s, d in zip(ids, step)]
+            st, nn = pf.pf_alloc_for_seqs(h, np.array(ids, dtype=np.uint64), new)
+            want = _plain_batch_reference(model, ids, new)
+            assert STATUS[st] == want, (it, ids, new)
+            if want == am.OK:
+                assert list(nn) == [model.alloc(s, ln)[1] for s, ln in zip(ids, new)]
+            else:
+                assert not nn.any()
+        model.check_invariants()
+        _same_state(h, model)
+    pf.pf_pool_destroy(h)
