@@ -103,6 +103,11 @@ class PagedKV:
         pf.check(pf.pf_pool_set_option(self.h, pf.PF_OPT_EXPORT_DELTA, 1 if delta_export else 0))
         self.ws = None
         self.ws_bytes = 0
+        # device addresses of the handle's own buffers, passed as ints on the
+        # per-layer path (the binding's tensor checks cost ~0.3 us each)
+        self._bt_ptr = self.bt.data_ptr()
+        self._ctx_ptr = self.ctx.data_ptr()
+        self._ws_ptr = None
 
     def close(self):
         if self.h is not None:
@@ -154,14 +159,23 @@ class PagedKV:
         if need > self.ws_bytes:
             self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
             self.ws_bytes = need
+            self._ws_ptr = self.ws.data_ptr()
         return need
 
     def attention(self, layer, q, out, max_ctx, out_dtype=None, scale=0.0, stream=None, hq=None):
+        """One layer's decode attention.  The call is made with the workspace
+        held so far; the library checks its size before launching anything and
+        reports PF_ERR_WORKSPACE, on which the workspace is grown and the call
+        made again (no size query on every call)."""
         hq = hq or self.w.hq
-        self.ensure_workspace(max_ctx, hq)
-        st = pf.pf_paged_decode_attention(self.h, layer, q, hq, self.bt, self.max_blocks, self.ctx,
-                                          self.w.n, max_ctx, scale, out,
-                                          out_dtype or self.w.dtype, self.ws, self.ws_bytes, stream)
+        od = out_dtype or self.w.dtype
+        st = pf.pf_paged_decode_attention(self.h, layer, q, hq, self._bt_ptr, self.max_blocks, self._ctx_ptr,
+                                          self.w.n, max_ctx, scale, out, od, self._ws_ptr, self.ws_bytes, stream)
+        if st == pf.PF_ERR_WORKSPACE:
+            self.ensure_workspace(max_ctx, hq)
+            st = pf.pf_paged_decode_attention(self.h, layer, q, hq, self._bt_ptr, self.max_blocks,
+                                              self._ctx_ptr, self.w.n, max_ctx, scale, out, od, self._ws_ptr,
+                                              self.ws_bytes, stream)
         pf.check(st, "pf_paged_decode_attention")
 
     def attention_append(self, layer, q, k_new, v_new, out, max_ctx, out_dtype=None, scale=0.0, stream=None,
