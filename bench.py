@@ -40,6 +40,7 @@ WORKLOADS = {
     "gqa": "GQA large batch: 14 q heads / 2 kv heads, d_head 64, bf16, 256 seqs, context U[1024,4096], block 16, pool 70k pages after 500x16 alloc/free churn, {frames} frames",
     "13b_32k": "13B-style at 32k-token contexts: 40 heads, d_head 128, fp16, one layer's decode, 2 seqs, context U[30720,32768], block 16, pool 1.1x blocks used, {frames} frames",
     "gqa_32k": "GQA at 32k-token contexts: 14 q heads / 2 kv heads, d_head 64, bf16, 32 seqs, context U[30720,32768], block 16, pool 1.1x blocks used, {frames} frames",
+    "gqa_1m": "GQA, one sequence of 2^20 tokens: 14 q heads / 2 kv heads, d_head 64, bf16, block 16, pool 1.1x blocks used, {frames} frames",
 }
 
 
@@ -760,7 +761,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="13b", choices=sorted(WORKLOADS))
     ap.add_argument("--frames", default="shuffled", choices=["shuffled", "ordered"])
-    ap.add_argument("--also", default="gqa,13b_32k,gqa_32k,mixed,mixed_s7,gpt2,tiny",
+    ap.add_argument("--also", default="gqa,13b_32k,gqa_32k,gqa_1m,mixed,mixed_s7,gpt2,tiny",
                     help="comma list of extra configs reported beside the headline (both frame orders)")
     ap.add_argument("--flush", choices=["on", "off"], default="on",
                     help="read a 1 GiB buffer before every step, outside the step's events (default on)")

@@ -310,8 +310,8 @@ __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) 
 // batch that raises M rescales what is summed so far, so with at most
 // kMergeBatch pieces this is the formula above exactly as written.  Record of
 // row c, piece j: rec0 + j * js + c.  Lanes lie across (row, 4-float chunk):
-// D/4 lanes per row, 64/(D/4) rows per pass; this wave does pass `pass`.  All
-// loads of a batch are issued before any is used.
+// D/4 lanes per row, 64/(D/4) rows per pass; a workgroup does pass `pass`.
+// All loads of a batch are issued before any is used.
 constexpr int kMergeBatch = 8;
 
 template <class T, bool OUT_F32>
@@ -326,20 +326,16 @@ __device__ inline void store_out4(void* out, int64_t idx, const float* v) {
   }
 }
 
-template <class T, bool OUT_F32>
-__device__ inline void merge_rows(const AttnArgs& a, int D, int64_t rec0, int64_t js, int cnt, int rows, int pass,
-                                  int64_t out_row0, int lane) {
-  const int lpr = D / 4;
-  const int c = pass * (kWave / lpr) + lane / lpr;
-  const int q = lane % lpr;
-  if (c >= rows) return;
-  float M = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < cnt; j0 += kMergeBatch) {
+// Pieces [jb, je) of row c, chunk q of 4 floats, folded into (M, den, num)
+// in piece order, kMergeBatch at a time (batch boundaries at jb + 8k).
+__device__ inline void merge_span(const AttnArgs& a, int D, int64_t rec0, int64_t js, int jb, int je, int c, int q,
+                                  float& M, float& den, float* num) {
+  for (int j0 = jb; j0 < je; j0 += kMergeBatch) {
     float2 ml[kMergeBatch];
     float4 av[kMergeBatch];
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
-      if (j0 + b < cnt) {
+      if (j0 + b < je) {
         const int64_t rec = rec0 + (int64_t)(j0 + b) * js + c;
         ml[b] = a.ws_ml[rec];
         av[b] = *reinterpret_cast<const float4*>(a.ws_acc + rec * D + 4 * q);
@@ -368,33 +364,90 @@ __device__ inline void merge_rows(const AttnArgs& a, int D, int64_t rec0, int64_
       num[3] += wj * av[b].w;
     }
   }
+}
+
+template <class T, bool OUT_F32>
+__device__ inline void store_merged(const AttnArgs& a, int D, int64_t out_row0, int c, int q, float den,
+                                    const float* num) {
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const float o[4] = {num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
   store_out4<T, OUT_F32>(a.out, (out_row0 + c) * D + 4 * q, o);
 }
 
-// One wave per (item or query head, pass, sequence).  Balanced schedule: the
-// item's (first record, pieces) pair, records (first + j) * rows_per_item + c;
-// grid schedule: query head h's splits are records row * max_splits + j.
-template <class T, bool OUT_F32, bool BAL>
-__global__ __launch_bounds__(kWave) void attn_merge_kernel(AttnArgs a, int D, int items_per_seq,
-                                                           int rows_per_item, int passes) {
+// Rows of many pieces (one long sequence split over most of the grid) are
+// merged by kMergeWaves waves at once: wave w folds the w-th contiguous run of
+// ceil(cnt / kMergeWaves) pieces, then wave 0 folds the waves' states in wave
+// order, rescaling each to the common max.  The runs depend only on the piece
+// count, so the result is still the same for any physical page order.
+constexpr int kMergeWaves = 8;
+
+// One workgroup per (item or query head, pass, sequence): one wave (W = 1)
+// or kMergeWaves waves (W = kMergeWaves).  Balanced schedule: the item's
+// (first record, pieces) pair, records (first + j) * rows_per_item + c; grid
+// schedule: query head h's splits are records row * max_splits + j.
+template <class T, bool OUT_F32, bool BAL, int W>
+__global__ __launch_bounds__(kWave * W) void attn_merge_kernel(AttnArgs a, int D, int items_per_seq,
+                                                               int rows_per_item, int passes) {
   const int x = blockIdx.x / passes;
   const int pass = blockIdx.x % passes;
   const int s = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
   const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
-  if (ctx == 0) return;
+  if (ctx == 0) return;  // uniform over the workgroup, as are the returns below
+  int64_t rec0, js, out_row0;
+  int cnt, rows;
   if constexpr (BAL) {
     const int2 meta = a.ws_meta[(int64_t)s * items_per_seq + x];
     if (meta.y <= 1) return;
-    merge_rows<T, OUT_F32>(a, D, (int64_t)meta.x * rows_per_item, rows_per_item, meta.y, rows_per_item, pass,
-                           (int64_t)s * a.hq + (int64_t)x * rows_per_item, lane);
+    rec0 = (int64_t)meta.x * rows_per_item;
+    js = rows_per_item;
+    cnt = meta.y;
+    rows = rows_per_item;
+    out_row0 = (int64_t)s * a.hq + (int64_t)x * rows_per_item;
   } else {
-    const int cnt = (ctx + a.split_tokens - 1) / a.split_tokens;
+    cnt = (ctx + a.split_tokens - 1) / a.split_tokens;
     if (cnt <= 1) return;
-    const int64_t row = (int64_t)s * a.hq + x;
-    merge_rows<T, OUT_F32>(a, D, row * a.max_splits, 1, cnt, 1, 0, row, lane);
+    out_row0 = (int64_t)s * a.hq + x;
+    rec0 = out_row0 * a.max_splits;
+    js = 1;
+    rows = 1;
+  }
+  const int lpr = D / 4;
+  const int c = pass * (kWave / lpr) + lane / lpr;
+  const int q = lane % lpr;
+  float M = -INFINITY, den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (W == 1) {
+    if (c >= rows) return;
+    merge_span(a, D, rec0, js, 0, cnt, c, q, M, den, num);
+    store_merged<T, OUT_F32>(a, D, out_row0, c, q, den, num);
+  } else {
+    __shared__ float sm[W][kWave], sd[W][kWave];
+    __shared__ float4 sn[W][kWave];
+    const int per = (cnt + W - 1) / W;
+    const int jb = wave * per, je = min(cnt, jb + per);
+    if (c < rows && jb < je) merge_span(a, D, rec0, js, jb, je, c, q, M, den, num);
+    sm[wave][lane] = M;
+    sd[wave][lane] = den;
+    sn[wave][lane] = make_float4(num[0], num[1], num[2], num[3]);
+    __syncthreads();
+    if (wave != 0 || c >= rows) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) Mt = fmaxf(Mt, sm[w][lane]);
+    float dt = 0.f, nt[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = sm[w][lane];
+      const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - Mt);
+      const float4 v = sn[w][lane];
+      dt += sd[w][lane] * f;
+      nt[0] += f * v.x;
+      nt[1] += f * v.y;
+      nt[2] += f * v.z;
+      nt[3] += f * v.w;
+    }
+    store_merged<T, OUT_F32>(a, D, out_row0, c, q, dt, nt);
   }
 }
 
@@ -499,19 +552,39 @@ static const void* valu_ptr_dtype(int D) {
   }
 }
 
+template <class T, bool BAL, int W>
+static void launch_merge_w(const AttnArgs& a, dim3 grid, int D, int items_per_seq, int rows_per_item, int passes,
+                           hipStream_t st) {
+  if (a.out_f32)
+    hipLaunchKernelGGL((attn_merge_kernel<T, true, BAL, W>), grid, dim3(kWave * W), 0, st, a, D, items_per_seq,
+                       rows_per_item, passes);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<T, false, BAL, W>), grid, dim3(kWave * W), 0, st, a, D, items_per_seq,
+                       rows_per_item, passes);
+}
+
+// Rows expected to hold many pieces -- the balanced schedule's waves spread
+// over few items (16 or more waves per item), or 16 or more fixed splits --
+// are merged kMergeWaves waves per row group; the choice depends only on the
+// call's sizes.  Measured on MI355X, one sequence of 2^20 tokens (GQA shape,
+// ~1000 pieces per row): one wave per row group took ~88 us, about as long as
+// the partition kernel; eight waves take ~15 us, and sixteen are no faster
+// (the few workgroups of such a call are then bound by their CUs' bandwidth).
 template <class T>
 static void launch_merge(const AttnArgs& a, int D, bool balanced, int items_per_seq, int rows_per_item,
                          hipStream_t st) {
   const int rows = balanced ? rows_per_item : 1;
-  const int rpp = kWave / (D / 4);  // rows per pass of merge_rows
+  const int rpp = kWave / (D / 4);  // rows per pass of the merge
   const int passes = (rows + rpp - 1) / rpp;
   const dim3 grid((balanced ? items_per_seq : a.hq) * passes, a.n);
+  const int64_t items = (int64_t)a.n * (balanced ? items_per_seq : a.hq);
+  const bool wide = balanced ? (int64_t)a.waves >= 16 * items : a.max_splits >= 16;
   if (balanced) {
-    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
-    else hipLaunchKernelGGL((attn_merge_kernel<T, false, true>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
+    if (wide) launch_merge_w<T, true, kMergeWaves>(a, grid, D, items_per_seq, rows_per_item, passes, st);
+    else launch_merge_w<T, true, 1>(a, grid, D, items_per_seq, rows_per_item, passes, st);
   } else {
-    if (a.out_f32) hipLaunchKernelGGL((attn_merge_kernel<T, true, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
-    else hipLaunchKernelGGL((attn_merge_kernel<T, false, false>), grid, dim3(kWave), 0, st, a, D, items_per_seq, rows_per_item, passes);
+    if (wide) launch_merge_w<T, false, kMergeWaves>(a, grid, D, items_per_seq, rows_per_item, passes, st);
+    else launch_merge_w<T, false, 1>(a, grid, D, items_per_seq, rows_per_item, passes, st);
   }
 }
 

@@ -29,6 +29,8 @@ Shapes follow the workloads on the pages and the ones derived from them:
   context U[30720,32768], fp16, pool sized to 1.1x the blocks in use.
 * ``gqa_32k`` -- the grouped-query shape at 32k-token contexts: 32 sequences
   with context U[30720,32768], bf16, pool sized to 1.1x the blocks in use.
+* ``gqa_1m`` -- one sequence of 2^20 tokens in the grouped-query shape: the
+  whole grid splits one sequence's context.
 
 Randomness: ``numpy.random.SeedSequence(seed).spawn(4)`` gives independent
 PCG64 streams for lengths, frame order, churn and values.  Values are drawn in
@@ -65,6 +67,8 @@ CONFIGS = {
                     lens=("uniform", 30720, 32768), seed=5, churn=None),
     "gqa_32k": dict(n=32, layers=1, hq=14, hkv=2, d=64, dtype="bf16", pool="1.1x",
                     lens=("uniform", 30720, 32768), seed=6, churn=None),
+    "gqa_1m": dict(n=1, layers=1, hq=14, hkv=2, d=64, dtype="bf16", pool="1.1x",
+                   lens=("uniform", 1 << 20, 1 << 20), seed=8, churn=None),
 }
 
 CHURN_SEQ_BASE = 1 << 40
