@@ -451,6 +451,100 @@ __global__ __launch_bounds__(kWave * W) void attn_merge_kernel(AttnArgs a, int D
   }
 }
 
+// Merge state of one 4-float chunk of a row: running max (log2 units), sum of
+// weights, weighted accumulator chunk.
+struct MergeState {
+  float M, den, num[4];
+};
+
+// Fold two states in the order given (a first): both rescaled to the common max.
+__device__ inline MergeState merge_fold(const MergeState& a, const MergeState& b) {
+  MergeState r;
+  r.M = fmaxf(a.M, b.M);
+  const float fa = a.M == -INFINITY ? 0.f : fast_exp2(a.M - r.M);
+  const float fb = b.M == -INFINITY ? 0.f : fast_exp2(b.M - r.M);
+  r.den = a.den * fa + b.den * fb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r.num[e] = a.num[e] * fa + b.num[e] * fb;
+  return r;
+}
+
+// The states of lanes lane & ~X and lane | X (X = 16 or 32), folded lower lane
+// first, in every lane (gfx950's lane swaps of each value with itself).
+template <int X>
+__device__ inline MergeState merge_fold_lanes(const MergeState& s) {
+  MergeState lo, hi;
+  auto swap = [](float v, float& l, float& h) {
+    const auto r = X == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)
+                           : __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    l = __uint_as_float(r[0]);
+    h = __uint_as_float(r[1]);
+  };
+  swap(s.M, lo.M, hi.M);
+  swap(s.den, lo.den, hi.den);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) swap(s.num[e], lo.num[e], hi.num[e]);
+  return merge_fold(lo, hi);
+}
+
+// Rows of many pieces at head dim 64, 128 or 256: one workgroup of W waves per
+// output row.  A wave's 64 lanes are G = 64 / (D/4) groups, each covering the
+// row's D floats; piece stream t = wave * G + group folds the t-th contiguous
+// run of ceil(pieces / (W * G)) pieces.  Each wave folds its groups by lane
+// swaps (groups 0+1 and 2+3, then the two pairs), wave 0 folds the waves in
+// order through LDS.  The runs depend only on the piece count.
+template <class T, bool OUT_F32, bool BAL, int W>
+__global__ __launch_bounds__(kWave * W) void attn_merge_row_kernel(AttnArgs a, int D, int items_per_seq,
+                                                                   int rows_per_item) {
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int ctx = clamp_ctx(a.ctx[s], a.max_ctx);
+  if (ctx == 0) return;  // uniform over the workgroup, as are the returns below
+  int64_t rec0, js, out_row0;
+  int cnt, c;
+  if constexpr (BAL) {
+    const int x = blockIdx.x / rows_per_item;
+    c = blockIdx.x % rows_per_item;
+    const int2 meta = a.ws_meta[(int64_t)s * items_per_seq + x];
+    if (meta.y <= 1) return;
+    rec0 = (int64_t)meta.x * rows_per_item;
+    js = rows_per_item;
+    cnt = meta.y;
+    out_row0 = (int64_t)s * a.hq + (int64_t)x * rows_per_item;
+  } else {
+    cnt = (ctx + a.split_tokens - 1) / a.split_tokens;
+    if (cnt <= 1) return;
+    out_row0 = (int64_t)s * a.hq + blockIdx.x;
+    rec0 = out_row0 * a.max_splits;
+    js = 1;
+    c = 0;
+  }
+  const int lpr = D / 4;       // 16, 32 or 64 lanes per row
+  const int G = kWave / lpr;   // 4, 2 or 1 streams per wave
+  const int g = lane / lpr, q = lane % lpr;
+  const int per = (cnt + W * G - 1) / (W * G);
+  const int jb = (wave * G + g) * per, je = min(cnt, jb + per);
+  MergeState st{-INFINITY, 0.f, {0.f, 0.f, 0.f, 0.f}};
+  if (jb < je) merge_span(a, D, rec0, js, jb, je, c, q, st.M, st.den, st.num);
+  if (G == 4) st = merge_fold_lanes<16>(st);
+  if (G >= 2) st = merge_fold_lanes<32>(st);
+  __shared__ float sm[W][kWave], sd[W][kWave];
+  __shared__ float4 sn[W][kWave];
+  sm[wave][lane] = st.M;
+  sd[wave][lane] = st.den;
+  sn[wave][lane] = make_float4(st.num[0], st.num[1], st.num[2], st.num[3]);
+  __syncthreads();
+  if (wave != 0 || g != 0) return;
+  MergeState acc{sm[0][lane], sd[0][lane], {sn[0][lane].x, sn[0][lane].y, sn[0][lane].z, sn[0][lane].w}};
+#pragma unroll
+  for (int w = 1; w < W; ++w) {
+    const float4 v = sn[w][lane];
+    acc = merge_fold(acc, MergeState{sm[w][lane], sd[w][lane], {v.x, v.y, v.z, v.w}});
+  }
+  store_merged<T, OUT_F32>(a, D, out_row0, c, q, acc.den, acc.num);
+}
+
 // ---------------------------------------------------------------- launchers
 // Pages per prefetch unit: two units are in flight per wave; a unit holds
 // about 32 VGPRs of K/V per lane.
@@ -552,6 +646,17 @@ static const void* valu_ptr_dtype(int D) {
   }
 }
 
+template <class T, bool BAL>
+static void launch_merge_row(const AttnArgs& a, int D, int items_per_seq, int rows_per_item, hipStream_t st) {
+  const dim3 grid(BAL ? items_per_seq * rows_per_item : a.hq, a.n);
+  if (a.out_f32)
+    hipLaunchKernelGGL((attn_merge_row_kernel<T, true, BAL, kMergeWaves>), grid, dim3(kWave * kMergeWaves), 0, st,
+                       a, D, items_per_seq, rows_per_item);
+  else
+    hipLaunchKernelGGL((attn_merge_row_kernel<T, false, BAL, kMergeWaves>), grid, dim3(kWave * kMergeWaves), 0,
+                       st, a, D, items_per_seq, rows_per_item);
+}
+
 template <class T, bool BAL, int W>
 static void launch_merge_w(const AttnArgs& a, dim3 grid, int D, int items_per_seq, int rows_per_item, int passes,
                            hipStream_t st) {
@@ -579,11 +684,16 @@ static void launch_merge(const AttnArgs& a, int D, bool balanced, int items_per_
   const dim3 grid((balanced ? items_per_seq : a.hq) * passes, a.n);
   const int64_t items = (int64_t)a.n * (balanced ? items_per_seq : a.hq);
   const bool wide = balanced ? (int64_t)a.waves >= 16 * items : a.max_splits >= 16;
+  // few rows in all (one long sequence): one workgroup per row, so the reading
+  // spreads over as many CUs as there are rows
+  const bool per_row = wide && D >= 64 && items * rows <= 256;
   if (balanced) {
-    if (wide) launch_merge_w<T, true, kMergeWaves>(a, grid, D, items_per_seq, rows_per_item, passes, st);
+    if (per_row) launch_merge_row<T, true>(a, D, items_per_seq, rows_per_item, st);
+    else if (wide) launch_merge_w<T, true, kMergeWaves>(a, grid, D, items_per_seq, rows_per_item, passes, st);
     else launch_merge_w<T, true, 1>(a, grid, D, items_per_seq, rows_per_item, passes, st);
   } else {
-    if (wide) launch_merge_w<T, false, kMergeWaves>(a, grid, D, items_per_seq, rows_per_item, passes, st);
+    if (per_row) launch_merge_row<T, false>(a, D, items_per_seq, rows_per_item, st);
+    else if (wide) launch_merge_w<T, false, kMergeWaves>(a, grid, D, items_per_seq, rows_per_item, passes, st);
     else launch_merge_w<T, false, 1>(a, grid, D, items_per_seq, rows_per_item, passes, st);
   }
 }
