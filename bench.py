@@ -8,12 +8,15 @@ attention for every layer (partition kernel + merge).  Inputs are resident in HB
 timed region starts.  Sequences keep growing over the steps; bytes are counted
 from the actual lengths.
 
-Prints ONE JSON line.  ``value`` is the algorithmic KV bandwidth of the whole
-step (attention's K/V + q + out + table + length bytes, plus the scatter's
-reads and writes) over the step time; ``roofline`` is for the attention
-partition kernel alone, timed with HIP events recorded around it on its own
-stream; ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the
-same workload.
+Output: one JSON line per side measurement as it finishes (``{"leg": ...}``:
+each other workload and frame order, the contiguous twin, copy-on-write,
+swapping, fused scatter + attention, the page-size sweep, the CPU baseline's
+details), then, LAST, the headline line, kept under 4 KB.  ``value`` is the
+algorithmic KV bandwidth of the whole step (attention's K/V + q + out + table
++ length bytes, plus the scatter's reads and writes) over the step time;
+``roofline`` is for the attention partition kernel alone, timed with HIP
+events recorded around it on its own stream; ``cpu_baseline`` times the CPU
+fp64 oracle on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -740,6 +743,8 @@ def cpu_baseline(name, budget_s, max_workers=16):
             "sample": "%d sequence-attentions in whole passes, the %d sequences dealt round-robin to %d worker "
                       "processes (one BLAS thread each, %.1f s each, timed from a common barrier), layer 0, all %d "
                       "query heads; decode + fp64 two-pass softmax attention" % (seqs, w.n, nw, per_worker_s, w.hq),
+            "sample_short": "%s layer 0, %d sequence-attentions over %d processes, %.0f s" % (
+                name, seqs, nw, secs),
             "one_core": one, "host": host}
 
 
@@ -752,6 +757,75 @@ def describe(r):
                 "whole (sequence, head) items, no merge" if r["whole"] else "fixed splits"),
             "waves": r["waves"] or None, "split_tokens": r["split"] or None,
             "kernel": "mfma" if r["mfma"] else "valu"}
+
+
+LINE_LIMIT = 4000   # bytes per printed JSON line: every line survives a short stdout tail
+
+
+def side_line(leg, name, payload):
+    """One side measurement as its own JSON line, printed at once."""
+    line = {"leg": leg, "name": name}
+    line.update(payload)
+    text = json.dumps(line)
+    if len(text) > LINE_LIMIT:
+        # keep the line short: drop the prose, then anything nested
+        line = {k: v for k, v in line.items() if k != "what" and k != "sample"}
+        for k, v in list(line.items()):
+            if isinstance(v, dict):
+                line[k] = {a: b for a, b in v.items() if a not in ("what", "sample")}
+        text = json.dumps(line)
+    print(text, flush=True)
+    return line
+
+
+def workload_summary(r):
+    """The figures of one workload run that its side line and the headline share."""
+    return {"value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
+            "seqs_per_ms": round(r["seqs_per_ms"], 2), "ms_per_step": round(r["ms_step"], 4),
+            "attn_partition_avg_us": round(r["part_avg_us"], 2),
+            "attn_partition_GBps": round(r["achieved"], 1)}
+
+
+def headline_line(head, args, traffic, cpu, cost):
+    """The compact headline: metric, value, step time, config, roofline and
+    the CPU baseline's figures, all scalars or small dicts (under 4 KB)."""
+    w = head["w"]
+    line = {
+        "metric": "paged decode attention KV GB/s (% of MI355X HBM peak) + sequences/ms",
+        "value": round(head["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": describe(head),
+        "pct_hbm_peak": round(100 * head["value"] / HBM_PEAK_GBS, 1),
+        "seqs_per_ms": round(head["seqs_per_ms"], 2),
+        "ms_per_step_wall": round(head["ms_step_wall"], 4),
+        "attention_median_us": head["attention"]["median_us"],
+        "attention_pct_hbm_peak": head["attention"]["pct_hbm_peak"],
+        "scatter_median_us": head["scatter"]["median_us"],
+        "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic[0] if traffic else None,
+                     "traffic_alg_bytes": traffic[1] if traffic else None,
+                     "traffic_over_alg": round(traffic[0] / traffic[1], 4) if traffic and traffic[1] else None,
+                     "kernel": "attention partition", "avg_launch_us": round(head["part_avg_us"], 2),
+                     "median_launch_us": round(head["part_med_us"], 2),
+                     "alg_bytes_per_launch": int(head["attn_bytes"])},
+        "shuffled_over_ordered": cost,
+    }
+    if cpu is not None:
+        line["cpu_baseline"] = {"value": cpu["value"], "unit": cpu["unit"], "cores": cpu["cores"],
+                                "kind": cpu["kind"], "seqs_per_ms": cpu["seqs_per_ms"],
+                                "seconds": cpu["seconds"], "sample": cpu["sample_short"],
+                                "one_core_GBps": cpu["one_core"]["value"]}
+    return line
 
 
 def main():
@@ -798,92 +872,61 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, args.flush == "on")
-    others = {}
+    flush = args.flush == "on"
+
+    def report(name, r):
+        summary = workload_summary(r)
+        side_line("workload", "%s_%s" % (name, r["frames"]), dict(
+            summary, attention=r["attention"], scatter=r["scatter"], config=describe(r)))
+        return summary
+
+    head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, flush)
+    report(args.config, head)
     head_ordered = run_gpu(args, args.config, "ordered" if args.frames == "shuffled" else "shuffled",
-                           args.steps, args.warmup, args.flush == "on", share=head["w"])
+                           args.steps, args.warmup, flush, share=head["w"])
+    report(args.config, head_ordered)
     head["w"].drop_values()
     head_ordered["w"].drop_values()
-    runs = [(args.config, head_ordered)]
+    attn = {(args.config, head["frames"]): head["attention"],
+            (args.config, head_ordered["frames"]): head_ordered["attention"]}
     for extra in [x for x in args.also.split(",") if x and x != args.config]:
         first = None
         for fr in ("shuffled", "ordered"):
-            r = run_gpu(args, extra, fr, args.steps, args.warmup, args.flush == "on",
+            r = run_gpu(args, extra, fr, args.steps, args.warmup, flush,
                         share=first["w"] if first else None)
+            report(extra, r)
+            attn[(extra, fr)] = r["attention"]
             if first is not None:   # both frame orders done: the drawn values are no longer needed
                 first["w"].drop_values()
                 r["w"].drop_values()
             first = first or r
-            runs.append((extra, r))
-    for name, r in runs:
-        others["%s_%s" % (name, r["frames"])] = {
-            "value_GBps": round(r["value"], 1), "pct_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 1),
-            "seqs_per_ms": round(r["seqs_per_ms"], 2), "ms_per_step": round(r["ms_step"], 4),
-            "attn_partition_avg_us": round(r["part_avg_us"], 2),
-            "attn_partition_GBps": round(r["achieved"], 1), "attention": r["attention"], "scatter": r["scatter"],
-            "config": describe(r)}
     # PageFault's pending "cost of scattering pages": shuffled / ordered median
     # attention time (partition + merge)
     cost = {}
-    for name in dict.fromkeys(n for n, _ in runs):
-        sh = head if name == args.config else None
-        key_s, key_o = "%s_shuffled" % name, "%s_ordered" % name
-        a_s = sh["attention"] if sh is not None and args.frames == "shuffled" else others.get(key_s, {}).get("attention")
-        a_o = others.get(key_o, {}).get("attention")
+    for name in dict.fromkeys(n for n, _ in attn):
+        a_s, a_o = attn.get((name, "shuffled")), attn.get((name, "ordered"))
         if a_s and a_o:
             cost[name] = round(a_s["median_us"] / a_o["median_us"], 3)
-    w = head["w"]
-    traffic = measured_traffic(args.config)
-    line = {
-        "metric": "paged decode attention KV GB/s (% of MI355X HBM peak) + sequences/ms",
-        "value": round(head["value"], 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(head["ms_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": describe(head),
-        "pct_hbm_peak": round(100 * head["value"] / HBM_PEAK_GBS, 1),
-        "seqs_per_ms": round(head["seqs_per_ms"], 2),
-        "ms_per_step_wall": round(head["ms_step_wall"], 4),
-        "attention": head["attention"],
-        "scatter": head["scatter"],
-        "roofline": {"bound": "hbm", "achieved": round(head["achieved"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head["achieved"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic[0] if traffic else None,
-                     "traffic_alg_bytes": traffic[1] if traffic else None,
-                     "traffic_over_alg": round(traffic[0] / traffic[1], 4) if traffic and traffic[1] else None,
-                     "kernel": "attention partition", "avg_launch_us": round(head["part_avg_us"], 2),
-                     "median_launch_us": round(head["part_med_us"], 2),
-                     "min_launch_us": round(head["part_min_us"], 2),
-                     "sd_launch_us": round(head["part_sd_us"], 2),
-                     "alg_bytes_per_launch": int(head["attn_bytes"])},
-        "others": others,
-        "shuffled_over_ordered": cost,
-    }
-    twin = {}
     for name in [x for x in args.twin.split(",") if x]:
-        twin[name] = run_twin(name, "shuffled", args.twin_reps)
-    if twin:
-        line["paged_vs_contiguous"] = twin
+        side_line("paged_vs_contiguous", name, run_twin(name, "shuffled", args.twin_reps))
     if args.cow == "on":
-        line["cow_prefix_sharing"] = run_cow(16, 4, 20)
+        side_line("cow_prefix_sharing", "13b_heads_16x4", run_cow(16, 4, 20))
     if args.swap == "on":
-        line["swap"] = run_swap(16, 10)
+        side_line("swap", "13b_heads_16", run_swap(16, 10))
     fused = [x for x in args.fused.split(",") if x]
     if fused:
-        line["fused_scatter_attention"] = run_fused(fused, 10)
+        for name, row in run_fused(fused, 10).items():
+            side_line("fused_scatter_attention", name, row)
     sweep = [x for x in args.block_sweep.split(",") if x]
     if sweep:
-        line["block_size_sweep"] = run_block_sweep(sweep, (8, 16, 32, 64), 15)
+        for name, rows in run_block_sweep(sweep, (8, 16, 32, 64), 15).items():
+            side_line("block_size_sweep", name, {"rows": rows})
+    cpu = None
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+        cpu = cpu_baseline(args.config, args.cpu_seconds)
+        side_line("cpu_baseline", args.config, cpu)
+    traffic = measured_traffic(args.config)
+    print(json.dumps(headline_line(head, args, traffic, cpu, cost)), flush=True)
 
 
 if __name__ == "__main__":

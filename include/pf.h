@@ -93,7 +93,11 @@ size_t pf_pool_bytes(const pf_pool* pool);
 size_t pf_page_bytes(const pf_pool* pool);
 
 /* Bind caller-owned device memory of at least pf_pool_bytes bytes, 256-byte
- * aligned.  Errors: PF_ERR_INVALID (null, too small, misaligned). */
+ * aligned: the one allocation that holds every page of the pool (PageFault,
+ * "Four stages", stage 2: one device allocation for the whole pool, from which
+ * a free list hands out frames; PageForge, "Four layers": K and V combined in
+ * one pool).
+ * Errors: PF_ERR_INVALID (null, too small, misaligned). */
 int pf_pool_bind(pf_pool* pool, void* dev_ptr, size_t bytes);
 
 /* Grow sequence seq_id to new_len tokens in total, taking
@@ -199,11 +203,17 @@ int pf_swap_in(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* stagi
 
 /* Release seq_id's hold on each of its pages and forget the sequence; pages no
  * other table holds go back on the free stack, last page first (so the
- * sequence's first page ends on top).
+ * sequence's first page ends on top).  PageForge, "Four layers, one pointer
+ * moving through all of them": free_seq returns a finished sequence's pages to
+ * the free list in O(1) per page; "Does the pool actually come back to zero?":
+ * a freed batch leaves the pool whole.
  * Errors: PF_ERR_UNKNOWN_SEQ (never allocated or already freed). */
 int pf_free_seq(pf_pool* pool, uint64_t seq_id);
 
-/* Pages currently on the free stack (-1 for a NULL handle). */
+/* Pages currently on the free stack (-1 for a NULL handle).  PageForge, "Four
+ * layers, one pointer moving through all of them": the allocator reports its
+ * free page count (free_pages), which returns to the pool size once every
+ * sequence is freed. */
 int32_t pf_free_pages(const pf_pool* pool);
 
 /* Most pages in use at once since the handle was created or the peak was last
@@ -223,7 +233,11 @@ int pf_seq_len(const pf_pool* pool, uint64_t seq_id, int32_t* len);
 
 /* Export dense host tables for n sequences: bt_host is [n][max_blocks] int32,
  * row i = the block table of seq_ids[i] padded with -1; lens_host (nullable)
- * is [n] int32 lengths.  Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID (a table
+ * is [n] int32 lengths (PagedAttention blog, "Architecture": a block table is
+ * an int32 array of max_blocks_per_seq entries mapping logical block i to a
+ * physical block; the blog zero-fills the unused entries and keeps the block
+ * count beside them, here they are -1, which names no page).  Rows follow the
+ * order of seq_ids (an id may repeat).  Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID (a table
  * longer than max_blocks, null pointers with n > 0), PF_ERR_SWAPPED. */
 int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
                     int32_t* bt_host, int32_t* lens_host);

@@ -31,9 +31,13 @@ Modules, and the passages each one follows:
 * ``accounting``   -- bytes per token, reserved memory, utilization and
   internal fragmentation (PageFault, "Calculate": core formulas).
 
-Pins (``tests/test_oracle_*.py``, fixtures in ``tests/golden/``) tie every
-function to something other than itself: worked examples printed on the pages,
-closed forms, brute force on tiny inputs and invariants.  No function here is
-"parity unpinned"; the rounding of the GPU's fp32 arithmetic is bounded only by
-the 2e-3 tolerance (there is no bit-exact attention target).
+Pins (``tests/pins.py``, run by ``tests/test_oracle_pins.py``; fixtures in
+``tests/golden/``) tie every public function and method here to something other
+than itself: worked examples printed on the pages, closed forms, brute force on
+tiny inputs and invariants; ``tests/test_oracle_planted.py`` plants plausible
+mistakes and checks that a pin catches each.  The dense table export
+(``AllocModel.block_tables``) is pinned to the blog's table [7, 13, 2, 41]
+exported wider than the table, in request order, with the -1 padding that is
+this package's reading.  The rounding of the GPU's fp32 arithmetic is bounded
+only by the 2e-3 tolerance (there is no bit-exact attention target).
 """

@@ -310,7 +310,14 @@ class AllocModel:
         return self.num_pages - len(self.stack)
 
     def block_tables(self, seq_ids, max_blocks):
-        """Dense int32-style table rows (padded with -1) and the lengths, as lists."""
+        """Dense table rows and the lengths, as lists, one row per requested id
+        in the order requested (PagedAttention blog, "Architecture": a fixed
+        array of max_blocks_per_seq int32 entries per sequence whose first
+        num_blocks entries map logical blocks to physical ones).  The blog
+        zero-fills the unused entries and tracks num_blocks beside them; here
+        they hold -1, which names no page (0 is a page id), so a table row
+        carries its own block count.  A sequence with more blocks than
+        max_blocks raises ValueError."""
         rows, lens = [], []
         for s in seq_ids:
             t = self.tables[s]
@@ -342,29 +349,3 @@ class AllocModel:
         for s, slots in self.swapped.items():
             assert s not in self.tables and len(slots) == blocks_for(self.lengths[s], self.block_size)
 
-
-def replay(num_pages, block_size, initial_free_order, ops):
-    """Replay an op log ``[("alloc", seq, new_len) | ("free", seq) |
-    ("fork", parent, child) | ("grow", seq, new_len), ...]``.
-
-    Returns the model and, per op, ``(status, n_new_pages, free_pages)`` (for
-    "grow" a fourth item, the copy or None) so a log recorded from another
-    implementation can be compared op by op.
-    """
-    m = AllocModel(num_pages, block_size, initial_free_order)
-    trace = []
-    for op in ops:
-        if op[0] == "alloc":
-            st, nn = m.alloc(op[1], op[2])
-        elif op[0] == "free":
-            st, nn = m.free(op[1]), 0
-        elif op[0] == "fork":
-            st, nn = m.fork(op[1], op[2]), 0
-        elif op[0] == "grow":
-            st, nn, copy = m.grow(op[1], op[2])
-            trace.append((st, nn, m.free_pages(), copy))
-            continue
-        else:
-            raise ValueError(op)
-        trace.append((st, nn, m.free_pages()))
-    return m, trace

@@ -193,6 +193,37 @@ def pin_lifo_reuse_order(o):
     assert m.table(2) == t
 
 
+def pin_block_table_export(o):
+    """The blog's table [7, 13, 2, 41] exported as a dense row of width 6:
+    the four physical blocks in logical order, then two entries that name no
+    page (-1; page 0 is a real page here and is live), one row per requested
+    id in the order requested, lengths beside them, and a row too narrow for
+    its table refused."""
+    g = GOLDEN["walk_table_7_13_2_41"]
+    am = o.alloc_model
+    B, table = g["block_size"], g["table"]
+    order = table + [p for p in range(48) if p not in table]
+    m = am.AllocModel(48, B, order)
+    assert m.alloc(9, 4 * B) == (am.OK, 4)            # pops 7, 13, 2, 41
+    assert m.alloc(3, B + 5) == (am.OK, 2)            # pops the next two: 0, 1
+    rows, lens = m.block_tables([9], 6)
+    assert rows == [table + [-1, -1]] and lens == [4 * B]
+    rows, lens = m.block_tables([9, 3], 6)
+    assert rows == [table + [-1, -1], [0, 1, -1, -1, -1, -1]] and lens == [4 * B, B + 5]
+    rows, lens = m.block_tables([3, 9, 3], 4)         # request order, repeats allowed
+    assert rows == [[0, 1, -1, -1], table, [0, 1, -1, -1]] and lens == [B + 5, 4 * B, B + 5]
+    for row, n in zip(rows, lens):                    # the row carries its own block count
+        used = [p for p in row if p != -1]
+        assert len(used) == am.blocks_for(n, B) and row[:len(used)] == used
+    try:
+        m.block_tables([9], 3)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a table longer than max_blocks must be refused")
+    assert m.block_tables([], 5) == ([], [])
+
+
 def pin_cow_blog_tables(o):
     """The blog's three sampled sequences: prefix blocks 7 and 13 held once by
     all three tables (count 3), private blocks 2, 5, 9 after the divergence;

@@ -199,6 +199,27 @@ class _PeakIsCurrentModel(oracle.alloc_model.AllocModel):
         self.peak = self.pages_in_use()                         # the current, not the highest
 
 
+class _ZeroPaddedTablesModel(oracle.alloc_model.AllocModel):
+    def block_tables(self, seq_ids, max_blocks):
+        rows, lens = super().block_tables(seq_ids, max_blocks)
+        return [[0 if p == -1 else p for p in r] for r in rows], lens   # pads with page 0
+
+
+class _SortedRowsTablesModel(oracle.alloc_model.AllocModel):
+    def block_tables(self, seq_ids, max_blocks):
+        return super().block_tables(sorted(seq_ids), max_blocks)          # rows by id, not as asked
+
+
+class _UncheckedWidthTablesModel(oracle.alloc_model.AllocModel):
+    def block_tables(self, seq_ids, max_blocks):
+        rows, lens = [], []
+        for s in seq_ids:                                                 # truncates instead of refusing
+            t = self.tables[s][:max_blocks]
+            rows.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.lengths[s])
+        return rows, lens
+
+
 MUTANTS = {
     "attention_without_scale": (oracle.attention, "attention", _no_scale),
     "attention_wrong_sign": (oracle.attention, "attention", _wrong_sign),
@@ -222,6 +243,9 @@ MUTANTS = {
     "swap_in_keeps_slots": (oracle.alloc_model, "AllocModel", _SwapInKeepsSlotsModel),
     "swap_copy_wrong_page": (oracle.layout, "swap_copy", _swap_copy_off_by_one_page),
     "peak_is_current_use": (oracle.alloc_model, "AllocModel", _PeakIsCurrentModel),
+    "tables_pad_with_zero": (oracle.alloc_model, "AllocModel", _ZeroPaddedTablesModel),
+    "tables_rows_sorted_by_id": (oracle.alloc_model, "AllocModel", _SortedRowsTablesModel),
+    "tables_truncate_long_rows": (oracle.alloc_model, "AllocModel", _UncheckedWidthTablesModel),
 }
 
 
