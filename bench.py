@@ -48,7 +48,7 @@ WORKLOADS = {
 
 
 # Sources that define the attention partition kernels (the roofline kernel).
-ATTN_SOURCES = ("pf_attn.hip", "pf_attn_mfma.hip", "pf_sched.h", "pf_common.h", "pf_attn.h", "pf_internal.h")
+ATTN_SOURCES = ("pf_attn.hip", "pf_attn_mfma.hip", "pf_sched.h", "pf_common.h", "pf_attn.h")
 
 
 def kernel_source_hash():
@@ -120,7 +120,7 @@ class TimingEvent:
         return self.m.elapsed_ms(stop.m)
 
 
-def run_gpu(args, name, frames, steps, warmup, flush, share=None, plan=True):
+def run_gpu(args, name, frames, steps, warmup, flush, share=None):
     import torch
     from paged_kv_cache_43_amd import inputs, pf, runner
 
@@ -165,11 +165,10 @@ def run_gpu(args, name, frames, steps, warmup, flush, share=None, plan=True):
         pf.check(st, "pf_alloc_for_seqs")
         if flush:
             _flush(flush_buf)   # read 1 GiB: evicts the K/V from L2 and the 256 MB MALL, leaves nothing dirty
-        mc = int(new_lens.max())
         if events:
             ev_step[t][0].record(stream)
-        # tables + every layer's new token (+ the schedule's plan), one launch
-        kv.decode_prepare(newk, newv, plan_max_ctx=mc if plan else None)
+        kv.decode_prepare(newk, newv)          # tables + every layer's new token, one launch
+        mc = int(new_lens.max())
         for layer in range(w.layers):
             if kernel_events:
                 pf.check(pf.pf_pool_set_timing_events(kv.h, ev_a[t][layer].cuda_event,
@@ -191,8 +190,6 @@ def run_gpu(args, name, frames, steps, warmup, flush, share=None, plan=True):
         step(t, flush)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    mc_last = int(ctx_per_step[-1].max())
-    plan_used = bool(pf.pf_attention_plan_current(kv.h, kv.meta, w.n, kv.max_blocks, w.hq, mc_last))
     # more steps with HIP events around every partition kernel (roofline)
     for t in range(warmup + steps, total_steps):
         step(t, True, kernel_events=True)
@@ -270,61 +267,9 @@ def run_gpu(args, name, frames, steps, warmup, flush, share=None, plan=True):
         seqs_per_ms=w.n / ms_step, part_avg_us=part_avg_ms * 1e3,
         part_med_us=float(np.median(part_ms)) * 1e3, part_min_us=float(np.min(part_ms)) * 1e3,
         part_sd_us=float(np.std(part_ms)) * 1e3,
-        attn_bytes=avg_attn_bytes, achieved=achieved, split=split, waves=waves, mfma=bool(mfma), plan=plan_used,
+        attn_bytes=avg_attn_bytes, achieved=achieved, split=split, waves=waves, mfma=bool(mfma),
         whole=bool(split) and split >= max_ctx_final,
         kernel_seqs_per_ms=w.n / (part_avg_ms * w.layers), attention=attention, scatter=scatter)
-
-
-def run_plan_ab(name, reps):
-    """The balanced schedule's plan on and off at the same lengths: per
-    repetition, flushed, a planned prepare + attention call, then flushed, a
-    plain prepare + attention call (each prepare rewrites every sequence's
-    newest token, the same bits both times); partition kernel and whole-step
-    times from stream markers, medians; the two outputs must be the same bits."""
-    import torch
-    from paged_kv_cache_43_amd import inputs, pf, runner
-
-    w = inputs.Workload(name, frames="shuffled")
-    kv = runner.PagedKV(w, sentinel=False)
-    q = runner.fill_workload(kv)
-    mc = int(w.ctx.max())
-    kv.ensure_workspace(mc)
-    rng = np.random.default_rng(5)
-    newk = runner.bits_to_device(inputs.normal_bits(rng, (w.layers, w.n, w.hkv, w.d), w.dtype))
-    newv = runner.bits_to_device(inputs.normal_bits(rng, (w.layers, w.n, w.hkv, w.d), w.dtype))
-    dt = torch.int32 if w.es == 4 else torch.int16
-    outs = {m: torch.empty((w.n, w.hq, w.d), dtype=dt, device="cuda") for m in ("plan", "no_plan")}
-    fl = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
-    order = [m for _ in range(reps + 3) for m in ("plan", "no_plan")]
-    ev = [[TimingEvent() for _ in range(4)] for _ in order]
-    for e in ev:
-        for x in e:
-            x.record()
-    torch.cuda.synchronize()
-    used = []
-    for e, m in zip(ev, order):
-        _flush(fl)
-        e[0].record()
-        kv.decode_prepare(newk, newv, plan_max_ctx=mc if m == "plan" else None)
-        if m == "plan":
-            used.append(pf.pf_attention_plan_current(kv.h, kv.meta, w.n, kv.max_blocks, w.hq, mc))
-        pf.check(pf.pf_pool_set_timing_events(kv.h, e[1].cuda_event, e[2].cuda_event))
-        kv.attention(0, q[0], outs[m], mc)
-        pf.check(pf.pf_pool_set_timing_events(kv.h, None, None))
-        e[3].record()
-    torch.cuda.synchronize()
-    res = {"frames": "shuffled", "median_of": reps, "plan_words": int(pf.pf_attention_plan_words(kv.h, w.n, w.hq, mc)),
-           "plan_used": bool(used) and all(u == 1 for u in used)}
-    for m in ("plan", "no_plan"):
-        sel = [e for e, mm in list(zip(ev, order))[6:] if mm == m]
-        res["partition_us_" + m] = round(float(np.median([a[1].elapsed_time(a[2]) * 1e3 for a in sel])), 2)
-        res["step_us_" + m] = round(float(np.median([a[0].elapsed_time(a[3]) * 1e3 for a in sel])), 2)
-    res["bitwise_equal"] = bool(torch.equal(outs["plan"], outs["no_plan"]))
-    alg = alg_bytes_attention(w.ctx, w, w.es)
-    res["partition_pct_hbm_peak_plan"] = round(100 * alg / res["partition_us_plan"] / 1e3 / HBM_PEAK_GBS, 1)
-    res["partition_pct_hbm_peak_no_plan"] = round(100 * alg / res["partition_us_no_plan"] / 1e3 / HBM_PEAK_GBS, 1)
-    kv.close()
-    return res
 
 
 def run_twin(name, frames, reps):
@@ -811,7 +756,7 @@ def describe(r):
             "schedule": "balanced" if r["waves"] else (
                 "whole (sequence, head) items, no merge" if r["whole"] else "fixed splits"),
             "waves": r["waves"] or None, "split_tokens": r["split"] or None,
-            "kernel": "mfma" if r["mfma"] else "valu", "plan": bool(r.get("plan"))}
+            "kernel": "mfma" if r["mfma"] else "valu"}
 
 
 LINE_LIMIT = 4000   # bytes per printed JSON line: every line survives a short stdout tail
@@ -897,10 +842,6 @@ def main():
     ap.add_argument("--twin", default="13b,gqa",
                     help="comma list of configs for the paged vs contiguous-cache comparison (shuffled frames)")
     ap.add_argument("--twin-reps", type=int, default=20)
-    ap.add_argument("--plan", choices=["on", "off"], default="on",
-                    help="write the balanced schedule's plan with each step's tables (default on)")
-    ap.add_argument("--plan-ab", default="13b,gqa,mixed",
-                    help="comma list of configs for the plan on / off comparison at fixed lengths")
     ap.add_argument("--fused", default="gpt2,mixed,13b,gqa",
                     help="comma list of configs for the fused scatter + attention comparison")
     ap.add_argument("--block-sweep", default="13b,gqa",
@@ -939,11 +880,10 @@ def main():
             summary, attention=r["attention"], scatter=r["scatter"], config=describe(r)))
         return summary
 
-    plan = args.plan == "on"
-    head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, flush, plan=plan)
+    head = run_gpu(args, args.config, args.frames, args.steps, args.warmup, flush)
     report(args.config, head)
     head_ordered = run_gpu(args, args.config, "ordered" if args.frames == "shuffled" else "shuffled",
-                           args.steps, args.warmup, flush, share=head["w"], plan=plan)
+                           args.steps, args.warmup, flush, share=head["w"])
     report(args.config, head_ordered)
     head["w"].drop_values()
     head_ordered["w"].drop_values()
@@ -953,7 +893,7 @@ def main():
         first = None
         for fr in ("shuffled", "ordered"):
             r = run_gpu(args, extra, fr, args.steps, args.warmup, flush,
-                        share=first["w"] if first else None, plan=plan)
+                        share=first["w"] if first else None)
             report(extra, r)
             attn[(extra, fr)] = r["attention"]
             if first is not None:   # both frame orders done: the drawn values are no longer needed
@@ -967,8 +907,6 @@ def main():
         a_s, a_o = attn.get((name, "shuffled")), attn.get((name, "ordered"))
         if a_s and a_o:
             cost[name] = round(a_s["median_us"] / a_o["median_us"], 3)
-    for name in [x for x in args.plan_ab.split(",") if x]:
-        side_line("plan_on_off", name, run_plan_ab(name, 20))
     for name in [x for x in args.twin.split(",") if x]:
         side_line("paged_vs_contiguous", name, run_twin(name, "shuffled", args.twin_reps))
     if args.cow == "on":

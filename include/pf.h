@@ -286,59 +286,6 @@ int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, i
                       int32_t* staging_host, int32_t* meta_dev, const void* k, const void* v,
                       int32_t layer0, int32_t num_layers, void* hip_stream);
 
-/* pf_decode_prepare that also writes, next to the tables, a plan of the
- * balanced schedule for one attention configuration (num_q_heads,
- * max_context_len: those of the pf_paged_decode_attention_planned calls that
- * follow): for each wave of the partition kernel, the table entries and
- * positions of the first two 16-token units of its slice, computed on the host
- * from the tables and lengths being exported.  With it the kernel issues
- * those page loads at launch instead of after it has loaded and scanned the
- * lengths and searched its slice (PagedAttention blog, "Quantitative Impact":
- * the block-table indirection should cost little of the kernel's time).
- *   staging_host  as pf_decode_prepare, at least
- *                 pf_plan_staging_words(n, max_blocks, plan_words) words;
- *   meta_dev      as pf_decode_prepare, at least
- *                 pf_plan_meta_words(n, max_blocks, plan_words) words;
- * where plan_words = pf_attention_plan_words(pool, n, num_q_heads,
- * max_context_len).  When that is 0 (the call will not use the balanced
- * schedule with 16-token pages) no plan is written and this is
- * pf_decode_prepare.  The plan is tied to meta_dev: any later export to
- * meta_dev without a plan (pf_export_tables, pf_decode_prepare,
- * pf_export_staging) or an option change retires it.  Errors: as
- * pf_decode_prepare, plus PF_ERR_INVALID for num_q_heads <= 0. */
-int pf_decode_prepare_planned(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
-                              int32_t* staging_host, int32_t* meta_dev, const void* k, const void* v,
-                              int32_t layer0, int32_t num_layers, int32_t num_q_heads, int32_t max_context_len,
-                              void* hip_stream);
-
-/* Host half of pf_decode_prepare_planned, with no launch (as pf_export_staging
- * with step != 0 is of pf_decode_prepare): fills staging_host exactly as that
- * call would, the plan at word pf_plan_staging_words(n, max_blocks, 0), and
- * counts the export, plan included, as made to meta_dev (not accessed).  For
- * callers that upload the staging themselves, and for tests.  Errors: as
- * pf_export_staging, plus PF_ERR_INVALID for num_q_heads <= 0. */
-int pf_export_staging_planned(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
-                              const void* meta_dev, int32_t num_q_heads, int32_t max_context_len,
-                              int32_t* staging_host, int64_t* pairs);
-
-/* 1 if a pf_paged_decode_attention_planned call with these arguments would
- * use the plan held in meta_dev (the last export to meta_dev wrote one for
- * this configuration), else 0 (also for a NULL handle or buffer). */
-int32_t pf_attention_plan_current(const pf_pool* pool, const int32_t* meta_dev, int32_t n, int32_t max_blocks,
-                                  int32_t num_q_heads, int32_t max_context_len);
-
-/* Words of the plan pf_decode_prepare_planned writes for these sizes under the
- * handle's options (8 + 8 per wave of the balanced schedule), or 0 when an
- * attention call with them uses no plan. */
-int64_t pf_attention_plan_words(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_context_len);
-
-/* Staging and metadata sizes, in int32 words, for a planned export of n rows
- * of max_blocks entries with a plan of plan_words words: the plan follows the
- * tables, lengths and newest positions (and in the staging the destination
- * pages), rounded up to 16 bytes.  -1 for negative sizes. */
-int64_t pf_plan_staging_words(int32_t n, int32_t max_blocks, int64_t plan_words);
-int64_t pf_plan_meta_words(int32_t n, int32_t max_blocks, int64_t plan_words);
-
 /* Write num_tokens tokens' K and V into their page slots for one layer.
  *   k, v     device [num_tokens][H][D] in the pool dtype.
  *   tok_seq  device [num_tokens] int32: row of bt_dev holding the token's table.
@@ -407,23 +354,6 @@ int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
                               int32_t n, int32_t max_context_len, float scale, void* out,
                               int32_t out_dtype, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
-
-/* pf_paged_decode_attention over the tables and lengths that the last
- * pf_decode_prepare_planned call wrote into meta_dev (table
- * [n][max_blocks] at meta_dev, lengths at meta_dev + n*max_blocks), using the
- * plan written with them when it matches this call's sizes (num_q_heads,
- * max_context_len, n, max_blocks) and options; otherwise, or when the plan has
- * been retired, exactly pf_paged_decode_attention.  A plan only lets the
- * kernel issue its first page loads earlier: the result is the same bits with
- * or without it.  Calls must be enqueued on the stream in the order they are
- * made (the plan's validity is tracked in call order).
- *   meta_dev  device, 16-byte aligned, as written by pf_decode_prepare_planned.
- * Other arguments as pf_paged_decode_attention.  Errors: as
- * pf_paged_decode_attention. */
-int pf_paged_decode_attention_planned(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
-                                      const int32_t* meta_dev, int32_t max_blocks, int32_t n,
-                                      int32_t max_context_len, float scale, void* out, int32_t out_dtype,
-                                      void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* pf_scatter_kv of each sequence's newest token fused into
  * pf_paged_decode_attention, in one launch (PageForge, "Five techniques" and its

@@ -34,9 +34,6 @@ struct AttnArgs {
   // null otherwise.
   const void* k_new;
   const void* v_new;
-  // Balanced-schedule plan (pf_sched.h: the first two units of each wave's
-  // slice, written by the host with the step's tables), or null.
-  const int32_t* plan;
 };
 
 template <int NW>
@@ -81,8 +78,6 @@ bool mfma_supports(int head_dim);
 // Launch the matrix-core partition kernel (balanced or grid schedule) over
 // the paged pool or, with contig, over a contiguous cache.
 int launch_mfma(const AttnArgs& a, int dtype, int head_dim, bool balanced, bool contig, hipStream_t st);
-// The balanced matrix-core kernel over pool pages with a plan (a.plan set).
-int launch_mfma_planned(const AttnArgs& a, int dtype, int head_dim, hipStream_t st);
 // The same for a pool of block_size 32 or 64 (balanced schedule, paged).
 int launch_mfma_bs(const AttnArgs& a, int dtype, int head_dim, int block_size, hipStream_t st);
 // The balanced matrix-core kernel of the default page size (for occupancy

@@ -106,9 +106,6 @@ struct ValuWave {
 
   static constexpr bool kContig = CONTIG;
 
-  // True when the call writes each sequence's newest token (fused append).
-  __device__ inline bool appends() const { return a.k_new != nullptr; }
-
   __device__ ValuWave(const AttnArgs& args, int ln) : a(args), lane(ln), dc(ln % S::LPT), tq(ln / S::LPT) {}
 
   __device__ inline Raw<S::NW> load_q(int s, int h) const {
@@ -293,26 +290,16 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
 }
 
 // Balanced schedule (pf_sched.h): four waves per workgroup, items are query
-// heads.  PLAN: a.plan holds the first two units of every wave's slice, whose
-// loads are issued before the lengths are scanned.
-template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock, bool PLAN = false>
+// heads.
+template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock>
 __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) {
   using Wv = ValuWave<T, D, OUT_F32, CONTIG, BS>;
   __shared__ SchedLds L;
+  sched_build<Wv::UT>(a, L);
+  zero_empty_rows<T, OUT_F32>(a, L, D);
   const int lane = threadIdx.x % kWave;
   Wv w(a, lane);
-  PlanPre<typename Wv::Tile> pre;
-  bool planned = false;
-  if constexpr (PLAN) {
-    const PlanHead ph = plan_read(a, blockIdx.x * (kSchedThreads / kWave) + threadIdx.x / kWave);
-    const SchedCtx cx = sched_load(a);
-    planned = plan_start(a, ph, a.hq, w, pre);
-    sched_scan<Wv::UT>(a, L, cx);
-  } else {
-    sched_build<Wv::UT>(a, L);
-  }
-  zero_empty_rows<T, OUT_F32>(a, L, D);
-  sched_run<U, BS>(a, L, a.hq, w, lane, pre, planned);
+  sched_run<U, BS>(a, L, a.hq, w, lane);
 }
 
 // Merge the pieces of output rows that were split (PagedAttention blog, "The
@@ -619,48 +606,6 @@ static void launch_valu(const AttnArgs& a, bool balanced, hipStream_t st) {
                        0, st, a);
 }
 
-// The balanced vector kernel with a plan: pool pages of 16 tokens, and only
-// where two pages fill at most two prefetch units (U <= 2).
-template <class T, int D>
-static constexpr bool valu_plannable() {
-  return ValuUnit<T, D>::U <= 2;
-}
-
-template <class T, int D>
-static void launch_valu_planned_d(const AttnArgs& a, hipStream_t st) {
-  constexpr int U = ValuUnit<T, D>::U;
-  if constexpr (U <= 2) {
-    const dim3 grid(a.waves / (kSchedThreads / kWave));
-    if (a.out_f32)
-      hipLaunchKernelGGL((attn_valu_balanced<T, D, U, true, false, kBlock, true>), grid, dim3(kSchedThreads), 0, st,
-                         a);
-    else
-      hipLaunchKernelGGL((attn_valu_balanced<T, D, U, false, false, kBlock, true>), grid, dim3(kSchedThreads), 0,
-                         st, a);
-  }
-}
-
-template <class T>
-static int launch_valu_planned(const AttnArgs& a, int D, hipStream_t st) {
-  switch (D) {
-    case 32:
-      if constexpr (valu_plannable<T, 32>()) { launch_valu_planned_d<T, 32>(a, st); return PF_OK; }
-      return PF_ERR_UNSUPPORTED;
-    case 64: launch_valu_planned_d<T, 64>(a, st); return PF_OK;
-    case 128: launch_valu_planned_d<T, 128>(a, st); return PF_OK;
-    default: return PF_ERR_UNSUPPORTED;
-  }
-}
-
-// Whether the vector kernel has a planned form for this element type and head
-// dim: where two pages fill at most two prefetch units, and not at head dim
-// 256, whose planned form needs every register of a SIMD lane (one wave per
-// SIMD instead of the two the balanced grid places).
-static bool valu_plan_supported(int dtype, int D) {
-  const int es = dtype == PF_F32 ? 4 : 2;
-  return (D == 32 && es == 4) || D == 64 || D == 128;
-}
-
 template <class T, bool OUT_F32, bool CONTIG>
 static int dispatch_valu_d(const AttnArgs& a, int D, bool balanced, hipStream_t st) {
   switch (D) {
@@ -906,52 +851,6 @@ size_t plan_workspace(const Plan& p, int head_dim) {
 
 }  // namespace
 
-bool pf_plan_config(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_context_len,
-                    pf_plan_cfg* cfg) {
-  if (!pool || !cfg || n <= 0 || num_q_heads <= 0 || max_context_len <= 0 ||
-      num_q_heads % pool->g.num_kv_heads != 0 || num_q_heads > 0xffff)
-    return false;
-  const pf_geometry& g = pool->g;
-  if (g.block_size != kBlock) return false;
-  const Plan p = make_plan(pool, n, num_q_heads, max_context_len);
-  if (!p.balanced) return false;
-  if (p.mfma ? !mfma_supports(g.head_dim) : !valu_plan_supported(g.dtype, g.head_dim)) return false;
-  cfg->items = p.items_per_seq;
-  cfg->unit_tokens = kBlock;
-  cfg->units_per_page = 1;
-  cfg->waves = p.waves;
-  cfg->max_ctx = max_context_len;
-  return true;
-}
-
-extern "C" int64_t pf_attention_plan_words(const pf_pool* pool, int32_t n, int32_t num_q_heads,
-                                           int32_t max_context_len) {
-  pf_plan_cfg c;
-  if (!pf_plan_config(pool, n, num_q_heads, max_context_len, &c)) return 0;
-  return kPlanHeaderWords + kPlanWaveWords * (int64_t)c.waves;
-}
-
-extern "C" int pf_export_staging_planned(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
-                                         const void* meta_dev, int32_t num_q_heads, int32_t max_context_len,
-                                         int32_t* staging_host, int64_t* pairs) {
-  if (!pool || !pairs || n < 0 || max_blocks < 0 || num_q_heads <= 0 || max_context_len < 0) return PF_ERR_INVALID;
-  if (n > 0 && (!staging_host || !meta_dev)) return PF_ERR_INVALID;
-  *pairs = -1;
-  if (n == 0) return PF_OK;
-  pf_plan_cfg cfg;
-  if (!pf_plan_config(pool, n, num_q_heads, max_context_len, &cfg))
-    return pf_fill_export(pool, meta_dev, seq_ids, n, max_blocks, true, staging_host, pairs);
-  return pf_fill_export(pool, meta_dev, seq_ids, n, max_blocks, true, staging_host, pairs, &cfg,
-                        staging_host + pf_plan_staging_offset(n, max_blocks));
-}
-
-extern "C" int32_t pf_attention_plan_current(const pf_pool* pool, const int32_t* meta_dev, int32_t n,
-                                             int32_t max_blocks, int32_t num_q_heads, int32_t max_context_len) {
-  pf_plan_cfg cfg;
-  if (!pool || !meta_dev || !pf_plan_config(pool, n, num_q_heads, max_context_len, &cfg)) return 0;
-  return pf_plan_current(pool, meta_dev, n, max_blocks, cfg) ? 1 : 0;
-}
-
 extern "C" int32_t pf_attention_kernel(const pf_pool* pool, int32_t num_q_heads) {
   if (!pool || num_q_heads <= 0 || num_q_heads % pool->g.num_kv_heads != 0) return -1;
   return use_mfma(pool, num_q_heads) ? 1 : 0;
@@ -1033,12 +932,7 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   hipStream_t st = (hipStream_t)hip_stream;
   if (pool->ev_start) (void)hipEventRecord((hipEvent_t)pool->ev_start, st);
   int rc;
-  if (a.plan != nullptr && p.balanced && bs == kBlock && !contig) {
-    if (p.mfma) rc = launch_mfma_planned(a, g.dtype, g.head_dim, st);
-    else if (g.dtype == PF_F32) rc = launch_valu_planned<ElF32>(a, g.head_dim, st);
-    else if (g.dtype == PF_F16) rc = launch_valu_planned<ElF16>(a, g.head_dim, st);
-    else rc = launch_valu_planned<ElBF16>(a, g.head_dim, st);
-  } else if (bs != kBlock) {
+  if (bs != kBlock) {
     if (p.mfma) rc = launch_mfma_bs(a, g.dtype, g.head_dim, bs, st);
     else if (g.dtype == PF_F16) rc = launch_valu_bs<ElF16>(a, g.head_dim, bs, st);
     else rc = launch_valu_bs<ElBF16>(a, g.head_dim, bs, st);
@@ -1070,8 +964,7 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
 static int paged_attention(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
                            const void* k_new, const void* v_new, const int32_t* bt_dev, int32_t max_blocks,
                            const int32_t* ctx_dev, int32_t n, int32_t max_context_len, float scale, void* out,
-                           int32_t out_dtype, void* workspace, size_t workspace_bytes, void* hip_stream,
-                           const int32_t* plan = nullptr) {
+                           int32_t out_dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (!pool) return PF_ERR_INVALID;
   if (!pool->dev) return PF_ERR_UNBOUND;
   const pf_geometry& g = pool->g;
@@ -1088,29 +981,8 @@ static int paged_attention(const pf_pool* pool, int32_t layer, const void* q, in
   a.max_blocks = max_blocks;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.plan = plan;
   return attend(pool, a, false, q, num_q_heads, ctx_dev, n, max_context_len, scale, out, out_dtype, workspace,
                 workspace_bytes, hip_stream);
-}
-
-extern "C" int pf_paged_decode_attention_planned(const pf_pool* pool, int32_t layer, const void* q,
-                                                 int32_t num_q_heads, const int32_t* meta_dev, int32_t max_blocks,
-                                                 int32_t n, int32_t max_context_len, float scale, void* out,
-                                                 int32_t out_dtype, void* workspace, size_t workspace_bytes,
-                                                 void* hip_stream) {
-  if (!pool || n < 0 || max_blocks <= 0) return PF_ERR_INVALID;
-  if (n > 0 && (!meta_dev || reinterpret_cast<uintptr_t>(meta_dev) % 16 != 0)) return PF_ERR_INVALID;
-  if (n == 0) return paged_attention(pool, layer, q, num_q_heads, nullptr, nullptr, meta_dev, max_blocks, meta_dev,
-                                     0, max_context_len, scale, out, out_dtype, workspace, workspace_bytes,
-                                     hip_stream);
-  const int32_t* lens = meta_dev + (int64_t)n * max_blocks;
-  pf_plan_cfg cfg;
-  const int32_t* plan = nullptr;
-  if (pf_plan_config(pool, n, num_q_heads, max_context_len, &cfg) &&
-      pf_plan_current(pool, meta_dev, n, max_blocks, cfg))
-    plan = meta_dev + pf_plan_meta_offset(n, max_blocks);
-  return paged_attention(pool, layer, q, num_q_heads, nullptr, nullptr, meta_dev, max_blocks, lens, n,
-                         max_context_len, scale, out, out_dtype, workspace, workspace_bytes, hip_stream, plan);
 }
 
 extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,

@@ -132,9 +132,6 @@ struct MfmaWave {
 
   static constexpr bool kContig = CONTIG;
 
-  // True when the call writes each sequence's newest token (fused append).
-  __device__ inline bool appends() const { return a.k_new != nullptr; }
-
   // The Q^T operand of (sequence s, kv head hk): head col, dims 32c + 8*grp
   // .. +8; zero rows past the group.
   __device__ inline void load_q(int s, int hk, uint4* dst) const {
@@ -389,27 +386,13 @@ __global__ __launch_bounds__(kWave) void attn_mfma_grid(AttnArgs a) {
 }
 
 // Balanced schedule (pf_sched.h): four waves per workgroup, items are kv
-// heads (each covering its group of query heads).  PLAN: a.plan holds the
-// first two units of every wave's slice, whose loads are issued before the
-// lengths are scanned.
-template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock, bool PLAN = false>
+// heads (each covering its group of query heads).
+template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock>
 __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) {
   using Wv = MfmaWave<T, D, OUT_F32, CONTIG, BS>;
   __shared__ SchedLds L;
   __shared__ __attribute__((aligned(16))) uint8_t vt[kSchedThreads / kWave][Wv::TILE_BYTES];
-  const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  Wv w(a, vt[wave], lane);
-  PlanPre<typename Wv::Tile> pre;
-  bool planned = false;
-  if constexpr (PLAN) {
-    const PlanHead ph = plan_read(a, blockIdx.x * (kSchedThreads / kWave) + wave);
-    const SchedCtx cx = sched_load(a);
-    planned = plan_start(a, ph, a.hkv, w, pre);
-    sched_scan<Wv::UT>(a, L, cx);
-  } else {
-    sched_build<Wv::UT>(a, L);
-  }
+  sched_build<Wv::UT>(a, L);
   if (blockIdx.x == 0) {  // zero rows of empty sequences: one thread per sequence
     const int64_t row_elems = (int64_t)a.hq * D;
     for (int s0 = threadIdx.x; s0 < a.n; s0 += kSchedThreads) {
@@ -420,7 +403,10 @@ __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) 
       }
     }
   }
-  sched_run<U, BS>(a, L, a.hkv, w, lane, pre, planned);
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  Wv w(a, vt[wave], lane);
+  sched_run<U, BS>(a, L, a.hkv, w, lane);
 }
 
 bool mfma_supports(int head_dim) { return head_dim == 64 || head_dim == 128; }
@@ -472,28 +458,6 @@ static int launch_bs_d(const AttnArgs& a, int bs, hipStream_t st) {
     case 64: hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, OUT_F32, false, 64>), grid, dim3(kSchedThreads), 0, st, a); return PF_OK;
     default: return PF_ERR_UNSUPPORTED;
   }
-}
-
-template <class T, int D>
-static void launch_planned_d(const AttnArgs& a, hipStream_t st) {
-  const dim3 grid(a.waves / (kSchedThreads / kWave));
-  if (a.out_f32)
-    hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, true, false, kBlock, true>), grid, dim3(kSchedThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_mfma_balanced<T, D, 1, false, false, kBlock, true>), grid, dim3(kSchedThreads), 0, st,
-                       a);
-}
-
-int launch_mfma_planned(const AttnArgs& a, int dtype, int head_dim, hipStream_t st) {
-  if (head_dim != 64 && head_dim != 128) return PF_ERR_UNSUPPORTED;
-  if (dtype == PF_F16) {
-    if (head_dim == 64) launch_planned_d<ElF16, 64>(a, st);
-    else launch_planned_d<ElF16, 128>(a, st);
-  } else {
-    if (head_dim == 64) launch_planned_d<ElBF16, 64>(a, st);
-    else launch_planned_d<ElBF16, 128>(a, st);
-  }
-  return PF_OK;
 }
 
 template <class T>

@@ -173,7 +173,7 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // npg-1 again and are not used.  proc(i, tile, ok) is called for every page
 // in order and may modify the tile (it is not used afterwards).
 template <int U, class Tile, class LoadF, class ProcF>
-__device__ __forceinline__ void page_pipeline(int npg, LoadF&& load, ProcF&& proc) {
+__device__ inline void page_pipeline(int npg, LoadF&& load, ProcF&& proc) {
   Tile ta[U], tb[U];
   bool oka[U], okb[U];
   auto load_unit = [&](int j, Tile* t, bool* ok) {
@@ -191,69 +191,6 @@ __device__ __forceinline__ void page_pipeline(int npg, LoadF&& load, ProcF&& pro
   const int nu = (npg + U - 1) / U;
   load_unit(0, ta, oka);
   int j = 0;
-  for (; j + 2 < nu; j += 2) {
-    load_unit(j + 1, tb, okb);
-    proc_unit(j, ta, oka);
-    load_unit(j + 2, ta, oka);
-    proc_unit(j + 1, tb, okb);
-  }
-  if (j + 1 < nu) {
-    load_unit(j + 1, tb, okb);
-    proc_unit(j, ta, oka);
-    proc_unit(j + 1, tb, okb);
-  } else {
-    proc_unit(j, ta, oka);
-  }
-}
-
-// page_pipeline with the loads of pages 0 and 1 already issued (into pre[0],
-// pre[1], valid flags okp): with one page per unit they are units 0 and 1,
-// with two pages per unit they are unit 0.  Same order of proc() calls and
-// the same tiles, so the same results; only the first loads come earlier.
-template <int U, class Tile, class LoadF, class ProcF>
-__device__ __forceinline__ void page_pipeline_pre(int npg, const Tile* pre, const bool* okp, LoadF&& load, ProcF&& proc) {
-  static_assert(U == 1 || U == 2, "two pre-issued pages fill one or two units");
-  Tile ta[U], tb[U];
-  bool oka[U], okb[U];
-  auto load_unit = [&](int j, Tile* t, bool* ok) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = j * U + u;
-      ok[u] = load(i < npg ? i : npg - 1, t[u]);
-    }
-  };
-  auto proc_unit = [&](int j, Tile* t, const bool* ok) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (j * U + u < npg) proc(j * U + u, t[u], ok[u]);
-  };
-  const int nu = (npg + U - 1) / U;
-  int j = 0;
-  if constexpr (U == 1) {
-    ta[0] = pre[0];
-    oka[0] = okp[0];
-    if (nu < 2) {
-      proc_unit(0, ta, oka);
-      return;
-    }
-    tb[0] = pre[1];
-    okb[0] = okp[1];
-    if (nu == 2) {
-      proc_unit(0, ta, oka);
-      proc_unit(1, tb, okb);
-      return;
-    }
-    // the first step of page_pipeline's loop, its load of unit 1 already done
-    proc_unit(0, ta, oka);
-    load_unit(2, ta, oka);
-    proc_unit(1, tb, okb);
-    j = 2;
-  } else {
-    ta[0] = pre[0];
-    ta[1] = pre[1];
-    oka[0] = okp[0];
-    oka[1] = okp[1];
-  }
   for (; j + 2 < nu; j += 2) {
     load_unit(j + 1, tb, okb);
     proc_unit(j, ta, oka);

@@ -483,81 +483,9 @@ int pf_block_tables(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int
 
 }  // extern "C"
 
-static void shadow_forget_locked(const pf_pool* pool) {
+static void export_forget_locked(const pf_pool* pool) {
   pool->shadow.target = nullptr;
   pool->shadow.max_blocks = -1;
-}
-
-// The previous export (shadow) and the plan it may have written.
-static void export_forget_locked(const pf_pool* pool) {
-  shadow_forget_locked(pool);
-  pool->plan_target = nullptr;
-}
-
-// The plan of the balanced schedule (see pf_sched.h) for these rows: the
-// same arithmetic as the kernels' schedule -- units per sequence from the
-// lengths clamped to the bound, items laid end to end, W equal slices of
-// ceil(total / W) units -- and, per wave, the table entries, keys and unit
-// indexes of the first two units of its slice (a one-unit slice repeats its
-// first unit with page -1; an empty slice has page -1 first).
-static void fill_plan(const std::vector<const pf_seq_entry*>& rows, const pf_plan_cfg& c, int32_t* out) {
-  const int32_t n = (int32_t)rows.size();
-  const int64_t X = c.items, UT = c.unit_tokens, W = c.waves;
-  std::vector<int64_t> P((size_t)n);
-  int64_t total = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    int64_t len = rows[(size_t)i]->len;
-    len = len < 0 ? 0 : (len > c.max_ctx ? c.max_ctx : len);
-    P[(size_t)i] = (len + UT - 1) / UT;
-    total += X * P[(size_t)i];
-  }
-  out[0] = kPlanMagic;
-  out[1] = c.items;
-  out[2] = c.waves;
-  out[3] = c.unit_tokens;
-  out[4] = n;
-  out[5] = c.max_ctx;
-  out[6] = (int32_t)(uint32_t)((uint64_t)total & 0xffffffffu);
-  out[7] = (int32_t)(uint32_t)((uint64_t)total >> 32);
-  const int64_t chunk = total > 0 ? (total + W - 1) / W : 1;
-  int32_t s = 0;
-  int64_t before = 0;  // units of the sequences before s
-  // (page, key, unit) of flat unit f; f never decreases from call to call
-  auto locate = [&](int64_t f, int32_t* page, int32_t* key, int32_t* unit) {
-    while (before + X * P[(size_t)s] <= f) before += X * P[(size_t)s++];
-    const int64_t rem = f - before;
-    const int64_t x = rem / P[(size_t)s], p = rem - x * P[(size_t)s];
-    const std::vector<int32_t>& pages = rows[(size_t)s]->pages;
-    const size_t blk = (size_t)(p / c.units_per_page);
-    *page = blk < pages.size() ? pages[blk] : -1;
-    *key = (int32_t)(x | ((p % c.units_per_page) << 16) | ((int64_t)s << 18));
-    *unit = (int32_t)p;
-  };
-  for (int64_t w = 0; w < W; ++w) {
-    int32_t* d = out + kPlanHeaderWords + kPlanWaveWords * w;
-    const int64_t wa = w * chunk, wb = std::min(wa + chunk, total);
-    d[6] = d[7] = 0;
-    if (wa >= wb) {
-      d[0] = d[1] = -1;
-      d[2] = d[3] = d[4] = d[5] = 0;
-      continue;
-    }
-    locate(wa, &d[0], &d[2], &d[4]);
-    if (wa + 1 < wb) {
-      locate(wa + 1, &d[1], &d[3], &d[5]);
-    } else {
-      d[1] = -1;
-      d[3] = d[2];
-      d[5] = d[4];
-    }
-  }
-}
-
-bool pf_plan_current(const pf_pool* pool, const void* target, int32_t n, int32_t max_blocks,
-                     const pf_plan_cfg& cfg) {
-  std::lock_guard<std::mutex> lk(pool->mu);
-  return target != nullptr && pool->plan_target == target && pool->plan_n == n &&
-         pool->plan_max_blocks == max_blocks && pool->plan_cfg == cfg;
 }
 
 void pf_export_forget(const pf_pool* pool) {
@@ -566,13 +494,9 @@ void pf_export_forget(const pf_pool* pool) {
 }
 
 int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_ids, int32_t n,
-                   int32_t max_blocks, bool step, int32_t* out, int64_t* pairs, const pf_plan_cfg* plan,
-                   int32_t* plan_out) {
+                   int32_t max_blocks, bool step, int32_t* out, int64_t* pairs) {
   return guarded([&]() -> int {
     if (!pool || !pairs || n < 0 || max_blocks < 0 || (n > 0 && (!seq_ids || !out))) return PF_ERR_INVALID;
-    if (plan && (!plan_out || plan->items <= 0 || plan->unit_tokens <= 0 || plan->units_per_page <= 0 ||
-                 plan->waves <= 0 || n >= (1 << 13) || plan->items > 0xffff || plan->units_per_page > 4))
-      return PF_ERR_INVALID;
     std::lock_guard<std::mutex> lk(pool->mu);
     std::vector<const pf_seq_entry*> rows((size_t)n);
     for (int32_t i = 0; i < n; ++i) {
@@ -591,16 +515,6 @@ int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_
       lens[i] = e.len;
       newest[i] = e.len - 1;
       if (step) newest[n + i] = e.len > 0 ? e.pages[(size_t)((e.len - 1) / B)] : -1;
-    }
-    // the plan goes with this export; any other export to its target ends it
-    if (plan) {
-      fill_plan(rows, *plan, plan_out);
-      pool->plan_target = target;
-      pool->plan_n = n;
-      pool->plan_max_blocks = max_blocks;
-      pool->plan_cfg = *plan;
-    } else if (target != nullptr && target == pool->plan_target) {
-      pool->plan_target = nullptr;
     }
     pf_export_shadow& sh = pool->shadow;
     bool delta = pool->export_delta && sh.target == target && target != nullptr && sh.max_blocks == max_blocks &&
@@ -654,7 +568,7 @@ int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_
       }
       sh.table.assign(out, out + nb);
     } else {
-      shadow_forget_locked(pool);
+      export_forget_locked(pool);
     }
     return PF_OK;
   });
@@ -669,16 +583,6 @@ int pf_export_staging(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, i
   *pairs = -1;
   if (n == 0) return PF_OK;
   return pf_fill_export(pool, meta_dev, seq_ids, n, max_blocks, step != 0, staging_host, pairs);
-}
-
-int64_t pf_plan_staging_words(int32_t n, int32_t max_blocks, int64_t plan_words) {
-  if (n < 0 || max_blocks < 0 || plan_words < 0) return -1;
-  return pf_plan_staging_offset(n, max_blocks) + plan_words;
-}
-
-int64_t pf_plan_meta_words(int32_t n, int32_t max_blocks, int64_t plan_words) {
-  if (n < 0 || max_blocks < 0 || plan_words < 0) return -1;
-  return pf_plan_meta_offset(n, max_blocks) + plan_words;
 }
 
 int pf_pool_set_option(pf_pool* pool, int32_t option, int32_t value) {

@@ -33,34 +33,6 @@ struct pf_export_shadow {
   std::vector<int32_t> table;  // [rows][max_blocks]
 };
 
-// The balanced schedule of one attention configuration, as far as a plan of
-// the first units of each wave's slice depends on it (pf_sched.h).
-struct pf_plan_cfg {
-  int32_t items = 0;           // items per sequence: query heads, or kv heads for the matrix-core kernel
-  int32_t unit_tokens = 0;     // tokens per unit of the walk
-  int32_t units_per_page = 0;
-  int32_t waves = 0;
-  int32_t max_ctx = 0;         // lengths are clamped to this
-  bool operator==(const pf_plan_cfg& o) const {
-    return items == o.items && unit_tokens == o.unit_tokens && units_per_page == o.units_per_page &&
-           waves == o.waves && max_ctx == o.max_ctx;
-  }
-};
-
-// Plan layout: header words, words per wave; where the plan sits in the
-// device metadata (after [n][max_blocks] table, n lengths, n newest
-// positions) and in the step staging (which also holds n destination pages),
-// both rounded up to 16 bytes.
-constexpr int32_t kPlanMagic = 0x504c414e;
-constexpr int64_t kPlanHeaderWords = 8;
-constexpr int64_t kPlanWaveWords = 8;
-inline int64_t pf_plan_meta_offset(int32_t n, int32_t max_blocks) {
-  return ((int64_t)n * max_blocks + 2 * (int64_t)n + 3) & ~(int64_t)3;
-}
-inline int64_t pf_plan_staging_offset(int32_t n, int32_t max_blocks) {
-  return ((int64_t)n * max_blocks + 3 * (int64_t)n + 3) & ~(int64_t)3;
-}
-
 struct pf_pool {
   pf_geometry g{};
   size_t elem_bytes = 0;
@@ -95,12 +67,6 @@ struct pf_pool {
   // Incremental table export (PF_OPT_EXPORT_DELTA) and its shadow.
   int32_t export_delta = 0;
   mutable pf_export_shadow shadow;
-  // The plan written by the last planned export, in the order calls were
-  // made: its target buffer (null: none), sequences, table width and
-  // configuration.  Any other export to that buffer clears it.
-  mutable const void* plan_target = nullptr;
-  mutable int32_t plan_n = 0, plan_max_blocks = 0;
-  mutable pf_plan_cfg plan_cfg;
   // Instrumentation events around the partition kernel (hipEvent_t).
   void* ev_start = nullptr;
   void* ev_stop = nullptr;
@@ -118,26 +84,10 @@ size_t pf_elem_bytes(int32_t dtype);
 // most n*max_blocks/2 of them; otherwise the whole [n][max_blocks] table
 // (padded with -1) at out[0..] and *pairs = -1.  Same errors as
 // pf_block_tables.
-// With plan non-null, also writes the plan of that configuration for these
-// sequences (their tables and lengths as exported) to plan_out and records it
-// as the plan of target; without, an export to the recorded target clears it.
 int pf_fill_export(const pf_pool* pool, const void* target, const uint64_t* seq_ids, int32_t n,
-                   int32_t max_blocks, bool step, int32_t* out, int64_t* pairs,
-                   const pf_plan_cfg* plan = nullptr, int32_t* plan_out = nullptr);
+                   int32_t max_blocks, bool step, int32_t* out, int64_t* pairs);
 
-// True if target's last export wrote a plan for these sequences' count, table
-// width and configuration (takes the pool lock).
-bool pf_plan_current(const pf_pool* pool, const void* target, int32_t n, int32_t max_blocks,
-                     const pf_plan_cfg& cfg);
-
-// The plan configuration of an attention call with these sizes under the
-// handle's options; false when the call would not use a plan (no balanced
-// schedule, pages other than 16 tokens, or a kernel without a planned form).
-bool pf_plan_config(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_context_len,
-                    pf_plan_cfg* cfg);
-
-// Forget the previous export (the next one is whole) and any plan; takes the
-// pool lock.
+// Forget the previous export (the next one is whole); takes the pool lock.
 void pf_export_forget(const pf_pool* pool);
 
 // Host half of pf_swap_out (to_host) / pf_swap_in: validate, move the

@@ -143,9 +143,6 @@ struct PrepArgs {
   const int32_t* tail_src;   // words after the n16 (whole) or lengths + newest (incremental)
   int32_t* tail_dst;
   int64_t tail;
-  const uint4* plan_src;     // planned export: the plan, plan16 16-byte words
-  uint4* plan_dst;
-  int64_t plan16;
   int64_t up_threads;
   uint8_t* pool;
   const uint8_t* k;
@@ -166,7 +163,6 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
       if (pr.x >= 0 && pr.x < a.table_words) a.table[pr.x] = pr.y;  // staging rewritten too early: no stray write
     }
     if (i < a.tail) a.tail_dst[i] = a.tail_src[i];
-    if (i < a.plan16) a.plan_dst[i] = a.plan_src[i];
     return;
   }
   int64_t r = i - a.up_threads;
@@ -280,17 +276,10 @@ extern "C" int pf_gather_kv(const pf_pool* pool, int32_t layer, const int32_t* b
 // Fill the staging for an export of seq_ids to meta_dev and set the upload
 // half of a: whole (16-byte words) or incremental (pairs).
 static int stage_export(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks, bool step,
-                        int32_t* staging_host, int32_t* meta_dev, pf::PrepArgs& a,
-                        const pf_plan_cfg* plan = nullptr) {
+                        int32_t* staging_host, int32_t* meta_dev, pf::PrepArgs& a) {
   int64_t pairs = -1;
-  int32_t* plan_host = plan ? staging_host + pf_plan_staging_offset(n, max_blocks) : nullptr;
-  const int st = pf_fill_export(pool, meta_dev, seq_ids, n, max_blocks, step, staging_host, &pairs, plan, plan_host);
+  const int st = pf_fill_export(pool, meta_dev, seq_ids, n, max_blocks, step, staging_host, &pairs);
   if (st != PF_OK) return st;
-  if (plan) {
-    a.plan_src = reinterpret_cast<const uint4*>(plan_host);
-    a.plan_dst = reinterpret_cast<uint4*>(meta_dev + pf_plan_meta_offset(n, max_blocks));
-    a.plan16 = (kPlanHeaderWords + kPlanWaveWords * (int64_t)plan->waves) / 4;
-  }
   const int64_t nb = (int64_t)n * max_blocks;
   if (pairs < 0) {
     const int64_t words = nb + 2 * (int64_t)n;
@@ -311,7 +300,6 @@ static int stage_export(const pf_pool* pool, const uint64_t* seq_ids, int32_t n,
   }
   int64_t up = a.n16 > a.npairs ? a.n16 : a.npairs;
   if (a.tail > up) up = a.tail;
-  if (a.plan16 > up) up = a.plan16;
   a.up_threads = up;
   return PF_OK;
 }
@@ -338,9 +326,9 @@ extern "C" int pf_export_tables(const pf_pool* pool, const uint64_t* seq_ids, in
   return PF_OK;
 }
 
-static int decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
-                          int32_t* staging_host, int32_t* meta_dev, const void* k, const void* v, int32_t layer0,
-                          int32_t num_layers, void* hip_stream, const pf_plan_cfg* plan) {
+extern "C" int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
+                                 int32_t* staging_host, int32_t* meta_dev, const void* k, const void* v,
+                                 int32_t layer0, int32_t num_layers, void* hip_stream) {
   using namespace pf;
   if (!pool || n < 0 || max_blocks < 0 || num_layers < 0) return PF_ERR_INVALID;
   if (!pool->dev) return PF_ERR_UNBOUND;
@@ -351,7 +339,7 @@ static int decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t 
   if (!staging_host || !meta_dev || !aligned16(staging_host) || !aligned16(meta_dev)) return PF_ERR_INVALID;
   if (num_layers > 0 && (!k || !v || !aligned16(k) || !aligned16(v))) return PF_ERR_INVALID;
   PrepArgs a{};
-  const int st = stage_export(pool, seq_ids, n, max_blocks, true, staging_host, meta_dev, a, plan);
+  const int st = stage_export(pool, seq_ids, n, max_blocks, true, staging_host, meta_dev, a);
   if (st != PF_OK) return st;
   a.pool = static_cast<uint8_t*>(pool->dev);
   a.k = static_cast<const uint8_t*>(k);
@@ -378,24 +366,6 @@ static int decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t 
     return PF_ERR_HIP;
   }
   return PF_OK;
-}
-
-extern "C" int pf_decode_prepare(const pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t max_blocks,
-                                 int32_t* staging_host, int32_t* meta_dev, const void* k, const void* v,
-                                 int32_t layer0, int32_t num_layers, void* hip_stream) {
-  return decode_prepare(pool, seq_ids, n, max_blocks, staging_host, meta_dev, k, v, layer0, num_layers, hip_stream,
-                        nullptr);
-}
-
-extern "C" int pf_decode_prepare_planned(const pf_pool* pool, const uint64_t* seq_ids, int32_t n,
-                                         int32_t max_blocks, int32_t* staging_host, int32_t* meta_dev,
-                                         const void* k, const void* v, int32_t layer0, int32_t num_layers,
-                                         int32_t num_q_heads, int32_t max_context_len, void* hip_stream) {
-  if (!pool || num_q_heads <= 0 || max_context_len < 0) return PF_ERR_INVALID;
-  pf_plan_cfg cfg;
-  const bool planned = pf_plan_config(pool, n, num_q_heads, max_context_len, &cfg);
-  return decode_prepare(pool, seq_ids, n, max_blocks, staging_host, meta_dev, k, v, layer0, num_layers, hip_stream,
-                        planned ? &cfg : nullptr);
 }
 
 extern "C" int pf_copy_pages(const pf_pool* pool, const int32_t* pairs, int32_t n, void* hip_stream) {

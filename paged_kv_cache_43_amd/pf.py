@@ -79,15 +79,6 @@ _SIGS = {
     "pf_export_staging": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _i32, _vp,
                                  ctypes.POINTER(ctypes.c_int64)]),
     "pf_decode_prepare": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
-    "pf_decode_prepare_planned": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
-    "pf_attention_plan_words": (ctypes.c_int64, [_vp, _i32, _i32, _i32]),
-    "pf_export_staging_planned": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, _i32, _i32, _vp,
-                                         ctypes.POINTER(ctypes.c_int64)]),
-    "pf_attention_plan_current": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32]),
-    "pf_plan_staging_words": (ctypes.c_int64, [_i32, _i32, ctypes.c_int64]),
-    "pf_plan_meta_words": (ctypes.c_int64, [_i32, _i32, ctypes.c_int64]),
-    "pf_paged_decode_attention_planned": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, ctypes.c_float,
-                                                 _vp, _i32, _vp, _sz, _vp]),
     "pf_scatter_kv": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp]),
     "pf_gather_kv": (_i32, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pf_attention_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
@@ -476,45 +467,6 @@ def pf_decode_prepare(pool, seq_ids, max_blocks, staging_host, meta_dev, k, v, l
                                  _stream(stream))
 
 
-def pf_decode_prepare_planned(pool, seq_ids, max_blocks, staging_host, meta_dev, k, v, layer0, num_layers,
-                              num_q_heads, max_context_len, stream=None):
-    """pf_decode_prepare plus the balanced schedule's plan for attention calls
-    with ``num_q_heads`` and ``max_context_len``; ``staging_host`` and
-    ``meta_dev`` sized by pf_plan_staging_words / pf_plan_meta_words."""
-    ids = _np(seq_ids, np.uint64)
-    return lib.pf_decode_prepare_planned(pool, _np_ptr(ids), len(ids), max_blocks, _pinned(staging_host),
-                                         _dev(meta_dev), _dev(k), _dev(v), layer0, num_layers, num_q_heads,
-                                         max_context_len, _stream(stream))
-
-
-def pf_export_staging_planned(pool, seq_ids, max_blocks, meta_dev, num_q_heads, max_context_len, staging_host):
-    """Host half of pf_decode_prepare_planned (no launch); ``meta_dev`` an
-    integer naming the target.  Returns (status, pairs)."""
-    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
-    pairs = ctypes.c_int64(0)
-    st = lib.pf_export_staging_planned(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), max_blocks,
-                                       meta_dev, num_q_heads, max_context_len, _host_ptr(staging_host),
-                                       ctypes.byref(pairs))
-    return st, pairs.value
-
-
-def pf_attention_plan_current(pool, meta_dev, n, max_blocks, num_q_heads, max_context_len):
-    return lib.pf_attention_plan_current(pool, meta_dev if isinstance(meta_dev, int) else _dev(meta_dev), n,
-                                         max_blocks, num_q_heads, max_context_len)
-
-
-def pf_attention_plan_words(pool, n, num_q_heads, max_context_len):
-    return lib.pf_attention_plan_words(pool, n, num_q_heads, max_context_len)
-
-
-def pf_plan_staging_words(n, max_blocks, plan_words):
-    return lib.pf_plan_staging_words(n, max_blocks, plan_words)
-
-
-def pf_plan_meta_words(n, max_blocks, plan_words):
-    return lib.pf_plan_meta_words(n, max_blocks, plan_words)
-
-
 def pf_scatter_kv(pool, layer, k, v, tok_seq, tok_pos, num_tokens, bt_dev, num_rows, max_blocks,
                   stream=None):
     return lib.pf_scatter_kv(pool, layer, _dev(k), _dev(v), _dev(tok_seq), _dev(tok_pos), num_tokens,
@@ -549,14 +501,6 @@ def pf_paged_decode_attention(pool, layer, q, num_q_heads, bt_dev, max_blocks, c
                                          _dev(ctx_dev), n, max_context_len, float(scale), _dev(out),
                                          DTYPES.get(out_dtype, out_dtype), _dev(workspace),
                                          workspace_bytes, _stream(stream))
-
-
-def pf_paged_decode_attention_planned(pool, layer, q, num_q_heads, meta_dev, max_blocks, n, max_context_len,
-                                      scale, out, out_dtype, workspace, workspace_bytes, stream=None):
-    return lib.pf_paged_decode_attention_planned(pool, layer, _dev(q), num_q_heads, _dev(meta_dev), max_blocks, n,
-                                                 max_context_len, float(scale), _dev(out),
-                                                 DTYPES.get(out_dtype, out_dtype), _dev(workspace),
-                                                 workspace_bytes, _stream(stream))
 
 
 def pf_paged_decode_attention_append(pool, layer, q, num_q_heads, k_new, v_new, bt_dev, max_blocks, ctx_dev,

@@ -75,8 +75,7 @@ class StagingRing:
 class PagedKV:
     """A pool handle bound to a torch-allocated device pool, plus device tables."""
 
-    def __init__(self, w, device="cuda", sentinel=True, extra_tokens=0, max_blocks=None, delta_export=True,
-                 plan_heads=None):
+    def __init__(self, w, device="cuda", sentinel=True, extra_tokens=0, max_blocks=None, delta_export=True):
         self.w = w
         self.device = device
         st, self.h = pf.pf_pool_create(w.num_pages, w.block, w.layers, w.hkv, w.d, w.dtype,
@@ -91,15 +90,10 @@ class PagedKV:
         self.max_blocks = max_blocks or w.max_blocks(extra_tokens)
         self.ids = np.arange(w.n, dtype=np.uint64)
         # Per-step metadata, packed so one copy moves it: block tables
-        # [n][max_blocks], lengths [n], and each sequence's newest position [n],
-        # then room for the balanced schedule's plan of attention calls with
-        # plan_heads query heads (pf_decode_prepare_planned): its size grows
-        # with the length bound, so it is taken at the largest bound.
+        # [n][max_blocks], lengths [n], and each sequence's newest position [n].
         nb = w.n * self.max_blocks
-        self.plan_heads = plan_heads or w.hq
-        self.plan_cap = pf.pf_attention_plan_words(self.h, w.n, self.plan_heads, self.max_blocks * w.block)
-        self.meta_elems = pf.pf_plan_meta_words(w.n, self.max_blocks, self.plan_cap)
-        self.stage_elems = pf.pf_plan_staging_words(w.n, self.max_blocks, self.plan_cap)
+        self.meta_elems = nb + 2 * w.n
+        self.stage_elems = nb + 3 * w.n
         self.meta = torch.empty(max(self.meta_elems, 1), dtype=torch.int32, device=device)
         self.bt = self.meta[:nb].view(w.n, self.max_blocks)
         self.ctx = self.meta[nb:nb + w.n]
@@ -113,7 +107,6 @@ class PagedKV:
         # per-layer path (the binding's tensor checks cost ~0.3 us each)
         self._bt_ptr = self.bt.data_ptr()
         self._ctx_ptr = self.ctx.data_ptr()
-        self._meta_ptr = self.meta.data_ptr()
         self._ws_ptr = None
 
     def close(self):
@@ -145,23 +138,14 @@ class PagedKV:
         pf.check(st, "pf_export_tables")
         self.ring.enqueued()
 
-    def decode_prepare(self, k_new, v_new, layer0=0, num_layers=None, plan_max_ctx=None):
+    def decode_prepare(self, k_new, v_new, layer0=0, num_layers=None):
         """Export the tables and scatter every sequence's newest token for
-        layers layer0.. (k_new, v_new: device [layers][n][H][D]) in one launch.
-        With plan_max_ctx, also write the plan of the attention calls that
-        follow with that length bound (pf_decode_prepare_planned), if it fits
-        the room reserved for it."""
+        layers layer0.. (k_new, v_new: device [layers][n][H][D]) in one launch."""
         num_layers = self.w.layers - layer0 if num_layers is None else num_layers
         buf = self.ring.acquire()
-        if plan_max_ctx is not None and \
-                pf.pf_attention_plan_words(self.h, self.w.n, self.plan_heads, plan_max_ctx) <= self.plan_cap:
-            st = pf.pf_decode_prepare_planned(self.h, self.ids, self.max_blocks, buf, self.meta, k_new, v_new,
-                                              layer0, num_layers, self.plan_heads, plan_max_ctx)
-            pf.check(st, "pf_decode_prepare_planned")
-        else:
-            st = pf.pf_decode_prepare(self.h, self.ids, self.max_blocks, buf, self.meta, k_new, v_new,
-                                      layer0, num_layers)
-            pf.check(st, "pf_decode_prepare")
+        st = pf.pf_decode_prepare(self.h, self.ids, self.max_blocks, buf, self.meta, k_new, v_new,
+                                  layer0, num_layers)
+        pf.check(st, "pf_decode_prepare")
         self.ring.enqueued()
 
     # --------------------------------------------------------------- kernels
@@ -185,25 +169,13 @@ class PagedKV:
         made again (no size query on every call)."""
         hq = hq or self.w.hq
         od = out_dtype or self.w.dtype
-        # the planned entry point reads the tables and lengths from self.meta,
-        # as the plain one would from self.bt / self.ctx, and uses the plan the
-        # last export wrote there only if it is current for this call
-        st = pf.pf_paged_decode_attention_planned(self.h, layer, q, hq, self._meta_ptr, self.max_blocks, self.w.n,
-                                                  max_ctx, scale, out, od, self._ws_ptr, self.ws_bytes, stream)
+        st = pf.pf_paged_decode_attention(self.h, layer, q, hq, self._bt_ptr, self.max_blocks, self._ctx_ptr,
+                                          self.w.n, max_ctx, scale, out, od, self._ws_ptr, self.ws_bytes, stream)
         if st == pf.PF_ERR_WORKSPACE:
             self.ensure_workspace(max_ctx, hq)
-            st = pf.pf_paged_decode_attention_planned(self.h, layer, q, hq, self._meta_ptr, self.max_blocks,
-                                                      self.w.n, max_ctx, scale, out, od, self._ws_ptr,
-                                                      self.ws_bytes, stream)
-        pf.check(st, "pf_paged_decode_attention_planned")
-
-    def attention_plain(self, layer, q, out, max_ctx, out_dtype=None, scale=0.0, stream=None, hq=None):
-        """pf_paged_decode_attention over self.bt / self.ctx (never a plan)."""
-        hq = hq or self.w.hq
-        self.ensure_workspace(max_ctx, hq)
-        st = pf.pf_paged_decode_attention(self.h, layer, q, hq, self._bt_ptr, self.max_blocks, self._ctx_ptr,
-                                          self.w.n, max_ctx, scale, out, out_dtype or self.w.dtype, self._ws_ptr,
-                                          self.ws_bytes, stream)
+            st = pf.pf_paged_decode_attention(self.h, layer, q, hq, self._bt_ptr, self.max_blocks,
+                                              self._ctx_ptr, self.w.n, max_ctx, scale, out, od, self._ws_ptr,
+                                              self.ws_bytes, stream)
         pf.check(st, "pf_paged_decode_attention")
 
     def attention_append(self, layer, q, k_new, v_new, out, max_ctx, out_dtype=None, scale=0.0, stream=None,

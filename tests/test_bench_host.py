@@ -108,7 +108,6 @@ def test_headline_is_compact_and_printed_last(monkeypatch, capsys):
     monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
     monkeypatch.setattr(bench, "run_gpu", lambda args, name, frames, *a, **k: _fake_run(name, frames))
     monkeypatch.setattr(bench, "run_twin", lambda name, frames, reps: {"paged_us": 1.0, "what": "t" * 100})
-    monkeypatch.setattr(bench, "run_plan_ab", lambda name, reps: {"partition_us_plan": 1.0})
     monkeypatch.setattr(bench, "run_cow", lambda *a: {"shared_pages": 1})
     monkeypatch.setattr(bench, "run_swap", lambda *a: {"out_ms": 6.4})
     monkeypatch.setattr(bench, "run_fused", lambda names, steps: {n: {"speedup": 1.0} for n in names})

@@ -16,15 +16,13 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fused", [False, True, "append", "planned"])
+@pytest.mark.parametrize("fused", [False, True, "append"])
 @pytest.mark.parametrize("name,steps", [("tiny", 40), ("gpt2", 12), ("gqa", 3), ("mixed", 3)])
 def test_decode_loop_matches_oracle(name, steps, fused):
     """fused=False: pf_export_tables then pf_scatter_kv per layer;
     fused=True: pf_decode_prepare (one launch for both); fused="append":
     pf_export_tables, then per layer the newest token is written by the
-    attention launch itself (pf_paged_decode_attention_append);
-    fused="planned": pf_decode_prepare_planned, whose plan the attention
-    calls use (checked current at every step where the schedule has one)."""
+    attention launch itself (pf_paged_decode_attention_append)."""
     print("decode loop", name, "fused" if fused else "separate", flush=True)
     from paged_kv_cache_43_amd import pf, runner
     w = inputs.Workload(name, frames="shuffled")
@@ -53,12 +51,6 @@ def test_decode_loop_matches_oracle(name, steps, fused):
         qd = runner.bits_to_device(q)
         if fused is True:
             kv.decode_prepare(runner.bits_to_device(nk), runner.bits_to_device(nv))
-        elif fused == "planned":
-            mc = int(lens.max())
-            kv.decode_prepare(runner.bits_to_device(nk), runner.bits_to_device(nv), plan_max_ctx=mc)
-            has_plan = pf.pf_attention_plan_words(kv.h, w.n, w.hq, mc) > 0
-            assert pf.pf_attention_plan_current(kv.h, kv.meta, w.n, kv.max_blocks, w.hq, mc) == int(has_plan)
-            assert has_plan == (name in ("gqa", "mixed"))
         else:
             kv.export_tables()
         for l in range(w.layers):
