@@ -57,9 +57,11 @@ typedef enum {
   PF_ERR_UNSUPPORTED = -7,  /* valid but not built: block size / head dim */
   PF_ERR_SHARED = -8,       /* growth would write into a page another table shares */
   PF_ERR_SWAPPED = -9,      /* the sequence is swapped out (pf_swap_out) */
-  PF_ERR_HOST_MEMORY = -10  /* host memory for the handle's own state ran out; any entry
+  PF_ERR_HOST_MEMORY = -10, /* host memory for the handle's own state ran out; any entry
                                point that grows the handle's state may return it (a batch
                                may then be partly applied: treat the handle as lost) */
+  PF_ERR_SCRATCH = -11      /* the call needs more workspace than the library's fixed device
+                               scratch holds (pf_paged_decode_attention_noalloc) */
 } pf_status;
 
 typedef struct {
@@ -354,6 +356,28 @@ int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q,
                               int32_t n, int32_t max_context_len, float scale, void* out,
                               int32_t out_dtype, void* workspace, size_t workspace_bytes,
                               void* hip_stream);
+
+/* pf_paged_decode_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and result, with the split partials in a
+ * fixed array of 16 MiB (PF_NOALLOC_SCRATCH_BYTES) of device memory inside
+ * the library instead of a caller's workspace.  Each GPU the library runs on
+ * holds its own copy until the process ends; the first call on a device asks
+ * the runtime for the copy's address (no allocation).  Nothing is allocated
+ * or freed by this call.  Every call on one GPU uses that GPU's copy, which
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads before the first has run) race on it, and their results are
+ * undefined.  The stream's device selects the copy (NULL: the current
+ * device).  Arguments as pf_paged_decode_attention without the workspace.
+ * Errors: as pf_paged_decode_attention, plus PF_ERR_SCRATCH when
+ * pf_attention_workspace_bytes for these sizes exceeds the scratch (nothing
+ * is enqueued), PF_ERR_HIP when the runtime gives no address. */
+#define PF_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int pf_paged_decode_attention_noalloc(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
+                                      const int32_t* bt_dev, int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
+                                      int32_t max_context_len, float scale, void* out, int32_t out_dtype,
+                                      void* hip_stream);
 
 /* pf_scatter_kv of each sequence's newest token fused into
  * pf_paged_decode_attention, in one launch (PageForge, "Five techniques" and its

@@ -995,6 +995,66 @@ extern "C" int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, con
                          max_context_len, scale, out, out_dtype, workspace, workspace_bytes, hip_stream);
 }
 
+// ------------------------------------------------- the no-allocation variant
+// The workspace of pf_paged_decode_attention_noalloc: a fixed device array,
+// one copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// its device address is asked of the runtime once per device, with that
+// device current, and that address is what the kernels receive.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The device address of `scratch` on device dev, or null if the runtime
+// cannot give it.  Thread-safe; the answer is kept per device.
+static void* scratch_on(int dev) {
+  static std::mutex mu;
+  static void* addr[64];
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+extern "C" int pf_paged_decode_attention_noalloc(const pf_pool* pool, int32_t layer, const void* q,
+                                                 int32_t num_q_heads, const int32_t* bt_dev, int32_t max_blocks,
+                                                 const int32_t* ctx_dev, int32_t n, int32_t max_context_len,
+                                                 float scale, void* out, int32_t out_dtype, void* hip_stream) {
+  if (!pool) return PF_ERR_INVALID;
+  const size_t need = pf_attention_workspace_bytes(pool, n, num_q_heads, max_context_len);
+  if (need > kScratchBytes) return PF_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = -1;
+    hipStream_t st = (hipStream_t)hip_stream;
+    if ((st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess) {
+      (void)hipGetLastError();
+      return PF_ERR_HIP;
+    }
+    ws = scratch_on(dev);
+    if (ws == nullptr) return PF_ERR_HIP;
+  }
+  return paged_attention(pool, layer, q, num_q_heads, nullptr, nullptr, bt_dev, max_blocks, ctx_dev, n,
+                         max_context_len, scale, out, out_dtype, ws, ws ? kScratchBytes : 0, hip_stream);
+}
+
 extern "C" int pf_paged_decode_attention_append(const pf_pool* pool, int32_t layer, const void* q,
                                                 int32_t num_q_heads, const void* k_new, const void* v_new,
                                                 const int32_t* bt_dev, int32_t max_blocks, const int32_t* ctx_dev,

@@ -651,6 +651,7 @@ const char* pf_status_string(int status) {
     case PF_ERR_SHARED: return "growth would write into a page another sequence shares (use pf_grow_seqs)";
     case PF_ERR_SWAPPED: return "sequence is swapped out";
     case PF_ERR_HOST_MEMORY: return "host memory for the handle state ran out";
+    case PF_ERR_SCRATCH: return "needs more workspace than the fixed device scratch holds";
     default: return "unknown status";
   }
 }

@@ -31,6 +31,8 @@ PF_ERR_UNSUPPORTED = -7
 PF_ERR_SHARED = -8
 PF_ERR_SWAPPED = -9
 PF_ERR_HOST_MEMORY = -10
+PF_ERR_SCRATCH = -11
+PF_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 PF_OPT_SPLIT_TOKENS = 0
 PF_OPT_GQA_MFMA = 1
@@ -84,6 +86,8 @@ _SIGS = {
     "pf_attention_workspace_bytes": (_sz, [_vp, _i32, _i32, _i32]),
     "pf_paged_decode_attention": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
                                          ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
+    "pf_paged_decode_attention_noalloc": (_i32, [_vp, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
+                                                 ctypes.c_float, _vp, _i32, _vp]),
     "pf_paged_decode_attention_append": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                                 ctypes.c_float, _vp, _i32, _vp, _sz, _vp]),
     "pf_contiguous_decode_attention": (_i32, [_vp, _vp, _i32, _vp, _vp, ctypes.c_int64, ctypes.c_int64,
@@ -501,6 +505,13 @@ def pf_paged_decode_attention(pool, layer, q, num_q_heads, bt_dev, max_blocks, c
                                          _dev(ctx_dev), n, max_context_len, float(scale), _dev(out),
                                          DTYPES.get(out_dtype, out_dtype), _dev(workspace),
                                          workspace_bytes, _stream(stream))
+
+
+def pf_paged_decode_attention_noalloc(pool, layer, q, num_q_heads, bt_dev, max_blocks, ctx_dev, n,
+                                      max_context_len, scale, out, out_dtype, stream=None):
+    return lib.pf_paged_decode_attention_noalloc(pool, layer, _dev(q), num_q_heads, _dev(bt_dev), max_blocks,
+                                                 _dev(ctx_dev), n, max_context_len, float(scale), _dev(out),
+                                                 DTYPES.get(out_dtype, out_dtype), _stream(stream))
 
 
 def pf_paged_decode_attention_append(pool, layer, q, num_q_heads, k_new, v_new, bt_dev, max_blocks, ctx_dev,
