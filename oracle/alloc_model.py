@@ -52,20 +52,25 @@ where the blog is silent:
   freeing sequence's table lists them, last first, skipping pages still held.
 
 Swapping (PagedAttention blog, "Preemption and Swapping": a sequence's blocks
-are evicted to CPU memory and copied back when it resumes, block by block).
+are evicted to CPU memory and copied back when it resumes; swapping works on
+blocks, so part of a sequence may be on the GPU and the rest on the CPU).
 Readings where the blog is silent:
 
 * The backing store is a set of page-sized host slots with its own LIFO
   stack (slot 0 first), like the device pool.
-* A whole sequence is swapped: every page of its table goes to a slot, in
-  table order, and the sequence drops its hold on the device pages (a page
-  another table still holds stays where it is; the swapped copy is private).
-  Its device pages go back to the stack as a free would push them.
-* Swapping in takes pages from the device stack in table order, copies the
-  slots back and returns the slots to their stack last first, as a free does.
-* Both are all or nothing over a batch of sequences (not enough slots, or
-  not enough device pages); a swapped sequence cannot grow, fork or be
-  exported (SWAPPED) until it is swapped in; freeing it releases its slots.
+* A block range of one sequence can be swapped out (every block in it on
+  the device) or in (every block in it on the host); a whole sequence, or
+  every block of a batch of sequences that is on the host, likewise.
+* Swapping out takes a slot per block in block order; the sequence drops
+  its hold on those pages (a page another table still holds stays where it
+  is; the swapped copy is private), which go back to the stack last block
+  first, as a free would push them.
+* Swapping in takes pages from the device stack in block order, copies the
+  slots back and returns the slots to their stack last block first.
+* Every swap is all or nothing (not enough slots, or not enough device
+  pages); a sequence with any block on the host cannot grow, fork or be
+  exported (SWAPPED) until all its blocks are back; freeing it releases its
+  device pages and its slots.
 """
 
 OK = "ok"
@@ -100,7 +105,9 @@ class AllocModel:
         self.peak = 0                 # most pages in use at once (see reset_peak)
         self.slot_stack = []          # host swap slots, top at the end
         self.num_slots = 0
-        self.swapped = {}             # seq id -> host slots, in table order
+        # sequences with blocks on the host: id -> (pages, host), pages[b] the
+        # device page of block b or None, host[b] the slot of a block on the host
+        self.offdev = {}
 
     # -- operations -----------------------------------------------------------
     def _writes_shared(self, seq_id, new_len):
@@ -115,7 +122,7 @@ class AllocModel:
         """Grow ``seq_id`` to ``new_len`` tokens.  Returns (status, n_new_pages)."""
         if new_len < 0:
             return INVALID, 0
-        if seq_id in self.swapped:
+        if seq_id in self.offdev:
             return SWAPPED, 0
         table = self.tables.get(seq_id, [])
         current = self.lengths.get(seq_id, 0)
@@ -137,11 +144,11 @@ class AllocModel:
     def fork(self, parent, child):
         """``child`` starts as a copy of ``parent``'s table and length, sharing
         every page.  Returns a status."""
-        if parent in self.swapped:
+        if parent in self.offdev:
             return SWAPPED
         if parent not in self.tables:
             return UNKNOWN_SEQ
-        if child in self.tables or child in self.swapped:
+        if child in self.tables or child in self.offdev:
             return INVALID
         self.tables[child] = list(self.tables[parent])
         self.lengths[child] = self.lengths[parent]
@@ -155,7 +162,7 @@ class AllocModel:
         every page taken from the stack, the copy's destination included."""
         if new_len < 0:
             return INVALID, 0, None
-        if seq_id in self.swapped:
+        if seq_id in self.offdev:
             return SWAPPED, 0, None
         table = self.tables.get(seq_id, [])
         current = self.lengths.get(seq_id, 0)
@@ -195,7 +202,7 @@ class AllocModel:
             if new_len < 0 or new_len < lens.get(seq_id, 0):
                 return INVALID, [0] * len(entries), []
             lens[seq_id] = new_len
-        if any(seq_id in self.swapped for seq_id, _ in entries):
+        if any(seq_id in self.offdev for seq_id, _ in entries):
             return SWAPPED, [0] * len(entries), []
         saved = (self.stack[:], {k: v[:] for k, v in self.tables.items()}, dict(self.lengths), self.refs[:],
                  self.peak)
@@ -212,10 +219,13 @@ class AllocModel:
 
     def free(self, seq_id):
         """Drop ``seq_id``'s hold on its pages, returning those no other table
-        holds to the pool, and forget the sequence."""
-        if seq_id in self.swapped:
-            for slot in reversed(self.swapped.pop(seq_id)):
-                self.slot_stack.append(slot)
+        holds to the pool, return its host slots (last block first), and
+        forget the sequence."""
+        if seq_id in self.offdev:
+            pages, host = self.offdev.pop(seq_id)
+            self._release([p for p in pages if p is not None])
+            for b in sorted(host, reverse=True):
+                self.slot_stack.append(host[b])
             del self.lengths[seq_id]
             return OK
         if seq_id not in self.tables:
@@ -237,13 +247,64 @@ class AllocModel:
         self.num_slots = num_slots
         self.slot_stack = list(reversed(range(num_slots)))
 
+    @property
+    def swapped(self):
+        """Sequences with blocks on the host: id -> the slots of those blocks,
+        in block order."""
+        return {s: [host[b] for b in sorted(host)] for s, (_, host) in self.offdev.items()}
+
+    def _split(self, seq_id):
+        """(pages, host) of a live sequence (pages: None for blocks on the host)."""
+        if seq_id in self.offdev:
+            return self.offdev[seq_id]
+        return self.tables[seq_id], {}
+
+    def _move_out(self, seq_id, blocks):
+        """Blocks (all on the device) to host slots taken in block order; the
+        pages are released last block first.  Returns the (page, slot) copies."""
+        pages, host = self._split(seq_id)
+        pages, host = list(pages), dict(host)
+        copies = []
+        for b in blocks:
+            slot = self.slot_stack.pop()
+            copies.append((pages[b], slot))
+            host[b] = slot
+        self._release([pages[b] for b in blocks])
+        for b in blocks:
+            pages[b] = None
+        self.tables.pop(seq_id, None)
+        self.offdev[seq_id] = (pages, host)
+        return copies
+
+    def _move_in(self, seq_id, blocks):
+        """Blocks (all on the host) to pages popped in block order; the slots
+        return last block first.  Returns the (slot, page) copies."""
+        pages, host = self.offdev[seq_id]
+        pages, host = list(pages), dict(host)
+        copies = []
+        for b in blocks:
+            page = self.stack.pop()
+            self.refs[page] = 1
+            copies.append((host[b], page))
+            pages[b] = page
+        for b in reversed(blocks):
+            self.slot_stack.append(host.pop(b))
+        if host:
+            self.offdev[seq_id] = (pages, host)
+        else:
+            del self.offdev[seq_id]
+            self.tables[seq_id] = pages
+        self._note_peak()
+        return copies
+
     def swap_out(self, seq_ids):
-        """Evict whole sequences.  Returns (status, [(page, slot), ...]) with
-        the copies to make, device to host, in order."""
+        """Evict whole sequences (every block on the device).  Returns
+        (status, [(page, slot), ...]) with the copies to make, device to host,
+        in order."""
         if len(set(seq_ids)) != len(seq_ids):
             return INVALID, []
         for s in seq_ids:
-            if s in self.swapped:
+            if s in self.offdev:
                 return SWAPPED, []
             if s not in self.tables:
                 return UNKNOWN_SEQ, []
@@ -251,47 +312,69 @@ class AllocModel:
             return OOM, []
         copies = []
         for s in seq_ids:
-            slots = []
-            for page in self.tables[s]:
-                slot = self.slot_stack.pop()
-                slots.append(slot)
-                copies.append((page, slot))
-            self._release(self.tables[s])
-            del self.tables[s]
-            self.swapped[s] = slots
+            copies += self._move_out(s, list(range(len(self.tables[s]))))
         return OK, copies
 
     def swap_in(self, seq_ids):
-        """Bring whole sequences back.  Returns (status, [(slot, page), ...])
-        with the copies to make, host to device, in order."""
+        """Bring back every block of these sequences that is on the host.
+        Returns (status, [(slot, page), ...]) with the copies to make, host to
+        device, in order."""
         if len(set(seq_ids)) != len(seq_ids):
             return INVALID, []
         for s in seq_ids:
-            if s not in self.swapped:
+            if s not in self.offdev:
                 return (INVALID if s in self.tables else UNKNOWN_SEQ), []
-        if sum(len(self.swapped[s]) for s in seq_ids) > len(self.stack):
+        if sum(len(self.offdev[s][1]) for s in seq_ids) > len(self.stack):
             return OOM, []
         copies = []
         for s in seq_ids:
-            slots = self.swapped.pop(s)
-            table = []
-            for slot in slots:
-                page = self.stack.pop()
-                self.refs[page] = 1
-                table.append(page)
-                copies.append((slot, page))
-            for slot in reversed(slots):
-                self.slot_stack.append(slot)
-            self.tables[s] = table
-        self._note_peak()
+            copies += self._move_in(s, sorted(self.offdev[s][1]))
         return OK, copies
+
+    def _block_range(self, seq_id, first, count):
+        """The blocks [first, first + count) of a live sequence, or None if the
+        range is empty or leaves its table."""
+        pages, _ = self._split(seq_id)
+        if count < 1 or first < 0 or first + count > len(pages):
+            return None
+        return list(range(first, first + count))
+
+    def swap_out_blocks(self, seq_id, first, count):
+        """Evict blocks [first, first + count) of one sequence, every one of
+        them on the device.  Returns (status, [(page, slot), ...])."""
+        if seq_id not in self.tables and seq_id not in self.offdev:
+            return UNKNOWN_SEQ, []
+        blocks = self._block_range(seq_id, first, count)
+        if blocks is None or any(self._split(seq_id)[0][b] is None for b in blocks):
+            return INVALID, []
+        if len(blocks) > len(self.slot_stack):
+            return OOM, []
+        return OK, self._move_out(seq_id, blocks)
+
+    def swap_in_blocks(self, seq_id, first, count):
+        """Bring back blocks [first, first + count) of one sequence, every one
+        of them on the host.  Returns (status, [(slot, page), ...])."""
+        if seq_id not in self.tables and seq_id not in self.offdev:
+            return UNKNOWN_SEQ, []
+        blocks = self._block_range(seq_id, first, count)
+        if blocks is None or any(b not in self._split(seq_id)[1] for b in blocks):
+            return INVALID, []
+        if len(blocks) > len(self.stack):
+            return OOM, []
+        return OK, self._move_in(seq_id, blocks)
 
     # -- queries --------------------------------------------------------------
     def free_pages(self):
         return len(self.stack)
 
     def table(self, seq_id):
-        return list(self.tables[seq_id])
+        """The sequence's block table: a page per block, None for a block on
+        the host."""
+        return list(self._split(seq_id)[0])
+
+    def host_blocks(self, seq_id):
+        """Block -> host slot for the sequence's blocks on the host."""
+        return dict(self._split(seq_id)[1])
 
     def seq_len(self, seq_id):
         return self.lengths[seq_id]
@@ -320,6 +403,8 @@ class AllocModel:
         max_blocks raises ValueError."""
         rows, lens = [], []
         for s in seq_ids:
+            if s in self.offdev:
+                raise ValueError("a sequence with blocks on the host has no device table")
             t = self.tables[s]
             if len(t) > max_blocks:
                 raise ValueError("sequence needs more than max_blocks blocks")
@@ -330,22 +415,25 @@ class AllocModel:
     # -- invariants (checked by the tests after every op) ----------------------
     def check_invariants(self):
         holders = [0] * self.num_pages
-        for s, t in self.tables.items():
+        assert not set(self.tables) & set(self.offdev), "a sequence both resident and not"
+        for s, t in list(self.tables.items()) + [(s, e[0]) for s, e in self.offdev.items()]:
             n = self.lengths[s]
             assert len(t) == blocks_for(n, self.block_size), "ceil(len/B) blocks per sequence"
             assert self.block_size * len(t) - n <= self.block_size - 1, "waste at most B-1 slots"
-            assert len(t) == len(set(t)), "a page twice in one table"
-            for p in t:
+            dev = [p for p in t if p is not None]
+            assert len(dev) == len(set(dev)), "a page twice in one table"
+            for p in dev:
                 holders[p] += 1
+        for s, (pages, host) in self.offdev.items():
+            assert host, "listed as off the device with every block on it"
+            assert set(host) == {b for b, p in enumerate(pages) if p is None}, "a block in neither place"
         assert holders == self.refs, "reference counts differ from the tables holding each page"
         live = {p for p in range(self.num_pages) if holders[p] > 0}
         assert not live & set(self.stack), "a live page is also on the free list"
         assert len(self.stack) + len(live) == self.num_pages, "pages leaked or duplicated"
         assert len(set(self.stack)) == len(self.stack), "page pushed twice"
-        held = [slot for slots in self.swapped.values() for slot in slots]
+        held = [slot for _, host in self.offdev.values() for slot in host.values()]
         assert len(held) == len(set(held)), "a host slot held twice"
         assert not set(held) & set(self.slot_stack), "a held slot is also free"
         assert len(held) + len(self.slot_stack) == self.num_slots, "host slots leaked"
-        for s, slots in self.swapped.items():
-            assert s not in self.tables and len(slots) == blocks_for(self.lengths[s], self.block_size)
 

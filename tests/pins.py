@@ -503,6 +503,152 @@ def pin_swap_random_ops_invariants(o):
     m.check_invariants()
 
 
+def pin_block_swap_round_trip(o):
+    """Blocks 1 and 2 of a five-block sequence swapped out (some blocks of the
+    sequence on the device, others on the host), their pages reused and
+    overwritten by another sequence, then swapped back into other pages:
+    every block reads back, and the stacks move last block first."""
+    am, L = o.alloc_model, o.layout
+    rng = _rng(44)
+    g = L.Geometry(12, 16, 2, 2, 4, 2)
+    m = am.AllocModel(12, 16, [int(x) for x in rng.permutation(12)])
+    m.set_swap_space(4)
+    host = np.zeros(4 * g.page_elems(), dtype=np.uint16)
+    assert m.alloc(0, 70) == (am.OK, 5)
+    pool, hist = _image_with(o, g, m, [0], rng)
+    t0 = m.table(0)
+    st, copies = m.swap_out_blocks(0, 1, 2)
+    assert st == am.OK and copies == [(t0[1], 0), (t0[2], 1)]
+    assert m.table(0) == [t0[0], None, None, t0[3], t0[4]] and m.host_blocks(0) == {1: 0, 2: 1}
+    assert m.free_pages() == 12 - 5 + 2 and m.stack[-2:] == [t0[2], t0[1]]   # block 1's page on top
+    assert 0 not in m.tables and m.swapped == {0: [0, 1]} and m.seq_len(0) == 70
+    pool, host = L.swap_copy(pool, host, g, copies, True)
+    m.check_invariants()
+    assert m.alloc(1, 32) == (am.OK, 2) and m.table(1) == [t0[1], t0[2]]    # reuses them, LIFO
+    pool, _ = _image_with(o, g, m, [1], rng, pool)                           # and overwrites them
+    st, back = m.swap_in_blocks(0, 1, 2)
+    assert st == am.OK and [c[0] for c in back] == [0, 1]
+    new = m.table(0)
+    assert [c[1] for c in back] == new[1:3] and not set(new[1:3]) & set(m.table(1))
+    assert new[0] == t0[0] and new[3:] == t0[3:]
+    assert m.slot_stack[-2:] == [1, 0] and 0 in m.tables and not m.swapped  # slots back last block first
+    pool, host = L.swap_copy(pool, host, g, back, False)
+    assert _reads_back(o, g, pool, m, 0, hist[0])
+    m.check_invariants()
+
+
+def pin_block_swap_rules(o):
+    """A range must lie in the table and be wholly on one side; all or
+    nothing on slots and on pages; a sequence with blocks on the host cannot
+    grow, fork, be exported or be swapped out whole, but can be swapped in
+    whole (the blocks still out come back) or block by block, also after a
+    whole swap-out (blocks fetched back one at a time)."""
+    am = o.alloc_model
+    m = am.AllocModel(10, 16)
+    m.set_swap_space(3)
+    assert m.alloc(0, 64) == (am.OK, 4)                # blocks 0..3 on pages 0..3
+    assert m.swap_out_blocks(5, 0, 1) == (am.UNKNOWN_SEQ, [])
+    for first, count in ((0, 0), (-1, 1), (3, 2), (4, 1), (0, 5)):
+        assert m.swap_out_blocks(0, first, count) == (am.INVALID, [])
+    assert m.swap_out_blocks(0, 0, 4) == (am.OOM, [])
+    assert m.free_pages() == 6 and len(m.slot_stack) == 3 and m.table(0) == [0, 1, 2, 3]
+    assert m.swap_out_blocks(0, 2, 2) == (am.OK, [(2, 0), (3, 1)])
+    assert m.swap_out_blocks(0, 1, 2) == (am.INVALID, [])       # block 2 is already out
+    assert m.swap_in_blocks(0, 1, 2) == (am.INVALID, [])        # block 1 is on the device
+    assert m.alloc(0, 65) == (am.SWAPPED, 0) and m.grow(0, 65)[0] == am.SWAPPED
+    assert m.fork(0, 7) == am.SWAPPED and m.swap_out([0]) == (am.SWAPPED, [])
+    try:
+        m.block_tables([0], 8)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a sequence with blocks on the host has no device table")
+    assert m.alloc(1, 16 * 7) == (am.OK, 7)            # 7 of the 8 free pages
+    assert m.swap_in_blocks(0, 2, 2) == (am.OOM, []) and m.host_blocks(0) == {2: 0, 3: 1}
+    assert m.swap_in([0]) == (am.OOM, []) and m.free_pages() == 1
+    m.check_invariants()
+    m.free(1)
+    st, back = m.swap_in([0])                          # whole swap-in: the two blocks still out
+    assert st == am.OK and [c[0] for c in back] == [0, 1] and 0 in m.tables and len(m.slot_stack) == 3
+    assert m.swap_out([0]) == (am.OOM, [])             # four blocks, three slots
+    m.set_swap_space(4)
+    st, out = m.swap_out([0])
+    assert st == am.OK and [c[1] for c in out] == [0, 1, 2, 3] and m.table(0) == [None] * 4
+    st, b1 = m.swap_in_blocks(0, 1, 1)                 # fetched back just in time, one block
+    assert st == am.OK and b1[0][0] == 1 and m.table(0)[1] == b1[0][1]
+    assert m.table(0)[0] is None and m.host_blocks(0) == {0: 0, 2: 2, 3: 3}
+    assert m.free(0) == am.OK and len(m.slot_stack) == 4 and m.free_pages() == 10
+    m.check_invariants()
+
+
+def pin_block_swap_shared_prefix(o):
+    """Swapping out a block a fork shares keeps the page for the other
+    holder; the block comes back into a private page with its contents."""
+    am, L = o.alloc_model, o.layout
+    rng = _rng(45)
+    g = L.Geometry(12, 16, 1, 2, 4, 2)
+    m = am.AllocModel(12, 16, [int(x) for x in rng.permutation(12)])
+    m.set_swap_space(4)
+    host = np.zeros(4 * g.page_elems(), dtype=np.uint16)
+    m.alloc(0, 48)
+    pool, hist = _image_with(o, g, m, [0], rng)
+    assert m.fork(0, 1) == am.OK
+    shared = m.table(0)
+    st, copies = m.swap_out_blocks(1, 0, 2)
+    assert st == am.OK and [c[0] for c in copies] == shared[:2]
+    assert m.refcount(shared[0]) == 1 and m.refcount(shared[1]) == 1 and m.refcount(shared[2]) == 2
+    assert m.free_pages() == 12 - 3
+    pool, host = L.swap_copy(pool, host, g, copies, True)
+    st, back = m.swap_in_blocks(1, 0, 2)
+    pool, host = L.swap_copy(pool, host, g, back, False)
+    assert not set(m.table(1)[:2]) & set(shared) and m.table(1)[2] == shared[2]
+    assert _reads_back(o, g, pool, m, 0, hist[0]) and _reads_back(o, g, pool, m, 1, hist[0])
+    m.check_invariants()
+
+
+def pin_block_swap_random_ops_invariants(o):
+    """Random alloc / fork / grow / block-range and whole swaps / free keep
+    every count consistent and lose no page or slot."""
+    am = o.alloc_model
+    rng = _rng(46)
+    m = am.AllocModel(80, 16, [int(x) for x in rng.permutation(80)])
+    m.set_swap_space(30)
+    nxt = 0
+    for step in range(1500):
+        live = sorted(set(m.tables) | set(m.offdev))
+        r = rng.random()
+        if not live or r < 0.15:
+            m.alloc(nxt, int(rng.integers(1, 70)))
+            nxt += 1
+        elif r < 0.22:
+            m.fork(int(rng.choice(live)), nxt)
+            nxt += 1
+        elif r < 0.35:
+            s = int(rng.choice(live))
+            m.grow(s, m.seq_len(s) + int(rng.integers(0, 20)))
+        elif r < 0.55:
+            s = int(rng.choice(live))
+            nb = len(m.table(s))
+            first = int(rng.integers(0, nb + 1))
+            m.swap_out_blocks(s, first, int(rng.integers(0, nb - first + 2)))
+        elif r < 0.75:
+            s = int(rng.choice(live))
+            nb = len(m.table(s))
+            first = int(rng.integers(0, nb + 1))
+            m.swap_in_blocks(s, first, int(rng.integers(0, nb - first + 2)))
+        elif r < 0.82:
+            m.swap_out([int(rng.choice(live))])
+        elif r < 0.9:
+            m.swap_in([int(rng.choice(live))])
+        else:
+            m.free(int(rng.choice(live)))
+        m.check_invariants()
+    for s in sorted(set(m.tables) | set(m.offdev)):
+        assert m.free(s) == am.OK
+    assert m.free_pages() == 80 and len(m.slot_stack) == 30
+    m.check_invariants()
+
+
 # ----------------------------------------------------------------------------
 # O2 / O3 layout
 # ----------------------------------------------------------------------------

@@ -214,10 +214,51 @@ class _UncheckedWidthTablesModel(oracle.alloc_model.AllocModel):
     def block_tables(self, seq_ids, max_blocks):
         rows, lens = [], []
         for s in seq_ids:                                                 # truncates instead of refusing
+            if s in self.offdev:
+                raise ValueError("blocks on the host")
             t = self.tables[s][:max_blocks]
             rows.append(t + [-1] * (max_blocks - len(t)))
             lens.append(self.lengths[s])
         return rows, lens
+
+
+class _BlockOutForwardPushModel(oracle.alloc_model.AllocModel):
+    def _move_out(self, seq_id, blocks):
+        before = len(self.stack)
+        copies = super()._move_out(seq_id, blocks)
+        self.stack[before:] = self.stack[before:][::-1]             # pushed first block first: last on top
+        return copies
+
+
+class _BlockInKeepsSlotsModel(oracle.alloc_model.AllocModel):
+    def swap_in_blocks(self, seq_id, first, count):
+        before = list(self.slot_stack)
+        st, copies = super().swap_in_blocks(seq_id, first, count)
+        if st == oracle.alloc_model.OK:
+            self.slot_stack = before                                # slots never returned
+        return st, copies
+
+
+class _BlockRangeOffByOneModel(oracle.alloc_model.AllocModel):
+    def swap_out_blocks(self, seq_id, first, count):
+        nb = len(self.table(seq_id)) if seq_id in self.tables or seq_id in self.offdev else 0
+        return super().swap_out_blocks(seq_id, first + 1 if first + count < nb else first, count)
+
+
+class _WholeSwapInWholeOnlyModel(oracle.alloc_model.AllocModel):
+    def swap_in(self, seq_ids):
+        for s in seq_ids:
+            if s in self.offdev and any(p is not None for p in self.offdev[s][0]):
+                return oracle.alloc_model.INVALID, []               # refuses a partly swapped sequence
+        return super().swap_in(seq_ids)
+
+
+class _BlockOutPartialOnOomModel(oracle.alloc_model.AllocModel):
+    def swap_out_blocks(self, seq_id, first, count):
+        st, copies = super().swap_out_blocks(seq_id, first, count)
+        if st == oracle.alloc_model.OOM and self.slot_stack:
+            return super().swap_out_blocks(seq_id, first, len(self.slot_stack))   # moves what fits
+        return st, copies
 
 
 MUTANTS = {
@@ -246,6 +287,11 @@ MUTANTS = {
     "tables_pad_with_zero": (oracle.alloc_model, "AllocModel", _ZeroPaddedTablesModel),
     "tables_rows_sorted_by_id": (oracle.alloc_model, "AllocModel", _SortedRowsTablesModel),
     "tables_truncate_long_rows": (oracle.alloc_model, "AllocModel", _UncheckedWidthTablesModel),
+    "block_swap_out_pushes_forward": (oracle.alloc_model, "AllocModel", _BlockOutForwardPushModel),
+    "block_swap_in_keeps_slots": (oracle.alloc_model, "AllocModel", _BlockInKeepsSlotsModel),
+    "block_swap_range_off_by_one": (oracle.alloc_model, "AllocModel", _BlockRangeOffByOneModel),
+    "whole_swap_in_refuses_partial": (oracle.alloc_model, "AllocModel", _WholeSwapInWholeOnlyModel),
+    "block_swap_out_partial_on_oom": (oracle.alloc_model, "AllocModel", _BlockOutPartialOnOomModel),
 }
 
 
