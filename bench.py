@@ -483,6 +483,26 @@ def run_swap(n_seqs, reps, seed=44):
             torch.cuda.synchronize()
             if r >= 2:
                 acc.append(a.elapsed_time(b) * 1e3)
+    # block ranges: the second half of every sequence's blocks out and back
+    # (the blocks a scheduler would evict first while the prefix stays), one
+    # call per sequence
+    halves = [(i, nb_i // 2, nb_i - nb_i // 2) for i, nb_i in enumerate(-(-lens // B))]
+    half_pages = sum(c for _, _, c in halves)
+    b_out, b_in = [], []
+    for r in range(reps + 2):
+        for to_host, acc in ((True, b_out), (False, b_in)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            fn = pf.pf_swap_out_blocks if to_host else pf.pf_swap_in_blocks
+            off = 0
+            for i, first, count in halves:
+                pf.check(fn(h, int(ids[i]), int(first), int(count), staging[off:], 2 * count))
+                off += 2 * count
+            b.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                acc.append(a.elapsed_time(b) * 1e3)
     dev = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
     dma_out, dma_in = [], []
     for r in range(reps + 2):
@@ -508,6 +528,11 @@ def run_swap(n_seqs, reps, seed=44):
            "dma_copy_d2h_GBps": round(nbytes / med(dma_out) / 1e3, 1),
            "dma_copy_h2d_GBps": round(nbytes / med(dma_in) / 1e3, 1),
            "host_link_peak_GBps_each_way": HOST_LINK_GBS, "median_of": reps}
+    res["block_ranges"] = {"what": "second half of each sequence's blocks, one call per sequence",
+                           "calls": n_seqs, "bytes_each_way": int(half_pages * pb),
+                           "out_us": round(med(b_out), 1), "in_us": round(med(b_in), 1),
+                           "out_GBps": round(half_pages * pb / med(b_out) / 1e3, 1),
+                           "in_GBps": round(half_pages * pb / med(b_in) / 1e3, 1)}
     res["swap_out_frac_of_link_peak"] = round(res["swap_out_GBps"] / HOST_LINK_GBS, 4)
     res["swap_in_frac_of_link_peak"] = round(res["swap_in_GBps"] / HOST_LINK_GBS, 4)
     return res

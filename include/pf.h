@@ -157,7 +157,10 @@ int pf_grow_seqs(pf_pool* pool, const uint64_t* seq_ids, const int32_t* new_lens
 int32_t pf_page_refcount(const pf_pool* pool, int32_t page);
 
 /* Swapping (PagedAttention blog, "Preemption and Swapping": a sequence's blocks
- * are evicted to CPU memory and copied back when it resumes).
+ * are evicted to CPU memory and copied back when it resumes; swapping works on
+ * blocks, so some blocks of a sequence may be on the GPU and others on the
+ * CPU).  Whole sequences (pf_swap_out, pf_swap_in) or a block range of one
+ * sequence (pf_swap_out_blocks, pf_swap_in_blocks).
  *
  * Bind a host backing store: host_ptr is caller-owned pinned memory
  * (hipHostMalloc / pin_memory), 16-byte aligned, of at least
@@ -170,8 +173,17 @@ int pf_swap_bind(pf_pool* pool, void* host_ptr, size_t bytes, int32_t num_slots)
 /* Free host slots (-1 for a NULL handle). */
 int32_t pf_swap_free_slots(const pf_pool* pool);
 
-/* *swapped = 1 if seq_id is swapped out, else 0.  Errors: PF_ERR_UNKNOWN_SEQ. */
+/* *swapped = 1 if any block of seq_id is on the host (swapped out), else 0.
+ * Errors: PF_ERR_UNKNOWN_SEQ. */
 int pf_seq_swapped(const pf_pool* pool, uint64_t seq_id, int32_t* swapped);
+
+/* Where each block of seq_id is: pages[b] = its device page, or -1 while it
+ * is on the host, and slots[b] = its host slot, or -1 while it is on the
+ * device, for b < *num_blocks = ceil(length / B).  pages and slots hold
+ * max_blocks entries.  Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID (NULL
+ * pointers, or more blocks than max_blocks: *num_blocks is still set). */
+int pf_seq_blocks(const pf_pool* pool, uint64_t seq_id, int32_t max_blocks, int32_t* pages, int32_t* slots,
+                  int32_t* num_blocks);
 
 /* Swap whole sequences out: each page of each sequence's table, in order, is
  * assigned a host slot and enqueued on the stream for copying device -> host;
@@ -179,7 +191,9 @@ int pf_seq_swapped(const pf_pool* pool, uint64_t seq_id, int32_t* swapped);
  * return to the free stack, last first, as pf_free_seq would push them; pages
  * still shared stay with their other holders).  The sequence keeps its length
  * and is "swapped": growing, forking or exporting it fails with
- * PF_ERR_SWAPPED until pf_swap_in; pf_free_seq releases its slots.
+ * PF_ERR_SWAPPED until every block is back (pf_swap_in, pf_swap_in_blocks);
+ * pf_free_seq releases its slots.  A sequence of length 0 has no block to
+ * move and stays resident.
  *   staging_host  caller-owned pinned memory, 8-byte aligned, of
  *                 staging_words int32 >= 2 * (pages of the sequences); receives
  *                 the (page, slot) pairs that the copy kernel reads when it
@@ -187,21 +201,57 @@ int pf_seq_swapped(const pf_pool* pool, uint64_t seq_id, int32_t* swapped);
  * The copy is enqueued before the call returns, so anything enqueued later on
  * the same stream (writes into the freed pages included) runs after it.
  * All or nothing over the batch.  Errors: PF_ERR_INVALID (a repeated id, a
- * small staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_SWAPPED (already out),
- * PF_ERR_OOM (not enough free slots), PF_ERR_UNBOUND (no device pool or no
- * swap space), PF_ERR_HIP. */
+ * small staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_SWAPPED (some block already
+ * out), PF_ERR_OOM (not enough free slots), PF_ERR_UNBOUND (no device pool or
+ * no swap space), PF_ERR_HIP. */
 int pf_swap_out(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
                 int64_t staging_words, void* hip_stream);
 
-/* Swap whole sequences back in: each host slot, in table order, gets a fresh
- * page from the free stack (pop order) and is enqueued for copying host ->
- * device; the slots return to their stack, last first.  Staging and ordering
- * as pf_swap_out, with (slot, page) pairs.  All or nothing.  Errors:
- * PF_ERR_INVALID (a repeated id, a sequence that is not swapped out, a small
- * staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_OOM (not enough free pages),
- * PF_ERR_UNBOUND, PF_ERR_HIP. */
+/* Swap sequences back in: every block of each that is on the host, in block
+ * order, gets a fresh page from the free stack (pop order) and is enqueued
+ * for copying host -> device; the slots return to their stack, last block
+ * first.  Staging and ordering as pf_swap_out, with (slot, page) pairs.  All
+ * or nothing.  Errors: PF_ERR_INVALID (a repeated id, a sequence with no
+ * block on the host, a small staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_OOM (not
+ * enough free pages), PF_ERR_UNBOUND, PF_ERR_HIP. */
 int pf_swap_in(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
                int64_t staging_words, void* hip_stream);
+
+/* Swap out blocks [first_block, first_block + num_blocks) of one sequence,
+ * every one of them on the device: as pf_swap_out for those blocks only (a
+ * slot per block in block order, (page, slot) pairs in staging_host of at
+ * least 2 * num_blocks words, the pages released last block first).  The
+ * sequence's other blocks stay where they are; it counts as swapped (no
+ * growth, fork or export) while any block is on the host.  All or nothing.
+ * Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID (num_blocks < 1, a range outside
+ * the table, a block in it already on the host, a small or misaligned
+ * staging), PF_ERR_OOM (not enough free slots), PF_ERR_UNBOUND, PF_ERR_HIP.
+ * Checked in the order UNBOUND, UNKNOWN_SEQ, INVALID, OOM. */
+int pf_swap_out_blocks(pf_pool* pool, uint64_t seq_id, int32_t first_block, int32_t num_blocks,
+                       int32_t* staging_host, int64_t staging_words, void* hip_stream);
+
+/* Swap in blocks [first_block, first_block + num_blocks) of one sequence,
+ * every one of them on the host (for instance fetching a swapped-out
+ * sequence's blocks back one at a time): fresh pages in block order, (slot,
+ * page) pairs, slots returned last block first.  When the last block on the
+ * host comes back, the sequence is resident again.  All or nothing.  Errors:
+ * as pf_swap_out_blocks, with PF_ERR_INVALID for a block in the range that is
+ * on the device and PF_ERR_OOM for too few free pages. */
+int pf_swap_in_blocks(pf_pool* pool, uint64_t seq_id, int32_t first_block, int32_t num_blocks,
+                      int32_t* staging_host, int64_t staging_words, void* hip_stream);
+
+/* Host halves of the swaps, with no launch: the state changes exactly as
+ * pf_swap_out (to_host != 0) / pf_swap_in, resp. pf_swap_out_blocks /
+ * pf_swap_in_blocks, would change it, and staging_host (any host memory)
+ * receives the (page, slot) / (slot, page) pairs, *pairs of them.  The caller
+ * must make those copies (a page-sized copy per pair between the bound pool
+ * and the bound host store) before the pages or slots are used again.  For
+ * callers that move pages themselves, and for tests.  Errors: as the calls,
+ * plus PF_ERR_INVALID for a NULL pairs. */
+int pf_swap_staging(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t to_host, int32_t* staging_host,
+                    int64_t staging_words, int32_t* pairs);
+int pf_swap_blocks_staging(pf_pool* pool, uint64_t seq_id, int32_t first_block, int32_t num_blocks, int32_t to_host,
+                           int32_t* staging_host, int64_t staging_words, int32_t* pairs);
 
 /* Release seq_id's hold on each of its pages and forget the sequence; pages no
  * other table holds go back on the free stack, last page first (so the

@@ -261,7 +261,9 @@ class AllocModel:
 
     def _move_out(self, seq_id, blocks):
         """Blocks (all on the device) to host slots taken in block order; the
-        pages are released last block first.  Returns the (page, slot) copies."""
+        pages are released last block first.  Returns the (page, slot) copies.
+        (A sequence of length 0 swapped out whole moves nothing and is listed
+        as swapped all the same.)"""
         pages, host = self._split(seq_id)
         pages, host = list(pages), dict(host)
         copies = []
@@ -425,7 +427,7 @@ class AllocModel:
             for p in dev:
                 holders[p] += 1
         for s, (pages, host) in self.offdev.items():
-            assert host, "listed as off the device with every block on it"
+            assert host or not pages, "listed as off the device with every block on it"
             assert set(host) == {b for b, p in enumerate(pages) if p is None}, "a block in neither place"
         assert holders == self.refs, "reference counts differ from the tables holding each page"
         live = {p for p in range(self.num_pages) if holders[p] > 0}

@@ -20,11 +20,14 @@
 // (pf_grow_seqs, which reports the copy for pf_copy_pages) or is refused
 // (pf_alloc_for_seq / pf_alloc_for_seqs, PF_ERR_SHARED).
 //
-// Swapping (PagedAttention blog, "Preemption and Swapping"): whole sequences
-// move to page-sized slots of a caller-owned pinned host store and back; the
-// state changes here, the copies are enqueued by pf_swap_out / pf_swap_in
-// (pf_kv.hip) in the same call.  A swapped sequence keeps its length and its
-// slots; it cannot grow, fork or be exported until it is swapped in.
+// Swapping (PagedAttention blog, "Preemption and Swapping"): blocks move to
+// page-sized slots of a caller-owned pinned host store and back -- whole
+// sequences, or a block range of one sequence, so that some of its blocks are
+// on the device and others on the host; the state changes here, the copies
+// are enqueued by pf_swap_out / pf_swap_in / pf_swap_out_blocks /
+// pf_swap_in_blocks (pf_kv.hip) in the same call.  A sequence with blocks on
+// the host keeps its length and its slots; it cannot grow, fork or be
+// exported until every block is back.
 #include <algorithm>
 #include <cstring>
 #include <limits>
@@ -273,11 +276,12 @@ int pf_free_seq(pf_pool* pool, uint64_t seq_id) {
   std::lock_guard<std::mutex> lk(pool->mu);
   auto it = pool->seqs.find(seq_id);
   if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
-  const std::vector<int32_t>& slots = it->second.slots;
-  for (size_t i = slots.size(); i-- > 0;) pool->slot_stack.push_back(slots[i]);
+  const std::vector<int32_t>& slots = it->second.slots;  // blocks on the host: slots back last first
+  for (size_t i = slots.size(); i-- > 0;)
+    if (slots[i] >= 0) pool->slot_stack.push_back(slots[i]);
   const std::vector<int32_t>& pages = it->second.pages;
   for (size_t i = pages.size(); i-- > 0;)
-    if (--pool->refs[(size_t)pages[i]] == 0) pool->stack.push_back(pages[i]);
+    if (pages[i] >= 0 && --pool->refs[(size_t)pages[i]] == 0) pool->stack.push_back(pages[i]);
   pool->seqs.erase(it);
   return PF_OK;
 }
@@ -415,6 +419,23 @@ int pf_seq_swapped(const pf_pool* pool, uint64_t seq_id, int32_t* swapped) {
   auto it = pool->seqs.find(seq_id);
   if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
   *swapped = it->second.swapped ? 1 : 0;
+  return PF_OK;
+}
+
+int pf_seq_blocks(const pf_pool* pool, uint64_t seq_id, int32_t max_blocks, int32_t* pages, int32_t* slots,
+                  int32_t* num_blocks) {
+  if (!pool || !num_blocks || max_blocks < 0 || (max_blocks > 0 && (!pages || !slots))) return PF_ERR_INVALID;
+  std::lock_guard<std::mutex> lk(pool->mu);
+  auto it = pool->seqs.find(seq_id);
+  if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+  const pf_seq_entry& e = it->second;
+  const int32_t nb = (int32_t)e.pages.size();
+  *num_blocks = nb;
+  if (nb > max_blocks) return PF_ERR_INVALID;
+  for (int32_t b = 0; b < nb; ++b) {
+    pages[b] = e.pages[(size_t)b];
+    slots[b] = e.slots.empty() ? -1 : e.slots[(size_t)b];
+  }
   return PF_OK;
 }
 
@@ -658,10 +679,57 @@ const char* pf_status_string(int status) {
 
 }  // extern "C"
 
-// Host half of swapping, under the pool lock: validate the batch, then move
-// the sequences' blocks between device pages and host slots and write the
-// copy list (pairs of (page, slot) for out, (slot, page) for in) into out.
-// Returns a status; *pairs receives the number of pairs written.
+// Swapping, under the pool lock.  Blocks move between device pages and host
+// slots: out, a slot per block taken in block order, then the pages released
+// last block first (a page another table holds stays with it); in, a page per
+// block popped in block order, then the slots returned last block first.
+// Each move writes its copy pairs ((page, slot) out, (slot, page) in) to out.
+
+// Move blocks [first, first + count) of e (all on the device) to the host.
+static void move_out(pf_pool* pool, pf_seq_entry& e, int32_t first, int32_t count, int32_t* out, int32_t* k) {
+  if (e.slots.empty()) e.slots.assign(e.pages.size(), -1);
+  for (int32_t b = first; b < first + count; ++b) {
+    const int32_t slot = pool->slot_stack.back();
+    pool->slot_stack.pop_back();
+    e.slots[(size_t)b] = slot;
+    out[2 * *k] = e.pages[(size_t)b];
+    out[2 * *k + 1] = slot;
+    ++*k;
+  }
+  for (int32_t b = first + count; b-- > first;) {
+    const int32_t page = e.pages[(size_t)b];
+    if (--pool->refs[(size_t)page] == 0) pool->stack.push_back(page);
+    e.pages[(size_t)b] = -1;
+  }
+  e.on_host += count;
+  e.swapped = true;
+  e.ver = ++pool->ver_clock;
+}
+
+// Move every block of e in [first, first + count) that is on the host back
+// to fresh pages.
+static void move_in(pf_pool* pool, pf_seq_entry& e, int32_t first, int32_t count, int32_t* out, int32_t* k) {
+  for (int32_t b = first; b < first + count; ++b) {
+    if (e.pages[(size_t)b] >= 0) continue;
+    const int32_t page = pop_page(pool);
+    out[2 * *k] = e.slots[(size_t)b];
+    out[2 * *k + 1] = page;
+    ++*k;
+    e.pages[(size_t)b] = page;
+  }
+  for (int32_t b = first + count; b-- > first;) {
+    if (e.slots[(size_t)b] < 0) continue;
+    pool->slot_stack.push_back(e.slots[(size_t)b]);
+    e.slots[(size_t)b] = -1;
+    --e.on_host;
+  }
+  if (e.on_host == 0) e.slots.clear();
+  e.swapped = e.on_host > 0;
+  e.ver = ++pool->ver_clock;
+}
+
+// Whole sequences, all or nothing: out needs every block on the device, in
+// brings back every block that is on the host (and needs one to be).
 int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host, int32_t* out,
                  int64_t out_words, int32_t* pairs) {
   return guarded([&]() -> int {
@@ -675,14 +743,13 @@ int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host
       if (seen[seq_ids[i]]++) return PF_ERR_INVALID;
     for (int32_t i = 0; i < n; ++i) {
       auto it = pool->seqs.find(seq_ids[i]);
+      if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
       if (to_host) {
-        if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
         if (it->second.swapped) return PF_ERR_SWAPPED;
         total += it->second.pages.size();
       } else {
-        if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
         if (!it->second.swapped) return PF_ERR_INVALID;
-        total += it->second.slots.size();
+        total += (size_t)it->second.on_host;
       }
     }
     if (total > (to_host ? pool->slot_stack.size() : pool->stack.size())) return PF_ERR_OOM;
@@ -690,37 +757,55 @@ int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host
     int32_t k = 0;
     for (int32_t i = 0; i < n; ++i) {
       pf_seq_entry& e = pool->seqs.find(seq_ids[i])->second;
+      const int32_t nb = (int32_t)e.pages.size();
       if (to_host) {
-        e.slots.clear();
-        for (int32_t page : e.pages) {
-          const int32_t slot = pool->slot_stack.back();
-          pool->slot_stack.pop_back();
-          e.slots.push_back(slot);
-          out[2 * k] = page;
-          out[2 * k + 1] = slot;
-          ++k;
-        }
-        for (size_t j = e.pages.size(); j-- > 0;)
-          if (--pool->refs[(size_t)e.pages[j]] == 0) pool->stack.push_back(e.pages[j]);
-        e.pages.clear();
-        e.ver = ++pool->ver_clock;
-        e.swapped = true;
+        move_out(pool, e, 0, nb, out, &k);
       } else {
-        e.pages.clear();
-        for (int32_t slot : e.slots) {
-          const int32_t page = pop_page(pool);
-          e.pages.push_back(page);
-          out[2 * k] = slot;
-          out[2 * k + 1] = page;
-          ++k;
-        }
-        for (size_t j = e.slots.size(); j-- > 0;) pool->slot_stack.push_back(e.slots[j]);
-        e.slots.clear();
-        e.ver = ++pool->ver_clock;
-        e.swapped = false;
+        move_in(pool, e, 0, nb, out, &k);
       }
     }
     *pairs = k;
     return PF_OK;
   });
 }
+
+int pf_swap_blocks_plan(pf_pool* pool, uint64_t seq_id, int32_t first, int32_t count, bool to_host, int32_t* out,
+                        int64_t out_words, int32_t* pairs) {
+  return guarded([&]() -> int {
+    *pairs = 0;
+    if (!pool || !out) return PF_ERR_INVALID;
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (!pool->dev || !pool->host) return PF_ERR_UNBOUND;
+    auto it = pool->seqs.find(seq_id);
+    if (it == pool->seqs.end()) return PF_ERR_UNKNOWN_SEQ;
+    pf_seq_entry& e = it->second;
+    const int64_t nb = (int64_t)e.pages.size();
+    if (count < 1 || first < 0 || (int64_t)first + count > nb) return PF_ERR_INVALID;
+    for (int32_t b = first; b < first + count; ++b)
+      if ((e.pages[(size_t)b] >= 0) != to_host) return PF_ERR_INVALID;  // wholly on the side it leaves
+    if ((size_t)count > (to_host ? pool->slot_stack.size() : pool->stack.size())) return PF_ERR_OOM;
+    if ((int64_t)count * 2 > out_words) return PF_ERR_INVALID;
+    int32_t k = 0;
+    if (to_host) move_out(pool, e, first, count, out, &k);
+    else move_in(pool, e, first, count, out, &k);
+    *pairs = k;
+    return PF_OK;
+  });
+}
+
+extern "C" {
+
+int pf_swap_staging(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t to_host, int32_t* staging_host,
+                    int64_t staging_words, int32_t* pairs) {
+  if (!pairs) return PF_ERR_INVALID;
+  return pf_swap_plan(pool, seq_ids, n, to_host != 0, staging_host, staging_words, pairs);
+}
+
+int pf_swap_blocks_staging(pf_pool* pool, uint64_t seq_id, int32_t first_block, int32_t num_blocks, int32_t to_host,
+                           int32_t* staging_host, int64_t staging_words, int32_t* pairs) {
+  if (!pairs) return PF_ERR_INVALID;
+  return pf_swap_blocks_plan(pool, seq_id, first_block, num_blocks, to_host != 0, staging_host, staging_words,
+                             pairs);
+}
+
+}  // extern "C"

@@ -11,10 +11,12 @@
 #include "pf.h"
 
 struct pf_seq_entry {
-  std::vector<int32_t> pages;  // block table: logical block i -> physical page
+  std::vector<int32_t> pages;  // block table: logical block i -> physical page, -1 while on the host
   int32_t len = 0;             // tokens held
-  bool swapped = false;        // swapped out: pages empty, slots hold the blocks
-  std::vector<int32_t> slots;  // host swap slots of logical blocks 0.. (swapped only)
+  int32_t on_host = 0;         // blocks swapped out to the host
+  bool swapped = false;        // on_host > 0, or a length-0 sequence swapped out whole: no growth,
+                               // fork or export until it is swapped in
+  std::vector<int32_t> slots;  // host slot of block i while it is on the host, else -1; empty if none is
   // Version of `pages`: set from the pool's clock whenever the table changes,
   // so equal versions mean an equal table (0: never held a page).
   uint64_t ver = 0;
@@ -96,3 +98,8 @@ void pf_export_forget(const pf_pool* pool);
 // written.  Same errors as the entry points.
 int pf_swap_plan(pf_pool* pool, const uint64_t* seq_ids, int32_t n, bool to_host, int32_t* out,
                  int64_t out_words, int32_t* pairs);
+
+// The same for blocks [first, first + count) of one sequence (pf_swap_out_blocks
+// / pf_swap_in_blocks).
+int pf_swap_blocks_plan(pf_pool* pool, uint64_t seq_id, int32_t first, int32_t count, bool to_host, int32_t* out,
+                        int64_t out_words, int32_t* pairs);

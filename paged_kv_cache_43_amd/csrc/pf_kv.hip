@@ -384,6 +384,19 @@ extern "C" int pf_copy_pages(const pf_pool* pool, const int32_t* pairs, int32_t 
   return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
 }
 
+// Enqueue the copies of `pairs` (page, slot) / (slot, page) pairs in staging_host.
+static int swap_launch(pf_pool* pool, int32_t* staging_host, int32_t pairs, bool to_host, void* hip_stream) {
+  const size_t page_bytes = pool->page_elems * pool->elem_bytes;
+  const int64_t chunks = (int64_t)(page_bytes / 16);
+  const int64_t total = chunks * pairs;
+  int blocks = 0;
+  pf::launch_grid(total, &blocks);
+  hipLaunchKernelGGL(pf::swap_copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream,
+                     static_cast<uint8_t*>(pool->dev), static_cast<uint8_t*>(pool->host), staging_host, chunks,
+                     total, pool->g.num_pages, pool->num_slots, to_host ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+}
+
 static int swap_call(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
                      int64_t staging_words, bool to_host, void* hip_stream) {
   if (!pool) return PF_ERR_INVALID;
@@ -393,14 +406,28 @@ static int swap_call(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t*
   int32_t pairs = 0;
   const int st = pf_swap_plan(pool, seq_ids, n, to_host, staging_host, staging_words, &pairs);
   if (st != PF_OK || pairs == 0) return st;
-  const int64_t chunks = (int64_t)(page_bytes / 16);
-  const int64_t total = chunks * pairs;
-  int blocks = 0;
-  pf::launch_grid(total, &blocks);
-  hipLaunchKernelGGL(pf::swap_copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream,
-                     static_cast<uint8_t*>(pool->dev), static_cast<uint8_t*>(pool->host), staging_host, chunks,
-                     total, pool->g.num_pages, pool->num_slots, to_host ? 1 : 0);
-  return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
+  return swap_launch(pool, staging_host, pairs, to_host, hip_stream);
+}
+
+static int swap_blocks_call(pf_pool* pool, uint64_t seq_id, int32_t first, int32_t count, int32_t* staging_host,
+                            int64_t staging_words, bool to_host, void* hip_stream) {
+  if (!pool) return PF_ERR_INVALID;
+  if (!staging_host || (reinterpret_cast<uintptr_t>(staging_host) & 7) != 0) return PF_ERR_INVALID;
+  if ((pool->page_elems * pool->elem_bytes) % 16 != 0) return PF_ERR_UNSUPPORTED;
+  int32_t pairs = 0;
+  const int st = pf_swap_blocks_plan(pool, seq_id, first, count, to_host, staging_host, staging_words, &pairs);
+  if (st != PF_OK || pairs == 0) return st;
+  return swap_launch(pool, staging_host, pairs, to_host, hip_stream);
+}
+
+extern "C" int pf_swap_out_blocks(pf_pool* pool, uint64_t seq_id, int32_t first_block, int32_t num_blocks,
+                                  int32_t* staging_host, int64_t staging_words, void* hip_stream) {
+  return swap_blocks_call(pool, seq_id, first_block, num_blocks, staging_host, staging_words, true, hip_stream);
+}
+
+extern "C" int pf_swap_in_blocks(pf_pool* pool, uint64_t seq_id, int32_t first_block, int32_t num_blocks,
+                                 int32_t* staging_host, int64_t staging_words, void* hip_stream) {
+  return swap_blocks_call(pool, seq_id, first_block, num_blocks, staging_host, staging_words, false, hip_stream);
 }
 
 extern "C" int pf_swap_out(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,

@@ -73,6 +73,11 @@ _SIGS = {
     "pf_seq_swapped": (_i32, [_vp, _u64, _pi32]),
     "pf_swap_out": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _vp, ctypes.c_int64, _vp]),
     "pf_swap_in": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _vp, ctypes.c_int64, _vp]),
+    "pf_swap_out_blocks": (_i32, [_vp, _u64, _i32, _i32, _vp, ctypes.c_int64, _vp]),
+    "pf_swap_in_blocks": (_i32, [_vp, _u64, _i32, _i32, _vp, ctypes.c_int64, _vp]),
+    "pf_seq_blocks": (_i32, [_vp, _u64, _i32, _pi32, _pi32, _pi32]),
+    "pf_swap_staging": (_i32, [_vp, ctypes.POINTER(_u64), _i32, _i32, _vp, ctypes.c_int64, _pi32]),
+    "pf_swap_blocks_staging": (_i32, [_vp, _u64, _i32, _i32, _i32, _vp, ctypes.c_int64, _pi32]),
     "pf_free_pages": (_i32, [_vp]),
     "pf_num_seqs": (_i32, [_vp]),
     "pf_seq_len": (_i32, [_vp, _u64, _pi32]),
@@ -329,6 +334,49 @@ def pf_swap_out(pool, seq_ids, staging, staging_words, stream=None):
 
 def pf_swap_in(pool, seq_ids, staging, staging_words, stream=None):
     return _swap(lib.pf_swap_in, pool, seq_ids, staging, staging_words, stream)
+
+
+def pf_swap_out_blocks(pool, seq_id, first_block, num_blocks, staging, staging_words, stream=None):
+    """``staging``: pinned int32 host tensor (or address) of staging_words words."""
+    return lib.pf_swap_out_blocks(pool, seq_id, first_block, num_blocks, _pinned(staging), staging_words,
+                                  _stream(stream))
+
+
+def pf_swap_in_blocks(pool, seq_id, first_block, num_blocks, staging, staging_words, stream=None):
+    return lib.pf_swap_in_blocks(pool, seq_id, first_block, num_blocks, _pinned(staging), staging_words,
+                                 _stream(stream))
+
+
+def pf_swap_staging(pool, seq_ids, to_host, staging_words=None):
+    """Host half of pf_swap_out / pf_swap_in.  Returns (status, pairs [k][2])."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.uint64)
+    words = 2 * 65536 if staging_words is None else staging_words
+    buf = np.zeros(max(words, 2), dtype=np.int32)
+    k = ctypes.c_int32(0)
+    st = lib.pf_swap_staging(pool, ids.ctypes.data_as(ctypes.POINTER(_u64)), len(ids), 1 if to_host else 0,
+                             buf.ctypes.data, words, ctypes.byref(k))
+    return st, buf[:2 * k.value].reshape(-1, 2).copy()
+
+
+def pf_swap_blocks_staging(pool, seq_id, first_block, num_blocks, to_host, staging_words=None):
+    """Host half of pf_swap_out_blocks / pf_swap_in_blocks.  Returns (status, pairs [k][2])."""
+    words = max(2 * num_blocks, 2) if staging_words is None else staging_words
+    buf = np.zeros(max(words, 2), dtype=np.int32)
+    k = ctypes.c_int32(0)
+    st = lib.pf_swap_blocks_staging(pool, seq_id, first_block, num_blocks, 1 if to_host else 0, buf.ctypes.data,
+                                    words, ctypes.byref(k))
+    return st, buf[:2 * k.value].reshape(-1, 2).copy()
+
+
+def pf_seq_blocks(pool, seq_id, max_blocks=4096):
+    """Returns (status, pages [nb], slots [nb]): -1 pages for blocks on the host,
+    -1 slots for blocks on the device."""
+    pages = np.zeros(max(max_blocks, 1), dtype=np.int32)
+    slots = np.zeros(max(max_blocks, 1), dtype=np.int32)
+    nb = ctypes.c_int32(0)
+    st = lib.pf_seq_blocks(pool, seq_id, max_blocks, pages.ctypes.data_as(_pi32), slots.ctypes.data_as(_pi32),
+                           ctypes.byref(nb))
+    return st, pages[:nb.value].copy(), slots[:nb.value].copy()
 
 
 def pf_copy_pages(pool, pairs, n, stream=None):
