@@ -42,3 +42,38 @@ def test_very_long_contexts(shape):
         print("  schedule", sched, "waves", pf.pf_attention_waves(kv.h, w.n, hq, mc), "split",
               pf.pf_attention_split_tokens(kv.h, w.n, hq, mc), "max err", err, flush=True)
     kv.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("lens", [[65536], [32768] + list(range(100, 740, 10))], ids=["one-64k", "65-seqs"])
+def test_head_dim_256_long_contexts(lens, dtype):
+    """Head dim 256, where a merge wave's 64 lanes cover one output row (one
+    piece stream per wave).  One 64k-token sequence of 4 heads: under both
+    schedules each row has many pieces and few rows exist, so every row gets
+    its own 8-wave workgroup.  65 sequences (one of 32k tokens) of 4 heads:
+    the fixed splits give 64 splits to the long rows and 260 rows in all, so
+    rows are merged 8 waves per row group; the balanced schedule's rows have
+    few pieces and take the one-wave merge.  16-bit and fp32 outputs, against
+    the oracle."""
+    from paged_kv_cache_43_amd import pf, runner
+    print("head dim 256", len(lens), "sequences", dtype, flush=True)
+    w = _custom(lens, 4, 4, 256, dtype, seed=256 + len(lens))
+    kv = runner.PagedKV(w)
+    q = runner.fill_workload(kv)
+    ref = gu.oracle_attention_contiguous(w, 0)
+    mc = int(max(lens))
+    for sched in (SCHED_BALANCED, SCHED_GRID):
+        pf.check(pf.pf_pool_set_option(kv.h, pf.PF_OPT_SCHEDULE, sched))
+        waves = pf.pf_attention_waves(kv.h, w.n, 4, mc)
+        split = pf.pf_attention_split_tokens(kv.h, w.n, 4, mc)
+        if sched == SCHED_GRID:
+            assert -(-mc // split) >= 16                  # the wide merge's condition
+        elif len(lens) == 1:
+            assert waves >= 16 * 4
+        for od in ("f32", dtype):
+            out = torch.empty((w.n, 4, 256), dtype=torch.float32 if od == "f32" else torch.int16, device="cuda")
+            kv.attention(0, q[0], out, mc, out_dtype=od)
+            torch.cuda.synchronize()
+            err = gu.assert_close(gu.out_to_f64(out, od), ref, od, "schedule %d out %s" % (sched, od))
+            print("  schedule", sched, "waves", waves, "split", split, "out", od, "max err", err, flush=True)
+    kv.close()
