@@ -104,23 +104,35 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* pool, const in
 // CPU memory and back): pair j moves one whole page between the device pool
 // and a page-sized slot of the pinned host store -- (page, slot) pairs when
 // to_host, (slot, page) otherwise.  The kernel reads and writes host memory
-// directly over the host link, 16 bytes per thread; the 64 lanes of a wave
-// fall in one pair, so its pair is one shared read.  Out-of-range ids copy
-// nothing.
+// directly over the host link.  Work unit: one 16 KiB span of one page per
+// workgroup, the span's pair read once, then kSwapPer independent 16-byte
+// loads per thread before any store.  (One chunk per thread, pair read and
+// data read back to back, cost about 50 us more per host-to-device launch on
+// MI355X at any size: two dependent host reads per wave.)  Units beyond the
+// grid are taken grid-stride.  Out-of-range ids copy nothing.
+constexpr int kSwapPer = 4;
+constexpr int kSwapSpan = 256 * kSwapPer;  // 16-byte chunks per unit
+
 __global__ __launch_bounds__(256) void swap_copy_kernel(uint8_t* pool, uint8_t* host, const int32_t* pairs,
-                                                        int64_t chunks, int64_t total, int32_t num_pages,
-                                                        int32_t num_slots, int32_t to_host) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t j = i / chunks;
-    const int64_t c = i - j * chunks;
+                                                        int64_t chunks, int64_t spans, int64_t units,
+                                                        int32_t num_pages, int32_t num_slots, int32_t to_host) {
+  for (int64_t w = blockIdx.x; w < units; w += gridDim.x) {
+    const int64_t j = w / spans;
+    const int64_t c0 = (w - j * spans) * kSwapSpan + threadIdx.x;
     const int32_t a = pairs[2 * j], b = pairs[2 * j + 1];
     const int32_t page = to_host ? a : b, slot = to_host ? b : a;
     if (page < 0 || page >= num_pages || slot < 0 || slot >= num_slots) continue;
-    uint4* dp = reinterpret_cast<uint4*>(pool + (int64_t)page * chunks * 16) + c;
-    uint4* hp = reinterpret_cast<uint4*>(host + (int64_t)slot * chunks * 16) + c;
-    if (to_host) *hp = *dp;
-    else *dp = *hp;
+    uint4* dp = reinterpret_cast<uint4*>(pool + (int64_t)page * chunks * 16);
+    uint4* hp = reinterpret_cast<uint4*>(host + (int64_t)slot * chunks * 16);
+    const uint4* src = to_host ? dp : hp;
+    uint4* dst = to_host ? hp : dp;
+    uint4 r[kSwapPer];
+#pragma unroll
+    for (int u = 0; u < kSwapPer; ++u)
+      if (c0 + 256 * u < chunks) r[u] = src[c0 + 256 * u];
+#pragma unroll
+    for (int u = 0; u < kSwapPer; ++u)
+      if (c0 + 256 * u < chunks) dst[c0 + 256 * u] = r[u];
   }
 }
 
@@ -388,12 +400,12 @@ extern "C" int pf_copy_pages(const pf_pool* pool, const int32_t* pairs, int32_t 
 static int swap_launch(pf_pool* pool, int32_t* staging_host, int32_t pairs, bool to_host, void* hip_stream) {
   const size_t page_bytes = pool->page_elems * pool->elem_bytes;
   const int64_t chunks = (int64_t)(page_bytes / 16);
-  const int64_t total = chunks * pairs;
-  int blocks = 0;
-  pf::launch_grid(total, &blocks);
-  hipLaunchKernelGGL(pf::swap_copy_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)hip_stream,
+  const int64_t spans = (chunks + pf::kSwapSpan - 1) / pf::kSwapSpan;
+  const int64_t units = spans * pairs;
+  const int64_t blocks = units < (int64_t(1) << 20) ? units : (int64_t(1) << 20);  // grid-stride beyond
+  hipLaunchKernelGGL(pf::swap_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream,
                      static_cast<uint8_t*>(pool->dev), static_cast<uint8_t*>(pool->host), staging_host, chunks,
-                     total, pool->g.num_pages, pool->num_slots, to_host ? 1 : 0);
+                     spans, units, pool->g.num_pages, pool->num_slots, to_host ? 1 : 0);
   return hipGetLastError() == hipSuccess ? PF_OK : PF_ERR_HIP;
 }
 
