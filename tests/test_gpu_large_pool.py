@@ -1,7 +1,8 @@
 """GPU: a pool larger than 4 GiB (more than 2^31 elements) whose sequences all
 live in pages that start past the 2^31-element mark.  Scatter, gather,
-attention (vector and matrix-core kernels, both layers) and page copies must
-address it with 64-bit offsets: results against the oracle as everywhere else."""
+attention (vector and matrix-core kernels, both layers), page copies and swap
+copies must address it with 64-bit offsets: results against the oracle as
+everywhere else, copies bit for bit."""
 import numpy as np
 import pytest
 
@@ -67,4 +68,30 @@ def test_pool_beyond_4gib(hq):
     torch.cuda.synchronize()
     assert torch.equal(kv.pool[dst * PAGE_ELEMS:(dst + 1) * PAGE_ELEMS],
                        kv.pool[src * PAGE_ELEMS:(src + 1) * PAGE_ELEMS])
+    # swap sequence 0 out to pinned host slots; a new sequence takes the pages
+    # it gave back, so it comes back into other pages, still past the mark
+    old = [int(p) for p in model.table(0)]
+    nb0 = len(old)
+    page = lambda p: kv.pool[p * PAGE_ELEMS:(p + 1) * PAGE_ELEMS]
+    before = [page(p).cpu() for p in old]
+    host = torch.zeros(nb0 * PAGE_ELEMS, dtype=torch.int16).pin_memory()
+    pf.check(pf.pf_swap_bind(kv.h, host, nb0 * PAGE_ELEMS * 2, nb0))
+    staging = torch.zeros(2 * nb0, dtype=torch.int32).pin_memory()
+    pf.check(pf.pf_swap_out(kv.h, [0], staging, 2 * nb0))
+    torch.cuda.synchronize()
+    pairs_out = staging.view(nb0, 2).tolist()
+    assert [a for a, _ in pairs_out] == old
+    for b, (_, slot) in enumerate(pairs_out):
+        assert torch.equal(host[slot * PAGE_ELEMS:(slot + 1) * PAGE_ELEMS], before[b]), b
+    st, taken = pf.pf_alloc_for_seq(kv.h, 1000, 16 * nb0)
+    assert st == pf.PF_OK and taken == nb0
+    pf.check(pf.pf_swap_in(kv.h, [0], staging, 2 * nb0))
+    torch.cuda.synchronize()
+    st, bt0, lens0 = pf.pf_block_tables(kv.h, [0], kv.max_blocks)
+    assert st == pf.PF_OK and lens0[0] == int(w.ctx[0])
+    new = [int(p) for p in bt0[0, :nb0]]
+    assert not set(new) & set(old) and min(new) * PAGE_ELEMS >= (1 << 31)
+    for b, p in enumerate(new):
+        assert torch.equal(page(p).cpu(), before[b]), b
+    assert pf.pf_free_seq(kv.h, 1000) == pf.PF_OK
     kv.close()
