@@ -108,10 +108,16 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint8_t* pool, const in
 // workgroup, the span's pair read once, then kSwapPer independent 16-byte
 // loads per thread before any store.  (One chunk per thread, pair read and
 // data read back to back, cost about 50 us more per host-to-device launch on
-// MI355X at any size: two dependent host reads per wave.)  Units beyond the
-// grid are taken grid-stride.  Out-of-range ids copy nothing.
+// MI355X at any size: two dependent host reads per wave.)  The grid holds at
+// most kSwapGrid workgroups (two per CU), which take the units grid-stride:
+// with every unit's workgroup resident at once, a host-to-device call of
+// 12-20 MB put all its host reads in flight together and ran 11-18 % slower
+// than the other direction; capped, host to device runs at the DMA engine's
+// rate (57 GB/s on MI355X) and device to host within a few percent of it.
+// Out-of-range ids copy nothing.
 constexpr int kSwapPer = 4;
 constexpr int kSwapSpan = 256 * kSwapPer;  // 16-byte chunks per unit
+constexpr int kSwapGrid = 512;
 
 __global__ __launch_bounds__(256) void swap_copy_kernel(uint8_t* pool, uint8_t* host, const int32_t* pairs,
                                                         int64_t chunks, int64_t spans, int64_t units,
@@ -402,7 +408,7 @@ static int swap_launch(pf_pool* pool, int32_t* staging_host, int32_t pairs, bool
   const int64_t chunks = (int64_t)(page_bytes / 16);
   const int64_t spans = (chunks + pf::kSwapSpan - 1) / pf::kSwapSpan;
   const int64_t units = spans * pairs;
-  const int64_t blocks = units < (int64_t(1) << 20) ? units : (int64_t(1) << 20);  // grid-stride beyond
+  const int64_t blocks = units < pf::kSwapGrid ? units : pf::kSwapGrid;
   hipLaunchKernelGGL(pf::swap_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)hip_stream,
                      static_cast<uint8_t*>(pool->dev), static_cast<uint8_t*>(pool->host), staging_host, chunks,
                      spans, units, pool->g.num_pages, pool->num_slots, to_host ? 1 : 0);
