@@ -194,6 +194,45 @@ def test_edge_lengths_and_empty(sched):
     kv.close()
 
 
+@pytest.mark.parametrize("mfma", [0, 1])
+@pytest.mark.parametrize("sched", [0, SCHED_GRID, SCHED_BALANCED])
+def test_lengths_clamped_to_bound(sched, mfma):
+    """Device lengths outside [0, max_context_len] are clamped into it: a
+    negative length attends to nothing (zeros), one above the bound attends to
+    the first max_context_len tokens.  Schedule 0 with a bound of at most 256
+    tokens is the whole-item path."""
+    from paged_kv_cache_43_amd import pf
+    print("clamped lengths", sched, mfma, flush=True)
+    w = _custom([100, 300, 50, 600, 37], hq=8, hkv=2, d=64, dtype="bf16", seed=21)
+    r = _r()
+    kv = r.PagedKV(w)
+    q = r.fill_workload(kv)
+    pf.check(pf.pf_pool_set_option(kv.h, pf.PF_OPT_GQA_MFMA, mfma))
+    pf.check(pf.pf_pool_set_option(kv.h, pf.PF_OPT_SCHEDULE, sched))
+    bound = 250
+    dev = [100, 900, -7, 600, 37]
+    kv.ctx.copy_(torch.tensor(dev, dtype=torch.int32))
+    out = torch.full((w.n, w.hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    kv.attention(0, q[0], out, bound, out_dtype="f32")
+    torch.cuda.synchronize()
+    got = gu.out_to_f64(out, "f32")
+    ks, vs, qb = w.values()
+    qd = oa.decode_bits(qb[0], w.dtype)
+    g = w.hq // w.hkv
+    for s, n in enumerate(dev):
+        eff = min(max(n, 0), bound)
+        if eff == 0:
+            assert np.all(got[s] == 0), s
+            continue
+        for hk in range(w.hkv):
+            K = oa.decode_bits(np.ascontiguousarray(ks[s][0][:eff, hk, :]), w.dtype)
+            V = oa.decode_bits(np.ascontiguousarray(vs[s][0][:eff, hk, :]), w.dtype)
+            for h in range(hk * g, (hk + 1) * g):
+                ref = oa.attention(qd[s, h], K, V, oa.default_scale(w.d))
+                assert np.max(np.abs(got[s, h] - ref)) <= gu.ATOL, (s, h)
+    kv.close()
+
+
 @pytest.mark.parametrize("split", [16, 32, 64, 128, 512, 1024])
 def test_split_invariance(split):
     print("split", split, flush=True)
