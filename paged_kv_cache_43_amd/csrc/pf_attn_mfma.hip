@@ -411,8 +411,9 @@ __global__ __launch_bounds__(kSchedThreads) void attn_mfma_balanced(AttnArgs a) 
 
 bool mfma_supports(int head_dim) { return head_dim == 64 || head_dim == 128; }
 
-// One page per prefetch unit (two pages in flight per wave): measured faster
-// than two-page units, which cost a wave of occupancy.
+// One page per prefetch unit (two pages in flight per wave): measured at least
+// as fast as two- or three-page units and as a ring of three one-page tiles on
+// MI355X, all at the same two waves per SIMD.
 template <class T, int D, bool OUT_F32, bool CONTIG>
 static void launch_d(const AttnArgs& a, bool balanced, hipStream_t st) {
   if (balanced)
