@@ -193,7 +193,7 @@ int pf_seq_blocks(const pf_pool* pool, uint64_t seq_id, int32_t max_blocks, int3
  * and is "swapped": growing, forking or exporting it fails with
  * PF_ERR_SWAPPED until every block is back (pf_swap_in, pf_swap_in_blocks);
  * pf_free_seq releases its slots.  A sequence of length 0 has no block to
- * move and stays resident.
+ * move: it is marked swapped all the same, with no copy, until pf_swap_in.
  *   staging_host  caller-owned pinned memory, 8-byte aligned, of
  *                 staging_words int32 >= 2 * (pages of the sequences); receives
  *                 the (page, slot) pairs that the copy kernel reads when it
@@ -211,9 +211,10 @@ int pf_swap_out(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* stag
  * order, gets a fresh page from the free stack (pop order) and is enqueued
  * for copying host -> device; the slots return to their stack, last block
  * first.  Staging and ordering as pf_swap_out, with (slot, page) pairs.  All
- * or nothing.  Errors: PF_ERR_INVALID (a repeated id, a sequence with no
- * block on the host, a small staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_OOM (not
- * enough free pages), PF_ERR_UNBOUND, PF_ERR_HIP. */
+ * or nothing; a swapped sequence of length 0 comes back with no copy.
+ * Errors: PF_ERR_INVALID (a repeated id, a sequence that is not swapped, a
+ * small staging), PF_ERR_UNKNOWN_SEQ, PF_ERR_OOM (not enough free pages),
+ * PF_ERR_UNBOUND, PF_ERR_HIP. */
 int pf_swap_in(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* staging_host,
                int64_t staging_words, void* hip_stream);
 
@@ -226,7 +227,8 @@ int pf_swap_in(pf_pool* pool, const uint64_t* seq_ids, int32_t n, int32_t* stagi
  * Errors: PF_ERR_UNKNOWN_SEQ, PF_ERR_INVALID (num_blocks < 1, a range outside
  * the table, a block in it already on the host, a small or misaligned
  * staging), PF_ERR_OOM (not enough free slots), PF_ERR_UNBOUND, PF_ERR_HIP.
- * Checked in the order UNBOUND, UNKNOWN_SEQ, INVALID, OOM. */
+ * A null or misaligned staging is refused first (PF_ERR_INVALID); then
+ * checked in the order UNBOUND, UNKNOWN_SEQ, INVALID, OOM. */
 int pf_swap_out_blocks(pf_pool* pool, uint64_t seq_id, int32_t first_block, int32_t num_blocks,
                        int32_t* staging_host, int64_t staging_words, void* hip_stream);
 
