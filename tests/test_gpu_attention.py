@@ -328,6 +328,25 @@ def test_block_sizes(block, dtype, hq, hkv, d, out_dtype):
     assert np.array_equal(res["ordered"], res["shuffled"])
 
 
+@pytest.mark.parametrize("name", ["13b", "gqa"])
+def test_block_sizes_full_size(name):
+    """The page-size sweep's workloads at full size (the same lengths and
+    values at 8, 32 and 64 tokens per page, shuffled frames): every output
+    against the oracle, 16-bit and fp32 output."""
+    print("block sizes full", name, flush=True)
+    ref = None
+    for block in (8, 32, 64):
+        w = inputs.Workload(name, frames="shuffled", block=block)
+        if ref is None:
+            ref = gu.oracle_attention_contiguous(w, 0)
+        got, kv, q = _run(w)
+        err = gu.assert_close(got, ref, w.dtype, "%s block %d" % (name, block))
+        got32 = _run(w, out_dtype="f32", kv=kv, q=q)
+        err32 = gu.assert_close(got32, ref, "f32", "%s block %d f32 out" % (name, block))
+        print("  block", block, "max err", err, "f32 out", err32, flush=True)
+        kv.close()
+
+
 @pytest.mark.parametrize("block,drops", [(8, {0: [1], 1: [2], 2: [4]}), (32, {0: [0], 1: [1]}),
                                          (16, {0: [1], 1: [2], 2: [0]})])
 def test_invalid_entries_grouped_heads(block, drops):
