@@ -91,7 +91,7 @@ def test_schedules_agree(name):
     kv.close()
 
 
-@pytest.mark.parametrize("name", ["13b", "gqa", "13b_32k", "gqa_32k"])
+@pytest.mark.parametrize("name", ["13b", "gqa", "13b_32k", "gqa_32k", "gqa_1m"])
 def test_attention_parity_full_size(name):
     """The bench's configurations at full size, in the launch configuration it
     times; every output against the oracle on the generated K/V, and sampled
