@@ -424,7 +424,10 @@ def pin_swap_round_trip(o):
 
 def pin_swap_rules(o):
     """All or nothing on slots and on device pages; a swapped sequence cannot
-    grow, fork or swap out again; freeing it returns its slots."""
+    grow, fork or swap out again; freeing it returns its slots.  A sequence of
+    length 0 has nothing to copy but is swapped out all the same: it waits for
+    its swap-in like any other (the blog resumes a preempted sequence by
+    swapping it back in; the empty case is this build's reading)."""
     am = o.alloc_model
     m = am.AllocModel(8, 16)
     m.set_swap_space(4)
@@ -442,6 +445,16 @@ def pin_swap_rules(o):
     assert m.swap_in([0]) == (am.OOM, []) and 0 in m.swapped and len(m.slot_stack) == 1
     m.check_invariants()
     assert m.free(0) == am.OK and len(m.slot_stack) == 4 and 0 not in m.lengths
+    m.check_invariants()
+    assert m.alloc(3, 0) == (am.OK, 0)
+    assert m.swap_out([3]) == (am.OK, []) and 3 in m.swapped and len(m.slot_stack) == 4
+    assert m.alloc(3, 1) == (am.SWAPPED, 0)
+    try:
+        m.block_tables([3], 4)
+        raise AssertionError("a swapped-out sequence has no device table")
+    except ValueError:
+        pass
+    assert m.swap_in([3]) == (am.OK, []) and 3 not in m.swapped and m.alloc(3, 1) == (am.OK, 1)
     m.check_invariants()
 
 

@@ -261,6 +261,17 @@ class _BlockOutPartialOnOomModel(oracle.alloc_model.AllocModel):
         return st, copies
 
 
+class _EmptySwapStaysResidentModel(oracle.alloc_model.AllocModel):
+    def swap_out(self, seq_ids):
+        st, copies = super().swap_out(seq_ids)
+        if st == oracle.alloc_model.OK:
+            for s in seq_ids:
+                if s in self.offdev and not self.offdev[s][0]:
+                    del self.offdev[s]
+                    self.tables[s] = []                     # nothing to move: left resident
+        return st, copies
+
+
 MUTANTS = {
     "attention_without_scale": (oracle.attention, "attention", _no_scale),
     "attention_wrong_sign": (oracle.attention, "attention", _wrong_sign),
@@ -292,6 +303,7 @@ MUTANTS = {
     "block_swap_range_off_by_one": (oracle.alloc_model, "AllocModel", _BlockRangeOffByOneModel),
     "whole_swap_in_refuses_partial": (oracle.alloc_model, "AllocModel", _WholeSwapInWholeOnlyModel),
     "block_swap_out_partial_on_oom": (oracle.alloc_model, "AllocModel", _BlockOutPartialOnOomModel),
+    "empty_swap_stays_resident": (oracle.alloc_model, "AllocModel", _EmptySwapStaysResidentModel),
 }
 
 
