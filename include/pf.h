@@ -401,6 +401,8 @@ size_t pf_attention_workspace_bytes(const pf_pool* pool, int32_t n, int32_t num_
  * the lengths, so results depend only on logical positions (the same bits for
  * any physical page order).  A length of 0 gives a zero output.  A table entry
  * that is not a valid page contributes nothing (no access outside the pool).
+ * Pools of 8-, 32- or 64-token pages and fp32 pools at head dim 256 (walked
+ * in 8-token units) always use the balanced schedule and take n <= 2048.
  * Errors: PF_ERR_INVALID, PF_ERR_UNBOUND, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED,
  * PF_ERR_HIP. */
 int pf_paged_decode_attention(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
@@ -443,8 +445,9 @@ int pf_paged_decode_attention_noalloc(const pf_pool* pool, int32_t layer, const 
  * contribute nothing (as for any invalid entry).
  *   k_new, v_new  device [n][H][D], pool dtype, 16-byte aligned.
  * Other arguments as pf_paged_decode_attention.  Built for 16-token pages
- * (PF_ERR_UNSUPPORTED otherwise) and head dims whose rows are a multiple of
- * 16 bytes.  Errors: as pf_paged_decode_attention. */
+ * walked in 16-token units and head dims whose rows are a multiple of 16 bytes
+ * (PF_ERR_UNSUPPORTED otherwise, also for fp32 pools at head dim 256).
+ * Errors: as pf_paged_decode_attention. */
 int pf_paged_decode_attention_append(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
                                      const void* k_new, const void* v_new, const int32_t* bt_dev,
                                      int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
@@ -470,7 +473,8 @@ int pf_paged_decode_attention_append(const pf_pool* pool, int32_t layer, const v
  *   q, ctx_dev, n, max_context_len (<= max_len), scale, out, out_dtype,
  *   workspace (sized by pf_attention_workspace_bytes): as
  *            pf_paged_decode_attention.
- * Errors: PF_ERR_INVALID, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED, PF_ERR_HIP. */
+ * Errors: PF_ERR_INVALID, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED (also for fp32
+ * at head dim 256), PF_ERR_HIP. */
 int pf_contiguous_decode_attention(const pf_pool* pool, const void* q, int32_t num_q_heads, const void* k,
                                    const void* v, int64_t seq_stride, int64_t token_stride, int64_t head_stride,
                                    int32_t max_len, const int32_t* ctx_dev, int32_t n, int32_t max_context_len,
@@ -485,7 +489,8 @@ typedef enum {
   PF_OPT_SCHEDULE = 2,     /* 0 (default): one split per (sequence, head) when max_context_len <= 256
                               (16-token pages, no split-tokens option set: no merge launch), else
                               balanced if n <= 2048, else fixed splits; 1: fixed splits;
-                              2: balanced (n <= 2048) */
+                              2: balanced (n <= 2048).  Pools of other page sizes and fp32 pools
+                              at head dim 256 are always balanced. */
   PF_OPT_WAVES_PER_CU = 3, /* balanced schedule: waves launched per compute unit; 0 (default) = 8,
                               or the kernel's resident capacity per CU if that is lower */
   PF_OPT_EXPORT_DELTA = 4  /* 0 (default): pf_export_tables / pf_decode_prepare upload the whole table;

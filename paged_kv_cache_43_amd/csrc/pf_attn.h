@@ -56,11 +56,11 @@ struct BlockAddr {
   bool ok;
 };
 
-// p is the unit index inside the sequence (units of BlockUnits<BS>::UT
+// p is the unit index inside the sequence (units of BlockUnits<BS, UTO>::UT
 // tokens); page is the table entry of the page holding it.
-template <bool CONTIG, int D, int ES, int BS = kBlock>
+template <bool CONTIG, int D, int ES, int BS = kBlock, int UTO = 0>
 __device__ inline BlockAddr block_addr(const AttnArgs& a, int page, int s, int p, int hk) {
-  using BU = BlockUnits<BS>;
+  using BU = BlockUnits<BS, UTO>;
   if constexpr (CONTIG) {
     const int64_t off = ((int64_t)s * a.c_seq + (int64_t)p * BU::UT * a.c_tok + (int64_t)hk * a.c_head) * ES;
     return {static_cast<const uint8_t*>(a.kc) + off, static_cast<const uint8_t*>(a.vc) + off, a.c_tok * ES, true};

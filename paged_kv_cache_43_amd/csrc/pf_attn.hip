@@ -87,12 +87,12 @@ __device__ inline void zero_empty_rows(const AttnArgs& a, const SchedLds& L, int
 
 // Per-wave state of the vector kernel: the current piece's online softmax.
 // CONTIG: blocks come from a contiguous cache instead of pool pages.  BS: the
-// pool's tokens per page.
-template <class T, int D, bool OUT_F32, bool CONTIG, int BS = kBlock>
+// pool's tokens per page.  UTO: unit size override (BlockUnits).
+template <class T, int D, bool OUT_F32, bool CONTIG, int BS = kBlock, int UTO = 0>
 struct ValuWave {
-  static constexpr int UT = BlockUnits<BS>::UT;  // tokens per unit of the walk
-  static constexpr int kPPU = 1;                   // pages per unit
-  static constexpr int kUPP = BlockUnits<BS>::R;   // units per page
+  static constexpr int UT = BlockUnits<BS, UTO>::UT;  // tokens per unit of the walk
+  static constexpr int kPPU = 1;                        // pages per unit
+  static constexpr int kUPP = BlockUnits<BS, UTO>::R;   // units per page
   using S = ValuShape<T, D, UT>;
   struct Tile {
     Raw<S::NW> k[S::ROWS], v[S::ROWS];
@@ -143,7 +143,7 @@ struct ValuWave {
   // query head h; false if the table entry is not a valid page (page 0 is
   // read instead, in bounds).
   __device__ inline bool load(int page, int s, int p, int h, Tile& t) const {
-    const BlockAddr b = block_addr<CONTIG, D, S::ES, BS>(a, page, s, p, h / a.group);
+    const BlockAddr b = block_addr<CONTIG, D, S::ES, BS, UTO>(a, page, s, p, h / a.group);
     const int64_t lo = (int64_t)tq * b.tok + dc * S::VEC * S::ES;
 #pragma unroll
     for (int r = 0; r < S::ROWS; ++r) t.k[r] = load_raw<S::NW>(b.k + lo + r * S::TPI * b.tok);
@@ -199,9 +199,11 @@ struct ValuWave {
   // token), in pool page `page` (ok: a valid page).  With a fused append the
   // newest token's K/V come from the input instead of the pool, patched into
   // the tile, and the first query head of each kv head group writes them into
-  // the page (16-token pages only); other waves that read the slot meanwhile
+  // the page (16-token pages walked in 16-token units only: the append entry
+  // point refuses every other walk); other waves that read the slot meanwhile
   // discard what they read.
   __device__ inline void patch_last(Tile& u, int nvalid, int s, int h, int page, bool ok) {
+    if constexpr (kUPP != 1 || BS != kBlock) return;
     if (a.k_new == nullptr || !ok) return;
     const int tn = nvalid - 1;
     const int hk = h / a.group;
@@ -291,9 +293,9 @@ __global__ __launch_bounds__(kWave) void attn_valu_grid(AttnArgs a) {
 
 // Balanced schedule (pf_sched.h): four waves per workgroup, items are query
 // heads.
-template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock>
+template <class T, int D, int U, bool OUT_F32, bool CONTIG, int BS = kBlock, int UTO = 0>
 __global__ __launch_bounds__(kSchedThreads) void attn_valu_balanced(AttnArgs a) {
-  using Wv = ValuWave<T, D, OUT_F32, CONTIG, BS>;
+  using Wv = ValuWave<T, D, OUT_F32, CONTIG, BS, UTO>;
   __shared__ SchedLds L;
   sched_build<Wv::UT>(a, L);
   zero_empty_rows<T, OUT_F32>(a, L, D);
@@ -582,6 +584,27 @@ static int launch_valu_bs(const AttnArgs& a, int D, int bs, hipStream_t st) {
   return PF_ERR_UNSUPPORTED;
 }
 
+// fp32 K/V at head dim 256: 16-token pages walked in 8-token units (a 16-token
+// unit is 128 VGPRs of K/V per lane, too many for two in flight); balanced
+// schedule, paged pool.
+constexpr int kHalfUnit = 8;
+
+static bool half_units(const pf_geometry& g) {
+  return g.dtype == PF_F32 && g.head_dim == 256 && g.block_size == kBlock;
+}
+
+template <bool OUT_F32>
+static void launch_valu_half(const AttnArgs& a, hipStream_t st) {
+  constexpr int U = ValuUnit<ElF32, 256, kHalfUnit>::U;
+  hipLaunchKernelGGL((attn_valu_balanced<ElF32, 256, U, OUT_F32, false, kBlock, kHalfUnit>),
+                     dim3(a.waves / (kSchedThreads / kWave)), dim3(kSchedThreads), 0, st, a);
+}
+
+static const void* valu_half_ptr() {
+  constexpr int U = ValuUnit<ElF32, 256, kHalfUnit>::U;
+  return reinterpret_cast<const void*>(&attn_valu_balanced<ElF32, 256, U, false, false, kBlock, kHalfUnit>);
+}
+
 // Block sizes other than 16 are built for 16-bit elements at head dim 64 or
 // 128, balanced schedule, paged pool.
 static bool block_size_supported(int bs, int dtype, int D) {
@@ -700,9 +723,9 @@ static void launch_merge(const AttnArgs& a, int D, bool balanced, int items_per_
 }
 
 static bool valu_supports(int dtype, int D) {
+  (void)dtype;
   switch (D) {
-    case 16: case 32: case 64: case 128: return true;
-    case 256: return dtype != PF_F32;
+    case 16: case 32: case 64: case 128: case 256: return true;  // fp32 at 256: half units
     default: return false;
   }
 }
@@ -801,13 +824,15 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
   p.items_per_seq = p.mfma ? g.num_kv_heads : num_q_heads;
   p.rows_per_item = p.mfma ? num_q_heads / g.num_kv_heads : 1;
   const int sched = pool->schedule;
-  p.balanced = sched == 2 || (sched == 0 && n <= kMaxSeqsBalanced) || g.block_size != kBlock;
+  const bool half = half_units(g);
+  p.balanced = sched == 2 || (sched == 0 && n <= kMaxSeqsBalanced) || g.block_size != kBlock || half;
   if (n > kMaxSeqsBalanced) p.balanced = false;
   // short contexts: every (sequence, head) whole in one wave, nothing to merge
-  const bool whole = sched == 0 && g.block_size == kBlock && pool->split_tokens == 0 &&
+  const bool whole = sched == 0 && g.block_size == kBlock && !half && pool->split_tokens == 0 &&
                      max_ctx <= kWholeItemTokens;
   if (whole) p.balanced = false;
-  const int ut = g.block_size < kBlock ? g.block_size : kBlock;  // tokens per unit of the walk
+  // tokens per unit of the walk
+  const int ut = half ? kHalfUnit : (g.block_size < kBlock ? g.block_size : kBlock);
   if (p.balanced) {
     // Waves: 8 per CU (two per SIMD), or fewer if the kernel's occupancy is
     // lower, and no more than one wave per 4 pages of the longest possible
@@ -817,6 +842,7 @@ Plan make_plan(const pf_pool* pool, int32_t n, int32_t num_q_heads, int32_t max_
     int per_cu = pool->waves_per_cu;
     if (per_cu <= 0) {
       const void* k = p.mfma ? mfma_balanced_kernel(g.dtype, g.head_dim)
+                      : half ? valu_half_ptr()
                       : g.dtype == PF_F32 ? valu_ptr_dtype<ElF32>(g.head_dim)
                       : (g.dtype == PF_F16 ? valu_ptr_dtype<ElF16>(g.head_dim) : valu_ptr_dtype<ElBF16>(g.head_dim));
       const int occ = occupancy_waves(k, 0);
@@ -895,6 +921,8 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   if (!valu_supports(g.dtype, g.head_dim) || !block_size_supported(bs, g.dtype, g.head_dim))
     return PF_ERR_UNSUPPORTED;
   if (bs != kBlock && n > kMaxSeqsBalanced) return PF_ERR_UNSUPPORTED;
+  const bool half = !contig && half_units(g);
+  if (g.dtype == PF_F32 && g.head_dim == 256 && (contig || n > kMaxSeqsBalanced)) return PF_ERR_UNSUPPORTED;
   if (n == 0) return PF_OK;
   if (n > 65535 || num_q_heads > 65535) return PF_ERR_INVALID;
   if (!q || !ctx_dev || !out) return PF_ERR_INVALID;
@@ -933,7 +961,11 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   hipStream_t st = (hipStream_t)hip_stream;
   if (pool->ev_start) (void)hipEventRecord((hipEvent_t)pool->ev_start, st);
   int rc;
-  if (bs != kBlock) {
+  if (half) {
+    if (a.out_f32) launch_valu_half<true>(a, st);
+    else launch_valu_half<false>(a, st);
+    rc = PF_OK;
+  } else if (bs != kBlock) {
     if (p.mfma) rc = launch_mfma_bs(a, g.dtype, g.head_dim, bs, st);
     else if (g.dtype == PF_F16) rc = launch_valu_bs<ElF16>(a, g.head_dim, bs, st);
     else rc = launch_valu_bs<ElBF16>(a, g.head_dim, bs, st);
@@ -1063,7 +1095,7 @@ extern "C" int pf_paged_decode_attention_append(const pf_pool* pool, int32_t lay
                                                 int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                                 void* hip_stream) {
   if (!pool) return PF_ERR_INVALID;
-  if (pool->g.block_size != kBlock) return PF_ERR_UNSUPPORTED;
+  if (pool->g.block_size != kBlock || half_units(pool->g)) return PF_ERR_UNSUPPORTED;
   if (n > 0 && (!k_new || !v_new || reinterpret_cast<uintptr_t>(k_new) % 16 != 0 ||
                 reinterpret_cast<uintptr_t>(v_new) % 16 != 0))
     return PF_ERR_INVALID;

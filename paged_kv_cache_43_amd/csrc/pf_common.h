@@ -14,10 +14,13 @@ constexpr int kBlock = 16;  // tokens per page of the default build (grid schedu
 // The attention kernels walk a sequence in units of at most 16 tokens: a
 // 16-token page is one unit, a 32- or 64-token page two or four (one table
 // entry, rows offset inside the page), an 8-token page one 8-token unit.
-template <int BS>
+// UTO > 0 sets the unit size instead (fp32 K/V at head dim 256 walks 16-token
+// pages in 8-token units: a 16-token unit is 128 VGPRs of K/V per lane there,
+// too many for two in flight).
+template <int BS, int UTO = 0>
 struct BlockUnits {
-  static constexpr int UT = BS < 16 ? BS : 16;  // tokens per unit
-  static constexpr int R = BS / UT;             // units per page
+  static constexpr int UT = UTO > 0 ? UTO : (BS < 16 ? BS : 16);  // tokens per unit
+  static constexpr int R = BS / UT;                                // units per page
   static_assert(UT * R == BS && (BS == 8 || BS % 16 == 0), "block size");
 };
 constexpr float kLog2e = 1.4426950408889634f;

@@ -77,3 +77,30 @@ def test_head_dim_256_long_contexts(lens, dtype):
             err = gu.assert_close(gu.out_to_f64(out, od), ref, od, "schedule %d out %s" % (sched, od))
             print("  schedule", sched, "waves", waves, "split", split, "out", od, "max err", err, flush=True)
     kv.close()
+
+
+@pytest.mark.parametrize("lens", [[65536], [32768] + list(range(100, 740, 10))], ids=["one-64k", "65-seqs"])
+def test_fp32_head_dim_256(lens):
+    """fp32 K/V at head dim 256, whose 16-token pages are walked in 8-token
+    units: the balanced schedule whatever is requested, with the per-row merge
+    (one 64k-token sequence, many pieces per row) and the one-wave merge (65
+    sequences); against the oracle."""
+    from paged_kv_cache_43_amd import pf, runner
+    print("fp32 head dim 256", len(lens), "sequences", flush=True)
+    w = _custom(lens, 4, 4, 256, "f32", seed=512 + len(lens))
+    kv = runner.PagedKV(w)
+    q = runner.fill_workload(kv)
+    ref = gu.oracle_attention_contiguous(w, 0)
+    mc = int(max(lens))
+    for sched in (0, SCHED_BALANCED, SCHED_GRID):
+        pf.check(pf.pf_pool_set_option(kv.h, pf.PF_OPT_SCHEDULE, sched))
+        waves = pf.pf_attention_waves(kv.h, w.n, 4, mc)
+        assert pf.pf_attention_split_tokens(kv.h, w.n, 4, mc) == 0 and waves > 0
+        if len(lens) == 1:
+            assert waves >= 16 * 4
+        out = torch.empty((w.n, 4, 256), dtype=torch.float32, device="cuda")
+        kv.attention(0, q[0], out, mc)
+        torch.cuda.synchronize()
+        err = gu.assert_close(gu.out_to_f64(out, "f32"), ref, "f32", "schedule %d" % sched)
+        print("  schedule", sched, "waves", waves, "max err", err, flush=True)
+    kv.close()
