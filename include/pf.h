@@ -445,9 +445,8 @@ int pf_paged_decode_attention_noalloc(const pf_pool* pool, int32_t layer, const 
  * contribute nothing (as for any invalid entry).
  *   k_new, v_new  device [n][H][D], pool dtype, 16-byte aligned.
  * Other arguments as pf_paged_decode_attention.  Built for 16-token pages
- * walked in 16-token units and head dims whose rows are a multiple of 16 bytes
- * (PF_ERR_UNSUPPORTED otherwise, also for fp32 pools at head dim 256).
- * Errors: as pf_paged_decode_attention. */
+ * and head dims whose rows are a multiple of 16 bytes (PF_ERR_UNSUPPORTED
+ * otherwise).  Errors: as pf_paged_decode_attention. */
 int pf_paged_decode_attention_append(const pf_pool* pool, int32_t layer, const void* q, int32_t num_q_heads,
                                      const void* k_new, const void* v_new, const int32_t* bt_dev,
                                      int32_t max_blocks, const int32_t* ctx_dev, int32_t n,
@@ -473,8 +472,7 @@ int pf_paged_decode_attention_append(const pf_pool* pool, int32_t layer, const v
  *   q, ctx_dev, n, max_context_len (<= max_len), scale, out, out_dtype,
  *   workspace (sized by pf_attention_workspace_bytes): as
  *            pf_paged_decode_attention.
- * Errors: PF_ERR_INVALID, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED (also for fp32
- * at head dim 256), PF_ERR_HIP. */
+ * Errors: PF_ERR_INVALID, PF_ERR_WORKSPACE, PF_ERR_UNSUPPORTED, PF_ERR_HIP. */
 int pf_contiguous_decode_attention(const pf_pool* pool, const void* q, int32_t num_q_heads, const void* k,
                                    const void* v, int64_t seq_stride, int64_t token_stride, int64_t head_stride,
                                    int32_t max_len, const int32_t* ctx_dev, int32_t n, int32_t max_context_len,

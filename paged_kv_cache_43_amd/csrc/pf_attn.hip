@@ -195,17 +195,18 @@ struct ValuWave {
     }
   }
 
-  // Before page() of the sequence's last unit (row nvalid-1 is its newest
-  // token), in pool page `page` (ok: a valid page).  With a fused append the
-  // newest token's K/V come from the input instead of the pool, patched into
-  // the tile, and the first query head of each kv head group writes them into
-  // the page (16-token pages walked in 16-token units only: the append entry
-  // point refuses every other walk); other waves that read the slot meanwhile
+  // Before page() of the sequence's last unit (unit index `unit`, row
+  // nvalid-1 is its newest token), in pool page `page` (ok: a valid page).
+  // With a fused append the newest token's K/V come from the input instead of
+  // the pool, patched into the tile, and the first query head of each kv head
+  // group writes them into the page (16-token pages only: the append entry
+  // point refuses other page sizes); other waves that read the slot meanwhile
   // discard what they read.
-  __device__ inline void patch_last(Tile& u, int nvalid, int s, int h, int page, bool ok) {
-    if constexpr (kUPP != 1 || BS != kBlock) return;
+  __device__ inline void patch_last(Tile& u, int nvalid, int s, int h, int page, bool ok, int unit = 0) {
+    if constexpr (BS != kBlock) return;
     if (a.k_new == nullptr || !ok) return;
     const int tn = nvalid - 1;
+    const int slot = (unit % kUPP) * UT + tn;  // the newest token's slot in its page
     const int hk = h / a.group;
     if (tq == tn % S::TPI) {
       const int64_t src = (((int64_t)s * a.hkv + hk) * D + dc * S::VEC) * S::ES;
@@ -220,7 +221,7 @@ struct ValuWave {
       if (h % a.group == 0) {
         uint8_t* base = const_cast<uint8_t*>(static_cast<const uint8_t*>(a.pool)) +
                         ((int64_t)page * a.page_elems + ((int64_t)a.layer * a.hkv + hk) * 2 * BS * D +
-                         (int64_t)tn * D + dc * S::VEC) * S::ES;
+                         (int64_t)slot * D + dc * S::VEC) * S::ES;
         store_raw<S::NW>(base, kk);
         store_raw<S::NW>(base + (int64_t)BS * D * S::ES, vv);
       }
@@ -593,10 +594,11 @@ static bool half_units(const pf_geometry& g) {
   return g.dtype == PF_F32 && g.head_dim == 256 && g.block_size == kBlock;
 }
 
-template <bool OUT_F32>
+// (fp32 output is the pool dtype, so there is no separate fp32-out form.)
+template <bool CONTIG>
 static void launch_valu_half(const AttnArgs& a, hipStream_t st) {
   constexpr int U = ValuUnit<ElF32, 256, kHalfUnit>::U;
-  hipLaunchKernelGGL((attn_valu_balanced<ElF32, 256, U, OUT_F32, false, kBlock, kHalfUnit>),
+  hipLaunchKernelGGL((attn_valu_balanced<ElF32, 256, U, false, CONTIG, kBlock, kHalfUnit>),
                      dim3(a.waves / (kSchedThreads / kWave)), dim3(kSchedThreads), 0, st, a);
 }
 
@@ -921,8 +923,8 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   if (!valu_supports(g.dtype, g.head_dim) || !block_size_supported(bs, g.dtype, g.head_dim))
     return PF_ERR_UNSUPPORTED;
   if (bs != kBlock && n > kMaxSeqsBalanced) return PF_ERR_UNSUPPORTED;
-  const bool half = !contig && half_units(g);
-  if (g.dtype == PF_F32 && g.head_dim == 256 && (contig || n > kMaxSeqsBalanced)) return PF_ERR_UNSUPPORTED;
+  const bool half = half_units(g);  // the contiguous twin walks 16-token blocks, so this holds for it too
+  if (half && n > kMaxSeqsBalanced) return PF_ERR_UNSUPPORTED;
   if (n == 0) return PF_OK;
   if (n > 65535 || num_q_heads > 65535) return PF_ERR_INVALID;
   if (!q || !ctx_dev || !out) return PF_ERR_INVALID;
@@ -962,7 +964,7 @@ int attend(const pf_pool* pool, AttnArgs& a, bool contig, const void* q, int32_t
   if (pool->ev_start) (void)hipEventRecord((hipEvent_t)pool->ev_start, st);
   int rc;
   if (half) {
-    if (a.out_f32) launch_valu_half<true>(a, st);
+    if (contig) launch_valu_half<true>(a, st);
     else launch_valu_half<false>(a, st);
     rc = PF_OK;
   } else if (bs != kBlock) {
@@ -1095,7 +1097,7 @@ extern "C" int pf_paged_decode_attention_append(const pf_pool* pool, int32_t lay
                                                 int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                                 void* hip_stream) {
   if (!pool) return PF_ERR_INVALID;
-  if (pool->g.block_size != kBlock || half_units(pool->g)) return PF_ERR_UNSUPPORTED;
+  if (pool->g.block_size != kBlock) return PF_ERR_UNSUPPORTED;
   if (n > 0 && (!k_new || !v_new || reinterpret_cast<uintptr_t>(k_new) % 16 != 0 ||
                 reinterpret_cast<uintptr_t>(v_new) % 16 != 0))
     return PF_ERR_INVALID;

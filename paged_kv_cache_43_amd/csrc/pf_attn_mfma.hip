@@ -285,7 +285,8 @@ struct MfmaWave {
   // newest token's K/V come from the input instead of the pool, patched into
   // the tile, and this wave (the only one for this kv head) writes them into
   // the page (16-token pages only).
-  __device__ inline void patch_last(Tile& u, int nvalid, int s, int hk, int page, bool ok) {
+  __device__ inline void patch_last(Tile& u, int nvalid, int s, int hk, int page, bool ok, int unit = 0) {
+    (void)unit;  // 16-token units: the newest token's row is its slot
     if (a.k_new == nullptr || !ok) return;
     const int tn = nvalid - 1;
     const int64_t row = ((int64_t)s * a.hkv + hk) * D * ES;

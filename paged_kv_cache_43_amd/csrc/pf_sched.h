@@ -199,7 +199,8 @@ __device__ inline void sched_run(const AttnArgs& a, const SchedLds& L, int X, Wv
             }
           }
           cplast = p;
-          if (p == cP - 1) w.patch_last(t, __builtin_amdgcn_readlane(lnv, i), s, x, __builtin_amdgcn_readlane(lpage, i), ok);
+          if (p == cP - 1)
+            w.patch_last(t, __builtin_amdgcn_readlane(lnv, i), s, x, __builtin_amdgcn_readlane(lpage, i), ok, p);
           if (ok) w.page(t, __builtin_amdgcn_readlane(lnv, i));
         });
   }

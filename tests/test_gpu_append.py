@@ -81,6 +81,40 @@ def test_append_equals_scatter_then_attend(name, mfma, sched):
         kv.close()
 
 
+@pytest.mark.parametrize("lens", [[1, 7, 8, 9, 15, 16, 17, 24, 100, 513], [4000, 25, 33]])
+def test_append_fp32_head_dim_256(lens):
+    """fp32 K/V at head dim 256, walked in 8-token units inside 16-token
+    pages: newest tokens in the first and the second half of their page.
+    Fused equals separate bit for bit, output and pool, and the oracle."""
+    print("append fp32 d256", lens, flush=True)
+    from paged_kv_cache_43_amd import runner
+    w = inputs.Workload("tiny", seed=len(lens), frames="shuffled", lens=lens)
+    w.hq, w.hkv, w.d, w.dtype, w.es = 4, 2, 256, "f32", 4
+    w.num_pages = sum(-(-int(c) // 16) for c in lens) + 8
+    w.free_order = np.random.default_rng(3).permutation(w.num_pages)
+    kvs, q = _pair(w, SCHED_AUTO, 1)
+    rng = np.random.default_rng(11)
+    ks, vs, qb = w.values()
+    nk = inputs.normal_bits(rng, (w.n, w.hkv, w.d), w.dtype)
+    nv = inputs.normal_bits(rng, (w.n, w.hkv, w.d), w.dtype)
+    sep, fused = _both(w, kvs, q, 0, runner.bits_to_device(nk), runner.bits_to_device(nv), "f32")
+    assert torch.equal(sep, fused)
+    assert torch.equal(kvs[0].pool, kvs[1].pool)
+    got = fused.cpu().numpy().astype(np.float64)
+    qd = oa.decode_bits(qb[0], w.dtype)
+    g = w.hq // w.hkv
+    for s in range(w.n):
+        K = oa.decode_bits(ks[s][0], w.dtype).copy()
+        V = oa.decode_bits(vs[s][0], w.dtype).copy()
+        K[-1] = oa.decode_bits(nk[s], w.dtype)
+        V[-1] = oa.decode_bits(nv[s], w.dtype)
+        for h in range(w.hq):
+            ref = oa.attention(qd[s, h], K[:, h // g], V[:, h // g], oa.default_scale(w.d))
+            assert np.max(np.abs(got[s, h] - ref)) <= gu.ATOL, (s, h)
+    for kv in kvs:
+        kv.close()
+
+
 @pytest.mark.parametrize("sched", [SCHED_GRID, SCHED_BALANCED])
 def test_append_with_invalid_newest_page(sched):
     """The newest token's table entry is not a valid page: nothing is written

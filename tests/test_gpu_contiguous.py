@@ -96,7 +96,7 @@ def _custom(lens, hq, hkv, d, dtype, seed):
 
 @pytest.mark.parametrize("sched", [SCHED_GRID, SCHED_BALANCED])
 @pytest.mark.parametrize("dtype,d,hq,hkv", [("f32", 16, 2, 2), ("f16", 32, 3, 3), ("f16", 128, 4, 2),
-                                            ("bf16", 64, 14, 2), ("bf16", 256, 2, 1)])
+                                            ("bf16", 64, 14, 2), ("bf16", 256, 2, 1), ("f32", 256, 4, 2)])
 def test_twin_shapes_and_edge_lengths(dtype, d, hq, hkv, sched):
     """Every kernel family (vector and matrix-core), edge lengths including 0,
     1 and block boundaries, and a cache longer than any sequence."""

@@ -281,8 +281,7 @@ def test_kernel_entry_points_validate_before_launch():
                                         stream=0) == pf.PF_ERR_UNSUPPORTED
     pf.pf_pool_destroy(h2)
     # fp32 at head dim 256: 8-token units, always the balanced schedule (a
-    # fixed-split request is overridden), n <= 2048, no fused append and no
-    # contiguous twin
+    # fixed-split request is overridden), n <= 2048
     st, h3 = pf.pf_pool_create(64, 16, 1, 1, 256, "f32")
     assert pf.pf_pool_bind(h3, fake, pf.pf_pool_bytes(h3)) == pf.PF_OK
     assert pf.pf_pool_set_option(h3, pf.PF_OPT_SCHEDULE, 1) == pf.PF_OK
@@ -290,9 +289,9 @@ def test_kernel_entry_points_validate_before_launch():
     assert pf.pf_attention_workspace_bytes(h3, 1, 1, 128) > 0
     assert pf.pf_paged_decode_attention(h3, 0, A, 1, A, 8, A, 2049, 128, 0.0, A, "f32", None, 0,
                                         stream=0) == pf.PF_ERR_UNSUPPORTED
-    assert pf.pf_paged_decode_attention_append(h3, 0, A, 1, A, A, A, 8, A, 1, 128, 0.0, A, "f32", None, 0,
+    assert pf.pf_paged_decode_attention_append(h3, 0, A, 1, A, A, A, 8, A, 2049, 128, 0.0, A, "f32", None, 0,
                                                stream=0) == pf.PF_ERR_UNSUPPORTED
-    assert pf.pf_contiguous_decode_attention(h3, A, 1, A, A, 128 * 256, 256, 256, 128, A, 1, 128, 0.0, A,
+    assert pf.pf_contiguous_decode_attention(h3, A, 1, A, A, 128 * 256, 256, 256, 128, A, 2049, 128, 0.0, A,
                                              "f32", None, 0, stream=0) == pf.PF_ERR_UNSUPPORTED
     pf.pf_pool_destroy(h3)
 
