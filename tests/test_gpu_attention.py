@@ -246,7 +246,7 @@ def test_split_invariance(split):
     kv.close()
 
 
-@pytest.mark.parametrize("group", [1, 2, 4, 7, 8, 16])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 7, 8, 16, 32])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_grouped_heads(group, dtype):
     print("group", group, dtype, flush=True)
@@ -255,6 +255,9 @@ def test_grouped_heads(group, dtype):
     for mfma in (0, 1):
         for sched in (SCHED_GRID, SCHED_BALANCED):
             got, kv, q = _run(w, out_dtype="f32", mfma=mfma, sched=sched, waves=1 if sched == SCHED_BALANCED else None)
+            from paged_kv_cache_43_amd import pf
+            # the matrix-core kernel takes groups of 2 to 16 heads; others run on the vector kernel
+            assert pf.pf_attention_kernel(kv.h, w.hq) == (1 if mfma and 1 < group <= 16 else 0)
             ref = gu.oracle_attention_contiguous(w, 0)
             gu.assert_close(got, ref, "f32", "group %d mfma %d sched %d" % (group, mfma, sched))
             kv.close()
