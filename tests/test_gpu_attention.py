@@ -233,6 +233,63 @@ def test_lengths_clamped_to_bound(sched, mfma):
     kv.close()
 
 
+@pytest.mark.parametrize("pattern", ["rising", "late_jump", "one_survivor", "flat"])
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f16", 8, 2, 64), ("bf16", 14, 2, 64), ("bf16", 4, 4, 128),
+                                            ("f32", 2, 2, 64)])
+def test_score_extremes(pattern, dtype, hq, hkv, d):
+    """Scores forced along each sequence: every query head gets the same unit
+    vector u and token t's key is a_t * sqrt(D) * u, so its score is about
+    a_t -- rising to 40 (the running max is raised again and again), one
+    score 60 above the rest near the end, all at -60 but one, all equal (the
+    mean of V).  Both schedules, vector and matrix-core kernels, against the
+    oracle on the stored bits."""
+    from paged_kv_cache_43_amd import runner
+    print("score extremes", pattern, dtype, hq, hkv, d, flush=True)
+    lens = [1, 17, 300, 2000]
+    w = _custom(lens, hq, hkv, d, dtype, seed=d + hq)
+    kv = runner.PagedKV(w)
+    q = runner.fill_workload(kv)
+    rng = np.random.default_rng(5)
+    sign = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    qbits = inputs.to_bits(np.broadcast_to(sign / np.sqrt(d), (w.n, w.hq, d)), dtype)
+    q[0].copy_(runner.bits_to_device(qbits))
+    _, vs, _ = w.values()
+    kbits = []
+    for n in lens:
+        if pattern == "rising":
+            a = 40.0 * np.arange(1, n + 1) / n
+        elif pattern == "late_jump":
+            a = np.zeros(n)
+            a[max(0, n - 3)] = 60.0
+        elif pattern == "one_survivor":
+            a = np.full(n, -60.0)
+            a[n // 3] = 0.0
+        else:
+            a = np.zeros(n)
+        kbits.append(inputs.to_bits(a[:, None, None] * np.broadcast_to(sign, (1, hkv, d)), dtype))
+    tok_seq, tok_pos = runner.token_arrays(w, [range(n) for n in lens])
+    kv.scatter(0, runner.bits_to_device(np.concatenate(kbits)),
+               runner.bits_to_device(np.concatenate([vs[s][0] for s in range(w.n)])),
+               torch.from_numpy(tok_seq).cuda(), torch.from_numpy(tok_pos).cuda())
+    qd = oa.decode_bits(qbits, dtype)
+    g = hq // hkv
+    ref = np.zeros((w.n, hq, d))
+    for s in range(w.n):
+        K = oa.decode_bits(kbits[s], dtype)
+        V = oa.decode_bits(vs[s][0], dtype)
+        for h in range(hq):
+            ref[s, h] = oa.attention(qd[s, h], K[:, h // g], V[:, h // g], oa.default_scale(d))
+    if pattern == "flat":
+        for s in range(w.n):
+            V = oa.decode_bits(vs[s][0], dtype)
+            assert np.allclose(ref[s], V.mean(axis=0)[np.arange(hq) // g], atol=1e-12)
+    for mfma in (0, 1):
+        for sched in (SCHED_GRID, SCHED_BALANCED):
+            got = _run(w, out_dtype="f32", mfma=mfma, sched=sched, kv=kv, q=q)
+            gu.assert_close(got, ref, "f32", "%s mfma %d sched %d" % (pattern, mfma, sched))
+    kv.close()
+
+
 @pytest.mark.parametrize("split", [16, 32, 64, 128, 512, 1024])
 def test_split_invariance(split):
     print("split", split, flush=True)
